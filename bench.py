@@ -1,0 +1,281 @@
+"""Benchmark of the decode MoE layer on one MI355X.
+
+Workload (one "step" = one decode MoE layer call: route, gate/up, down):
+a Flint-shaped layer (hidden 2048, 256 routed experts + 1 shared, expert
+intermediate 512, sigmoid top-6, NVFP4 weights with BF16 activations) at
+batch 1, with 32 independently seeded layer copies rotated call by call so
+that the weights come from HBM, not from the 256 MB cache.  Weights and the
+per-step activations are generated and repacked on the GPU before timing.
+
+Reported (one JSON line):
+  value        algorithmic HBM bytes per step / time per step, in TB/s: the
+               selected experts' packed gate/up/down bytes (counted from the
+               returned expert indices), the router matrix, and the
+               activations in and out
+  roofline     the dominant kernel (gate/up): its algorithmic bytes per
+               launch / its average duration (HIP events around a graph of
+               back-to-back launches of that kernel on the launch stream),
+               against 8 TB/s
+  cpu_baseline the float64 NumPy oracle on a bounded sample of the same
+               workload, on the host, one thread
+  batch8       the same layer at batch 8 (up to 48 distinct experts)
+The timed loops replay HIP graphs of the layer calls, so host launch cost is
+not on the clock.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+import w4a16_moe_decode_amd as fm  # noqa: E402
+
+METRIC = "MoE-layer decode µs & achieved HBM TB/s (batch 1, 8); prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+N_COPIES = 32
+
+
+def build_copies(shape: gen.MoeShape, n_copies: int, seed: int, device):
+    """n_copies independently seeded packed layers, generated on the GPU."""
+    layers, host_src0 = [], None
+    for c in range(n_copies):
+        src = gen.moe_layer_source(shape, gen.seed_for(seed, "copy", c), device)
+        layers.append(fm.pack_moe_layer(src.router, src.gate, src.up, src.down, src.gscale,
+                                        src.sh_gate, src.sh_up, src.sh_down, src.sh_gscale,
+                                        src.layout, device))
+        if c == 0:      # the oracle baseline runs on exactly copy 0's bytes
+            host_src0 = gen.MoeLayerSource(**{
+                k: (v.cpu() if isinstance(v, torch.Tensor) else v)
+                for k, v in src.__dict__.items()})
+        del src
+    torch.cuda.synchronize()
+    return layers, host_src0
+
+
+def expert_bytes(shape: gen.MoeShape):
+    H, I, SI = shape.hidden, shape.inter, shape.shared_inter
+    per = lambda r, c: r * c // 2 + r * c // 16
+    return {"gate_up": 2 * per(I, H), "down": per(H, I),
+            "sh_gate_up": 2 * per(SI, H), "sh_down": per(H, SI)}
+
+
+def step_bytes(shape: gen.MoeShape, batch: int, n_distinct: int):
+    """Algorithmic HBM bytes of one decode call and of its gate/up kernel."""
+    eb = expert_bytes(shape)
+    router = shape.n_experts * shape.hidden * 2
+    act = 2 * batch * shape.hidden * 2
+    gu = n_distinct * eb["gate_up"] + eb["sh_gate_up"] + batch * shape.hidden * 2
+    total = n_distinct * (eb["gate_up"] + eb["down"]) + eb["sh_gate_up"] + eb["sh_down"] + router + act
+    return total, gu
+
+
+class Bench:
+    def __init__(self, layers, shape, batch, n_steps, seed):
+        self.layers, self.shape, self.batch = layers, shape, batch
+        self.runners = [fm.DecodeRunner(L, shape.top_k, 0) for L in layers]
+        ws = self.runners[0].ws
+        for r in self.runners:
+            r.ws = ws                       # one workspace for the whole stream
+        dev = layers[0].router.device
+        n = max(n_steps, len(layers))
+        self.x = gen.activations(gen.seed_for(seed, "x", batch), n * batch, shape.hidden, dev
+                                 ).view(n, batch, shape.hidden)
+        self.out = torch.empty_like(self.x)
+        self.idx = torch.zeros((n, batch, shape.top_k), dtype=torch.int32, device=dev)
+        self.w = torch.zeros((n, batch, shape.top_k), dtype=torch.float32, device=dev)
+
+    def call(self, i):
+        r = self.runners[i % len(self.runners)]
+        r(self.x[i], out=self.out[i], topk_idx=self.idx[i], topk_w=self.w[i])
+
+    def graph(self, n_steps):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(min(n_steps, 3)):     # eager warm-up before capture
+                self.call(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_steps):
+                self.call(i)
+        return g
+
+    def distinct(self, n_steps):
+        idx = self.idx[:n_steps].cpu()
+        return [len(set(idx[i].reshape(-1).tolist())) for i in range(n_steps)]
+
+    def stage_times(self, n_launch=256, ws_per_copy=4):
+        """Average duration of each stage, from HIP events around a graph of
+        back-to-back launches of that stage alone on the launch stream.  Each
+        launch uses its own (layer copy, workspace) pair holding a routing
+        computed from its own activations, so consecutive launches read
+        different experts of different copies (about 1 GB touched per pass,
+        well past the 256 MB cache)."""
+        pairs = []
+        for k in range(ws_per_copy):
+            for c, L in enumerate(self.layers):
+                r = fm.DecodeRunner(L, self.shape.top_k, 0)
+                i = (k * len(self.layers) + c) % self.x.shape[0]
+                r(self.x[i], out=self.out[i], topk_idx=self.idx[i], topk_w=self.w[i])
+                pairs.append((r, i))
+        torch.cuda.synchronize()
+        res = []
+        for st in range(3):
+            def body(st=st):
+                for j in range(n_launch):
+                    r, i = pairs[j % len(pairs)]
+                    r.stage(st, self.x[i], self.out[i], self.idx[i], self.w[i])
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                body()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                body()
+            g.replay()
+            res.append(timed(g) / n_launch * 1e6)
+            del g
+        del pairs
+        return res
+
+
+def timed(graph, reps=1):
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e-3     # seconds
+
+
+def cpu_baseline(layer_src, shape, budget_s: float):
+    """The oracle, one thread, on batch-1 calls of copy 0 until the time
+    budget is spent; TB/s of algorithmic bytes, like the GPU value."""
+    from threadpoolctl import threadpool_limits
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _parity import oracle_experts
+    from oracle import moe
+
+    with threadpool_limits(1):
+        torch.set_num_threads(1)
+        t_start = time.perf_counter()
+        n, nbytes = 0, 0
+        while time.perf_counter() - t_start < budget_s:
+            ex = oracle_experts(layer_src)    # decode from the source bytes every call
+            x = gen.numpy_f64(gen.activations(gen.seed_for(0, "cpu", n), 1, shape.hidden))
+            _, r = moe.moe_layer(x, ex, shape.top_k, False)
+            nbytes += step_bytes(shape, 1, len(set(r.idx.reshape(-1).tolist())))[0]
+            n += 1
+        el = time.perf_counter() - t_start
+    return {"value": nbytes / el / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} batch-1 decode calls of one Flint-shaped layer (copy 0), "
+                      f"{el:.1f} s, float64 NumPy, 1 thread",
+            "us_per_layer": el / n * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=N_COPIES)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-batch8", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode layer is replicated per GPU; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fm.lib()
+    dev = torch.device("cuda:0")
+    shape = gen.SHAPE_FLINT
+    print(f"[bench] generating {args.copies} layer copies on the GPU", file=sys.stderr, flush=True)
+    layers, src0 = build_copies(shape, args.copies, args.seed, dev)
+
+    res = {}
+    for batch in ([1] if args.no_batch8 else [1, 8]):
+        b = Bench(layers, shape, batch, max(args.steps, args.warmup), args.seed)
+        gw = b.graph(args.warmup)
+        gt = b.graph(args.steps)
+        gw.replay()
+        torch.cuda.synchronize()
+        secs = timed(gt)
+        dist = b.distinct(args.steps)
+        nbytes = sum(step_bytes(shape, batch, d)[0] for d in dist)
+        gu_bytes = sum(step_bytes(shape, batch, d)[1] for d in dist) / len(dist)
+        st_us = b.stage_times()
+        res[batch] = dict(secs=secs, nbytes=nbytes, gu_bytes=gu_bytes, stage_us=st_us,
+                          distinct=sum(dist) / len(dist))
+        print(f"[bench] batch {batch}: {secs / args.steps * 1e6:.2f} us/layer, "
+              f"{nbytes / secs / 1e12:.3f} TB/s, stages {['%.2f' % s for s in st_us]} us, "
+              f"distinct experts {res[batch]['distinct']:.2f}", file=sys.stderr, flush=True)
+        del b, gw, gt
+
+    r1 = res[1]
+    us = r1["secs"] / args.steps * 1e6
+    gu_us = r1["stage_us"][1]
+    achieved = r1["gu_bytes"] / (gu_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(r1["nbytes"] / r1["secs"] / 1e12, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "flint_moe_decode_layer", "hidden": shape.hidden,
+                   "routed_experts": shape.n_experts, "shared_experts": 1,
+                   "expert_inter": shape.inter, "top_k": shape.top_k, "batch": 1,
+                   "weights": "nvfp4 (e2m1 + ue4m3/16 + fp32 per expert)", "activations": "bf16",
+                   "layer_copies": args.copies, "parallelism": "single-gpu"},
+        "us_per_layer": round(us, 3),
+        "tokens_per_s_per_layer": round(1e6 / us, 1),
+        "stage_us": {"route": round(r1["stage_us"][0], 3), "gate_up": round(gu_us, 3),
+                     "down": round(r1["stage_us"][2], 3)},
+        "roofline": {"bound": "hbm", "kernel": "gate_up_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+    }
+    if 8 in res:
+        r8 = res[8]
+        us8 = r8["secs"] / args.steps * 1e6
+        gu8 = r8["gu_bytes"] / (r8["stage_us"][1] * 1e-6) / 1e9
+        line["batch8"] = {"us_per_layer": round(us8, 3),
+                          "tb_s": round(r8["nbytes"] / r8["secs"] / 1e12, 4),
+                          "tokens_per_s_per_layer": round(8e6 / us8, 1),
+                          "distinct_experts": round(r8["distinct"], 2),
+                          "stage_us": [round(v, 3) for v in r8["stage_us"]],
+                          "gate_up_frac": round(gu8 / HBM_PEAK_GBS, 4)}
+    if not args.no_cpu:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(src0, shape, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,277 @@
+/*
+ * flint_moe.h -- C ABI of the MI355X (gfx950) W4A16 MoE decode library.
+ *
+ * The library runs the MoE sublayer of a Flint-shaped model: a router GEMV,
+ * sigmoid top-k over the routed experts, SwiGLU expert GEMVs that read only
+ * the selected experts' 4-bit weights, an always-on shared expert and a
+ * weighted combine, with BF16 activations and NVFP4 (or BF16) weights.
+ *
+ * Sources for what is computed (cited by page title and section):
+ *  [D0]  "Day-0 Support for Flint on vLLM" (wpnews.pro), sections
+ *        "Model architecture" and "Optimizations".
+ *  [AR]  "vLLM 宣布首日支持 Recursive 的 Flint：单张 GB200 上达约 500 tokens/s，
+ *        每层内核启动从 22 次降至 7 次" (arex-research.com), sections
+ *        "Flint 是什么" and "七个内核的依赖链：低延迟路径、无损重排与参考舍入".
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) are device addresses on the current HIP
+ *    device; (host) pointers are read during the call only.  The caller owns
+ *    all memory; the library never allocates, frees, or keeps per-call state.
+ *  - Every device pointer must be 16-byte aligned (FLINT_ERR_ALIGNMENT),
+ *    except the top-k outputs of decode and prefill (4-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work: the return value covers argument checks and launch errors, and
+ *    results are valid after the stream is synchronised.  No call blocks or
+ *    synchronises, so every call can be captured in a HIP graph.
+ *  - Arguments are validated before anything is enqueued; on error nothing
+ *    is enqueued.  No call prints or throws.
+ *  - BF16 is IEEE binary32's top 16 bits; rounding to BF16 is to nearest,
+ *    ties to even.
+ *
+ * Packed NVFP4 layout (the gfx950 layout written by flint_moe_repack)
+ *  A matrix of R rows by C columns (C = reduction dimension, multiple of 64)
+ *  becomes two planes:
+ *    codes : uint8 [R][C/2]   two E2M1 codes per byte, column 2i in the low
+ *                             nibble, column 2i+1 in the high nibble
+ *    scales: uint8 [R][C/16]  the UE4M3 scale of columns 16j..16j+15
+ *  A GEMV wave reads 16 bytes of codes (32 columns) per lane and the two
+ *  matching scale bytes, so every load is a coalesced 128-bit row segment.
+ *  Several matrices are stored back to back (matrix m at m*R*C/2 bytes of the
+ *  code plane, m*R*C/16 of the scale plane).  Expert e's gate/up pair is
+ *  matrices 2e (gate) and 2e+1 (up) of one [E][2][I][H] array.
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stdint.h>
+
+/* Exported symbols keep default visibility; the library builds with
+ * -fvisibility=hidden so nothing else leaks out of it. */
+#define FLINT_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status -- */
+#define FLINT_OK                0
+#define FLINT_ERR_INVALID_ARG   1   /* NULL where required, negative or zero size */
+#define FLINT_ERR_ALIGNMENT     2   /* a device pointer is not 16-byte aligned */
+#define FLINT_ERR_UNSUPPORTED   3   /* shape, batch or flag outside the envelope:
+                                       the caller falls back (e.g. to prefill) */
+#define FLINT_ERR_WORKSPACE     4   /* workspace NULL or smaller than required */
+#define FLINT_ERR_DEVICE        5   /* a HIP launch reported an error */
+
+/* ----------------------------------------------------------------- flags -- */
+#define FLINT_RENORM       0x1u  /* combine weight = s_k / sum of selected s
+                                    (default: the raw sigmoid score s_k) */
+#define FLINT_W_BF16       0x2u  /* weights are BF16 (W16A16), not NVFP4 */
+#define FLINT_PRE_RMSNORM  0x4u  /* input is the residual x: the layer first
+                                    computes xn = RMSNorm(x) * gamma */
+#define FLINT_RESIDUAL     0x8u  /* out = BF16(x + BF16(layer(xn))) */
+
+/* source NVFP4 super-block byte orders accepted by the repack */
+#define FLINT_SRC_INTERLEAVED   0  /* 4 x [scale byte, 8 code bytes]          */
+#define FLINT_SRC_SCALES_FIRST  1  /* 4 scale bytes, then 32 code bytes       */
+
+/* dense GEMV epilogues */
+#define FLINT_EPI_NONE     0   /* y = BF16(g * W x)                              */
+#define FLINT_EPI_SWIGLU   1   /* W = [gate; up]: y = BF16(BF16(SiLU(BF16(g0 Wg x)))
+                                  * BF16(g1 Wu x))                               */
+#define FLINT_EPI_RESIDUAL 2   /* y = BF16(aux + BF16(g * W x))                  */
+
+#define FLINT_MAX_DECODE_BATCH 8
+#define FLINT_MAX_TOP_K        8
+#define FLINT_MAX_EXPERTS      256
+
+/* Shape of one MoE layer.
+ *   hidden        H, multiple of 64, at most 4096
+ *   n_experts     E, routed experts, 1..256
+ *   inter         I, routed expert intermediate, multiple of 64
+ *   shared_inter  SI, shared expert intermediate, multiple of 64; 0 = none
+ *   top_k         K, 1..min(8, E)
+ *   flags         FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL
+ *   rms_eps       RMSNorm epsilon (used with FLINT_PRE_RMSNORM)
+ * Sizes: [D0] "Model architecture" (hidden 2048; 256 experts, sigmoid top-6,
+ * one shared expert); the expert intermediate is not printed on the pages. */
+typedef struct flint_moe_shape {
+  int32_t hidden;
+  int32_t n_experts;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t top_k;
+  uint32_t flags;
+  float rms_eps;
+} flint_moe_shape;
+
+/* Weights of one MoE layer (all device pointers, read-only).
+ *   router        BF16 [E][H]
+ * NVFP4 (flags without FLINT_W_BF16; packed layout above):
+ *   gu_codes      [E][2][I][H/2]     gu_scales  [E][2][I][H/16]
+ *   d_codes       [E][H][I/2]        d_scales   [E][H][I/16]
+ *   gscale        float [E][3]       FP32 tensor scale of (gate, up, down)
+ *                                    per expert ([AR] "七个内核的依赖链",
+ *                                    second paragraph)
+ *   sh_gu_codes   [2][SI][H/2]       sh_gu_scales [2][SI][H/16]
+ *   sh_d_codes    [H][SI/2]          sh_d_scales  [H][SI/16]
+ *   sh_gscale     float [3]
+ * BF16 (FLINT_W_BF16; the scale fields are ignored):
+ *   gu_bf16 [E][2][I][H], d_bf16 [E][H][I], sh_gu_bf16 [2][SI][H], sh_d_bf16 [H][SI]
+ * Shared-expert fields may be NULL when shared_inter is 0. */
+typedef struct flint_moe_weights {
+  const void* router;
+  const void* gu_codes;
+  const void* gu_scales;
+  const void* d_codes;
+  const void* d_scales;
+  const float* gscale;
+  const void* sh_gu_codes;
+  const void* sh_gu_scales;
+  const void* sh_d_codes;
+  const void* sh_d_scales;
+  const float* sh_gscale;
+  const void* gu_bf16;
+  const void* d_bf16;
+  const void* sh_gu_bf16;
+  const void* sh_d_bf16;
+} flint_moe_weights;
+
+/* ---------------------------------------------------------------- helpers -- */
+
+/* Library version string (static storage). */
+FLINT_API const char* flint_version(void);
+
+/* Text of a status code (static storage; unknown codes give "unknown"). */
+FLINT_API const char* flint_status_string(int32_t status);
+
+/* Bytes of the packed planes of n_mats matrices of rows x cols (cols a
+ * multiple of 64).  Writes *code_bytes = n_mats*rows*cols/2 and
+ * *scale_bytes = n_mats*rows*cols/16.  Host pointers. */
+FLINT_API int32_t flint_nvfp4_packed_bytes(int64_t n_mats, int64_t rows, int64_t cols,
+                                 int64_t* code_bytes, int64_t* scale_bytes);
+
+/* Workspace bytes flint_moe_decode (max_tokens <= 8) or flint_moe_prefill
+ * (any max_tokens >= 1) needs for this shape; negative = a FLINT_ERR_* code
+ * negated.  The workspace must be zero-filled once after allocation (it
+ * carries a launch counter from call to call); calls that share one
+ * workspace must be ordered on one stream. */
+FLINT_API int64_t flint_moe_workspace_bytes(const flint_moe_shape* shape, int32_t max_tokens);
+
+/* ------------------------------------------------------------------ repack -- */
+
+/* Lossless load-time repack of source NVFP4 super-blocks into the packed
+ * planes ([D0] "Model architecture", paragraph after the bullets: the
+ * checkpoint's NVFP4 blocks come in another byte order and are repacked
+ * without loss at load; [AR] "七个内核的依赖链", second paragraph: a 64-value
+ * super-block is four groups of one UE4M3 scale and 16 E2M1 codes).
+ *   src          (device) uint8 [n_mats][rows][cols/64][36] in `src_layout`
+ *   dst_codes    (device) packed code plane; matrix m is written at matrix
+ *                index m*dst_mat_stride of the plane (stride 2 writes every
+ *                other matrix, e.g. gate into the even and up into the odd
+ *                slots of a [E][2] array)
+ *   dst_scales   (device) packed scale plane, same matrix indexing
+ * A pure byte permutation: every byte is copied, NaN and sign-bit scale
+ * bytes included.  Source and destination must not overlap. */
+FLINT_API int32_t flint_moe_repack(const void* src, int64_t n_mats, int32_t rows, int32_t cols,
+                         int32_t src_layout, void* dst_codes, void* dst_scales,
+                         int64_t dst_mat_stride, void* stream);
+
+/* Exact inverse of flint_moe_repack (for round-trip checks and export):
+ * reads matrices m*src_mat_stride of the packed planes and writes
+ * dst uint8 [n_mats][rows][cols/64][36] in `src_layout`. */
+FLINT_API int32_t flint_moe_unpack(const void* codes, const void* scales, int64_t n_mats,
+                         int32_t rows, int32_t cols, int32_t src_layout,
+                         int64_t src_mat_stride, void* dst, void* stream);
+
+/* Dequantise packed matrices to float32, the same E2M1 x UE4M3 decode the
+ * GEMV kernels use: out[m][r][c] = E2M1 * UE4M3 * tensor_scale[m]
+ * (tensor_scale (device) float [n_mats] or NULL for 1.0).  A verification
+ * aid: it exposes the kernels' decode so it can be compared bit for bit. */
+FLINT_API int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int64_t n_mats,
+                            int32_t rows, int32_t cols, const float* tensor_scale,
+                            float* out, void* stream);
+
+/* ------------------------------------------------------------------ decode -- */
+
+/* The small-batch decode MoE layer ([D0] "Optimizations": router and
+ * expert GEMVs that read only the selected experts' weights, with routing
+ * and the expert combine fused into the neighbouring GEMV kernels, for up
+ * to 8 concurrent requests).  Per token t of the batch:
+ *   xn    = x, or BF16(BF16(x / sqrt(mean(x^2) + eps)) * gamma) with
+ *           FLINT_PRE_RMSNORM
+ *   s_e   = sigmoid(router[e] . xn)              logits accumulated in fp32
+ *   idx   = top_k experts by descending s, ties to the lower index
+ *   w_k   = s_idx[k]  (or s_idx[k] / sum_k s_idx[k] with FLINT_RENORM)
+ *   E(z)  = W_d (BF16(BF16(SiLU(BF16(W_g z))) * BF16(W_u z)))
+ *   out   = BF16(sum_k w_k E_idx[k](xn) + E_shared(xn))
+ *   with FLINT_RESIDUAL: out = BF16(x + out)
+ * Each selected expert's weights are read once per call, for all tokens
+ * routed to it.
+ *   x         (device) BF16 [batch][H]
+ *   batch     1..8, else FLINT_ERR_UNSUPPORTED (use flint_moe_prefill)
+ *   out       (device) BF16 [batch][H]; may equal x only with FLINT_RESIDUAL
+ *   topk_idx  (device) int32 [batch][K] or NULL; ordered by descending score
+ *   topk_w    (device) float [batch][K] or NULL; the combine weights
+ *   gamma     (device) BF16 [H], required with FLINT_PRE_RMSNORM
+ *   ws        (device) workspace of at least flint_moe_workspace_bytes(shape, batch)
+ * Enqueues three kernels: route (RMSNorm, router GEMV, top-k, expert set),
+ * gate/up (+SiLU*up), down (weighted combine, shared expert, residual). */
+FLINT_API int32_t flint_moe_decode(const flint_moe_shape* shape, const flint_moe_weights* weights,
+                         const void* x, int32_t batch, void* out, int32_t* topk_idx,
+                         float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
+                         void* stream);
+
+/* One stage of flint_moe_decode, same arguments: stage 0 = route (router
+ * GEMV and top-k), 1 = gate/up, 2 = down + combine.  Enqueuing stages 0, 1, 2 in order on one
+ * stream with the same workspace is exactly flint_moe_decode; a stage reads
+ * what the previous one left in the workspace.  For per-kernel timing and
+ * for callers that interleave other work between stages. */
+FLINT_API int32_t flint_moe_decode_stage(int32_t stage, const flint_moe_shape* shape,
+                               const flint_moe_weights* weights, const void* x, int32_t batch,
+                               void* out, int32_t* topk_idx, float* topk_w, const void* gamma,
+                               void* ws, int64_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------- prefill -- */
+
+/* The same layer for any number of tokens ([D0] "Optimizations": the
+ * small-batch MoE change also gives the largest gain on an 8,192-token
+ * prefill, on the same packed weights as the large-batch kernel).  The
+ * result per token equals flint_moe_decode's definition.  Tokens are
+ * grouped by expert (histogram, scan, stable permutation by expert then
+ * token), run through grouped GEMMs on MFMA, and un-permuted into the
+ * weighted combine with the shared expert.
+ *   n_tokens  >= 1; ws at least flint_moe_workspace_bytes(shape, n_tokens)
+ * Other arguments as flint_moe_decode. */
+FLINT_API int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_moe_weights* weights,
+                          const void* x, int32_t n_tokens, void* out, int32_t* topk_idx,
+                          float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
+                          void* stream);
+
+/* --------------------------------------------------------------- dense GEMV -- */
+
+/* Small-batch dense GEMV on the same packed NVFP4 weights ([D0]
+ * "Optimizations", third bullet), used for the dense MLP layers.
+ *   codes, scales  (device) packed matrix [rows][cols] (FLINT_EPI_SWIGLU:
+ *                  two matrices [2][rows][cols], gate then up)
+ *   gscale         (device) float [1] (FLINT_EPI_SWIGLU: [2]) tensor scales
+ *   w_bf16         (device) BF16 weights of the same shape, used instead of
+ *                  codes/scales/gscale when flags has FLINT_W_BF16
+ *   flags          FLINT_W_BF16 and/or FLINT_PRE_RMSNORM (then x is the
+ *                  residual and the GEMV input is RMSNorm(x) * gamma)
+ *   x              (device) BF16 [batch][cols];  batch 1..8
+ *   y              (device) BF16 [batch][rows]
+ *   epilogue       FLINT_EPI_NONE | FLINT_EPI_SWIGLU | FLINT_EPI_RESIDUAL
+ *   aux            (device) BF16 [batch][rows], the residual for
+ *                  FLINT_EPI_RESIDUAL (y may equal aux), else NULL
+ *   gamma, rms_eps RMSNorm weight (device, BF16 [cols]) and epsilon with
+ *                  FLINT_PRE_RMSNORM */
+FLINT_API int32_t flint_dense_gemv(const void* codes, const void* scales, const float* gscale,
+                         const void* w_bf16, int32_t rows, int32_t cols, uint32_t flags,
+                         const void* x, int32_t batch, void* y, int32_t epilogue,
+                         const void* aux, const void* gamma, float rms_eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLINT_MOE_H */

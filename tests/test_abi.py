@@ -1,0 +1,124 @@
+"""The C-ABI library loads on the CPU, exports every symbol the header
+declares, and rejects bad arguments before enqueuing anything (these checks
+make no HIP call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a16_moe_decode_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flint_moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^FLINT_API\s+[\w\s\*]+?\b(flint_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declarations_match_binding_list():
+    assert _declared() == sorted(fm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fm.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    # nothing but the C ABI is exported
+    out = os.popen(f"nm -D --defined-only {fm.LIB_PATH}").read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(_declared())
+
+
+def test_version_and_status_strings():
+    assert fm.version().startswith("flint-moe")
+    assert fm.status_string(fm.FLINT_OK) == "ok"
+    assert fm.status_string(fm.FLINT_ERR_UNSUPPORTED).startswith("unsupported")
+    assert fm.status_string(12345) == "unknown"
+
+
+def test_packed_and_workspace_sizes():
+    assert fm.flint_nvfp4_packed_bytes(2, 512, 2048) == (2 * 512 * 1024, 2 * 512 * 128)
+    with pytest.raises(fm.FlintError):
+        fm.flint_nvfp4_packed_bytes(1, 4, 100)          # cols not a multiple of 64
+    s = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
+    ws = fm.flint_moe_workspace_bytes(s, 8)
+    # at least the h buffer: (min(8*6, 256) + 1) slots x 8 tokens x 512 x 2 bytes
+    assert ws >= 49 * 8 * 512 * 2
+    assert fm.flint_moe_workspace_bytes(s, 1) == ws
+    bad = fm.FlintMoeShape(2048, 256, 500, 512, 6, 0, 1e-6)
+    assert fm.lib().flint_moe_workspace_bytes(ctypes.byref(bad), 1) == -fm.FLINT_ERR_UNSUPPORTED
+
+
+def _decode_status(shape, weights, x=16, batch=1, out=32, ws=1024, ws_bytes=1 << 30, gamma=None):
+    L = fm.lib()
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.flint_moe_decode(ctypes.byref(shape), ctypes.byref(weights), v(x), batch, v(out), None,
+                              None, v(gamma), v(ws), ws_bytes, None)
+
+
+def _fake_weights(align=16):
+    w = fm.FlintMoeWeights()
+    for i, (f, _) in enumerate(fm.FlintMoeWeights._fields_):
+        setattr(w, f, 4096 * (i + 1) + (0 if align == 16 else 4))
+    return w
+
+
+def test_decode_validation_codes():
+    s = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
+    w = _fake_weights()
+    assert _decode_status(s, w, batch=9) == fm.FLINT_ERR_UNSUPPORTED     # use prefill
+    assert _decode_status(s, w, batch=0) == fm.FLINT_ERR_INVALID_ARG
+    assert _decode_status(s, w, x=None) == fm.FLINT_ERR_INVALID_ARG
+    assert _decode_status(s, w, x=20) == fm.FLINT_ERR_ALIGNMENT
+    assert _decode_status(s, w, ws=None) == fm.FLINT_ERR_WORKSPACE
+    assert _decode_status(s, w, ws_bytes=100) == fm.FLINT_ERR_WORKSPACE
+    assert _decode_status(s, w, out=16) == fm.FLINT_ERR_INVALID_ARG     # out == x without residual
+    assert _decode_status(s, _fake_weights(align=4)) == fm.FLINT_ERR_ALIGNMENT
+    w2 = _fake_weights()
+    w2.d_codes = None
+    assert _decode_status(s, w2) == fm.FLINT_ERR_INVALID_ARG
+    for bad in (fm.FlintMoeShape(2048, 256, 512, 512, 9, 0, 1e-6),      # top_k > 8
+                fm.FlintMoeShape(2048, 257, 512, 512, 6, 0, 1e-6),      # > 256 experts
+                fm.FlintMoeShape(2000, 256, 512, 512, 6, 0, 1e-6),      # H not a multiple of 64
+                fm.FlintMoeShape(2048, 4, 512, 512, 6, 0, 1e-6),        # top_k > E
+                fm.FlintMoeShape(2048, 256, 512, 512, 6, 0x100, 1e-6)):  # unknown flag
+        assert _decode_status(bad, w) == fm.FLINT_ERR_UNSUPPORTED
+    L = fm.lib()
+    v = ctypes.c_void_p
+    for idx_ptr, want in ((v(4100), fm.FLINT_OK), (v(4098), fm.FLINT_ERR_ALIGNMENT)):
+        # top-k outputs need 4-byte alignment only; validation order puts the
+        # workspace check last, so a good pointer reaches FLINT_ERR_WORKSPACE
+        st = L.flint_moe_decode(ctypes.byref(s), ctypes.byref(w), v(16), 1, v(32), idx_ptr, None,
+                                None, v(1024), 10, None)
+        assert st == (fm.FLINT_ERR_WORKSPACE if want == fm.FLINT_OK else want)
+    pre = fm.FlintMoeShape(2048, 256, 512, 512, 6, fm.FLINT_PRE_RMSNORM, 1e-6)
+    assert _decode_status(pre, w, gamma=None) == fm.FLINT_ERR_INVALID_ARG
+    L = fm.lib()
+    assert L.flint_moe_decode_stage(3, ctypes.byref(s), ctypes.byref(w), ctypes.c_void_p(16), 1,
+                                    ctypes.c_void_p(32), None, None, None, ctypes.c_void_p(1024),
+                                    1 << 30, None) == fm.FLINT_ERR_INVALID_ARG
+
+
+def test_repack_and_dense_validation_codes():
+    L = fm.lib()
+    v = ctypes.c_void_p
+    assert L.flint_moe_repack(v(16), 1, 4, 96, 0, v(32), v(48), 1, None) == fm.FLINT_ERR_UNSUPPORTED
+    assert L.flint_moe_repack(v(16), 1, 4, 64, 7, v(32), v(48), 1, None) == fm.FLINT_ERR_UNSUPPORTED
+    assert L.flint_moe_repack(None, 1, 4, 64, 0, v(32), v(48), 1, None) == fm.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_repack(v(18), 1, 4, 64, 0, v(32), v(48), 1, None) == fm.FLINT_ERR_ALIGNMENT
+    assert L.flint_moe_unpack(v(16), v(32), 0, 4, 64, 0, 1, v(48), None) == fm.FLINT_ERR_INVALID_ARG
+    d = L.flint_dense_gemv
+    eps = ctypes.c_float(1e-6)
+    assert d(v(16), v(32), v(48), None, 64, 64, 0, v(64), 9, v(80), 0, None, None, eps, None) \
+        == fm.FLINT_ERR_UNSUPPORTED
+    assert d(v(16), v(32), v(48), None, 64, 64, 0, v(64), 1, v(80), 5, None, None, eps, None) \
+        == fm.FLINT_ERR_UNSUPPORTED
+    assert d(v(16), v(32), v(48), None, 64, 64, 0, v(64), 1, v(80), fm.FLINT_EPI_RESIDUAL, None,
+             None, eps, None) == fm.FLINT_ERR_INVALID_ARG
+    assert d(v(16), v(32), v(48), None, 64, 64, fm.FLINT_PRE_RMSNORM, v(64), 1, v(80),
+             fm.FLINT_EPI_NONE, None, v(96), eps, None) == fm.FLINT_ERR_UNSUPPORTED
+    assert d(None, None, None, None, 64, 64, fm.FLINT_W_BF16, v(64), 1, v(80), 0, None, None, eps,
+             None) == fm.FLINT_ERR_INVALID_ARG

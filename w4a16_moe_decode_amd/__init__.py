@@ -1,0 +1,350 @@
+"""Python binding of libflint_moe.so, the MI355X (gfx950) W4A16 MoE library.
+
+Thin ctypes marshalling over the C ABI in ``include/flint_moe.h``: every
+function named ``flint_*`` here calls the C function of the same name with
+the data pointers of torch tensors and the current HIP stream.  PyTorch only
+provides device memory and streams; all arithmetic of the layer runs in the
+library's HIP kernels.  There is no CPU fallback: when the library is not
+built, every call raises.
+
+Higher-level helpers (``pack_moe_layer``, ``PackedMoeLayer``) allocate the
+packed planes with torch and fill them with ``flint_moe_repack``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+from ._build import LIB_PATH
+
+# ---------------------------------------------------------------- constants --
+FLINT_OK = 0
+FLINT_ERR_INVALID_ARG = 1
+FLINT_ERR_ALIGNMENT = 2
+FLINT_ERR_UNSUPPORTED = 3
+FLINT_ERR_WORKSPACE = 4
+FLINT_ERR_DEVICE = 5
+
+FLINT_RENORM = 0x1
+FLINT_W_BF16 = 0x2
+FLINT_PRE_RMSNORM = 0x4
+FLINT_RESIDUAL = 0x8
+
+FLINT_SRC_INTERLEAVED = 0
+FLINT_SRC_SCALES_FIRST = 1
+SRC_LAYOUT_CODES = {"interleaved": FLINT_SRC_INTERLEAVED, "scales_first": FLINT_SRC_SCALES_FIRST}
+
+FLINT_EPI_NONE = 0
+FLINT_EPI_SWIGLU = 1
+FLINT_EPI_RESIDUAL = 2
+
+MAX_DECODE_BATCH = 8
+
+# Every symbol the header declares (checked by the CPU export test).
+EXPORTS = (
+    "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
+    "flint_moe_workspace_bytes", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
+    "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_prefill", "flint_dense_gemv",
+)
+
+
+class FlintError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class FlintMoeShape(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("flags", ctypes.c_uint32), ("rms_eps", ctypes.c_float)]
+
+
+class FlintMoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router", "gu_codes", "gu_scales", "d_codes", "d_scales", "gscale",
+        "sh_gu_codes", "sh_gu_scales", "sh_d_codes", "sh_d_scales", "sh_gscale",
+        "gu_bf16", "d_bf16", "sh_gu_bf16", "sh_d_bf16")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+        L.flint_version.restype = ctypes.c_char_p
+        L.flint_status_string.restype = ctypes.c_char_p
+        L.flint_status_string.argtypes = [i32]
+        L.flint_nvfp4_packed_bytes.restype = i32
+        L.flint_nvfp4_packed_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.flint_moe_workspace_bytes.restype = i64
+        L.flint_moe_workspace_bytes.argtypes = [ctypes.POINTER(FlintMoeShape), i32]
+        L.flint_moe_repack.restype = i32
+        L.flint_moe_repack.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp]
+        L.flint_moe_unpack.restype = i32
+        L.flint_moe_unpack.argtypes = [vp, vp, i64, i32, i32, i32, i64, vp, vp]
+        L.flint_nvfp4_dequant.restype = i32
+        L.flint_nvfp4_dequant.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+        dec = [ctypes.POINTER(FlintMoeShape), ctypes.POINTER(FlintMoeWeights), vp, i32, vp, vp, vp,
+               vp, vp, i64, vp]
+        L.flint_moe_decode.restype = i32
+        L.flint_moe_decode.argtypes = dec
+        L.flint_moe_decode_stage.restype = i32
+        L.flint_moe_decode_stage.argtypes = [i32] + dec
+        L.flint_moe_prefill.restype = i32
+        L.flint_moe_prefill.argtypes = dec
+        L.flint_dense_gemv.restype = i32
+        L.flint_dense_gemv.argtypes = [vp, vp, vp, vp, i32, i32, u32, vp, i32, vp, i32, vp, vp,
+                                       ctypes.c_float, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().flint_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().flint_version().decode()
+
+
+def _check(fn: str, status: int):
+    if status != FLINT_OK:
+        raise FlintError(fn, status)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+# -------------------------------------------------------- raw C-ABI calls --
+
+def flint_nvfp4_packed_bytes(n_mats: int, rows: int, cols: int):
+    cb, sb = ctypes.c_int64(), ctypes.c_int64()
+    _check("flint_nvfp4_packed_bytes",
+           lib().flint_nvfp4_packed_bytes(n_mats, rows, cols, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def flint_moe_workspace_bytes(shape: FlintMoeShape, max_tokens: int) -> int:
+    v = lib().flint_moe_workspace_bytes(ctypes.byref(shape), int(max_tokens))
+    if v < 0:
+        raise FlintError("flint_moe_workspace_bytes", -v)
+    return v
+
+
+def flint_moe_repack(src, n_mats, rows, cols, src_layout, dst_codes, dst_scales, dst_mat_stride=1,
+                     stream=None):
+    _check("flint_moe_repack", lib().flint_moe_repack(
+        _p(src), n_mats, rows, cols, src_layout, _p(dst_codes), _p(dst_scales), dst_mat_stride,
+        _stream(stream)))
+
+
+def flint_moe_unpack(codes, scales, n_mats, rows, cols, src_layout, src_mat_stride, dst, stream=None):
+    _check("flint_moe_unpack", lib().flint_moe_unpack(
+        _p(codes), _p(scales), n_mats, rows, cols, src_layout, src_mat_stride, _p(dst),
+        _stream(stream)))
+
+
+def flint_nvfp4_dequant(codes, scales, n_mats, rows, cols, tensor_scale, out, stream=None):
+    _check("flint_nvfp4_dequant", lib().flint_nvfp4_dequant(
+        _p(codes), _p(scales), n_mats, rows, cols, _p(tensor_scale), _p(out), _stream(stream)))
+
+
+def flint_moe_decode(shape, weights, x, batch, out, topk_idx, topk_w, gamma, ws, ws_bytes, stream=None):
+    _check("flint_moe_decode", lib().flint_moe_decode(
+        ctypes.byref(shape), ctypes.byref(weights), _p(x), batch, _p(out), _p(topk_idx), _p(topk_w),
+        _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+
+
+def flint_moe_decode_stage(stage, shape, weights, x, batch, out, topk_idx, topk_w, gamma, ws,
+                           ws_bytes, stream=None):
+    _check("flint_moe_decode_stage", lib().flint_moe_decode_stage(
+        stage, ctypes.byref(shape), ctypes.byref(weights), _p(x), batch, _p(out), _p(topk_idx),
+        _p(topk_w), _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+
+
+def flint_moe_prefill(shape, weights, x, n_tokens, out, topk_idx, topk_w, gamma, ws, ws_bytes,
+                      stream=None):
+    _check("flint_moe_prefill", lib().flint_moe_prefill(
+        ctypes.byref(shape), ctypes.byref(weights), _p(x), n_tokens, _p(out), _p(topk_idx),
+        _p(topk_w), _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+
+
+def flint_dense_gemv(codes, scales, gscale, w_bf16, rows, cols, flags, x, batch, y, epilogue,
+                     aux=None, gamma=None, rms_eps=1e-6, stream=None):
+    _check("flint_dense_gemv", lib().flint_dense_gemv(
+        _p(codes), _p(scales), _p(gscale), _p(w_bf16), rows, cols, flags, _p(x), batch, _p(y),
+        epilogue, _p(aux), _p(gamma), ctypes.c_float(rms_eps), _stream(stream)))
+
+
+# ------------------------------------------------------------ conveniences --
+
+def _empty_u8(n: int, device) -> torch.Tensor:
+    return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
+def repack_matrices(src: torch.Tensor, layout: str = "interleaved", out_codes=None, out_scales=None,
+                    mat_stride: int = 1):
+    """Repack source super-blocks uint8 [n][rows][cols/64][36] (on the GPU)
+    into new (or given) packed planes; returns (codes, scales)."""
+    n, rows, nb, _ = src.shape
+    cols = nb * 64
+    cb, sb = flint_nvfp4_packed_bytes(n, rows, cols)
+    if out_codes is None:
+        out_codes = _empty_u8(cb, src.device)
+        out_scales = _empty_u8(sb, src.device)
+    flint_moe_repack(src, n, rows, cols, SRC_LAYOUT_CODES[layout], out_codes, out_scales, mat_stride)
+    return out_codes, out_scales
+
+
+@dataclasses.dataclass
+class PackedMoeLayer:
+    """Device tensors of one MoE layer in the packed layout (plus, optionally,
+    BF16 copies for the W16A16 path) and the matching C structs."""
+
+    hidden: int
+    n_experts: int
+    inter: int
+    shared_inter: int
+    router: torch.Tensor
+    gu_codes: torch.Tensor
+    gu_scales: torch.Tensor
+    d_codes: torch.Tensor
+    d_scales: torch.Tensor
+    gscale: torch.Tensor
+    sh_gu_codes: Optional[torch.Tensor] = None
+    sh_gu_scales: Optional[torch.Tensor] = None
+    sh_d_codes: Optional[torch.Tensor] = None
+    sh_d_scales: Optional[torch.Tensor] = None
+    sh_gscale: Optional[torch.Tensor] = None
+    gu_bf16: Optional[torch.Tensor] = None
+    d_bf16: Optional[torch.Tensor] = None
+    sh_gu_bf16: Optional[torch.Tensor] = None
+    sh_d_bf16: Optional[torch.Tensor] = None
+
+    def shape(self, top_k: int, flags: int = 0, rms_eps: float = 1e-6) -> FlintMoeShape:
+        return FlintMoeShape(self.hidden, self.n_experts, self.inter, self.shared_inter, top_k,
+                             flags, rms_eps)
+
+    def weights(self) -> FlintMoeWeights:
+        w = FlintMoeWeights()
+        for f, _ in FlintMoeWeights._fields_:
+            t = getattr(self, f)
+            setattr(w, f, None if t is None else t.data_ptr())
+        return w
+
+    def nvfp4_bytes(self) -> int:
+        return sum(t.numel() for t in (self.gu_codes, self.gu_scales, self.d_codes, self.d_scales)
+                   ) + (0 if self.sh_gu_codes is None else sum(
+                       t.numel() for t in (self.sh_gu_codes, self.sh_gu_scales, self.sh_d_codes,
+                                           self.sh_d_scales)))
+
+    def add_bf16(self):
+        """Attach BF16 copies of the weights (the exact dequantisation of the
+        packed NVFP4 matrices, which is exact when the per-tensor scales are
+        powers of two) for the W16A16 path."""
+        dev = self.gu_codes.device
+        H, E, I, SI = self.hidden, self.n_experts, self.inter, self.shared_inter
+        gs = self.gscale
+        ts_gu = torch.stack([gs[:, 0], gs[:, 1]], 1).reshape(-1).contiguous()
+        ts_d = gs[:, 2].contiguous()
+        self.gu_bf16 = _dequant_bf16(self.gu_codes, self.gu_scales, 2 * E, I, H, ts_gu, dev)
+        self.d_bf16 = _dequant_bf16(self.d_codes, self.d_scales, E, H, I, ts_d, dev)
+        if SI:
+            sg = self.sh_gscale.reshape(-1)
+            self.sh_gu_bf16 = _dequant_bf16(self.sh_gu_codes, self.sh_gu_scales, 2, SI, H,
+                                            sg[:2].clone(), dev)
+            self.sh_d_bf16 = _dequant_bf16(self.sh_d_codes, self.sh_d_scales, 1, H, SI,
+                                           sg[2:3].clone(), dev)
+        return self
+
+
+def _dequant_bf16(codes, scales, n, rows, cols, ts, dev, chunk_mats: int = 16):
+    out = torch.empty((n, rows, cols), dtype=torch.bfloat16, device=dev)
+    tmp = torch.empty((min(n, chunk_mats), rows, cols), dtype=torch.float32, device=dev)
+    cpm, spm = rows * cols // 2, rows * cols // 16
+    for m0 in range(0, n, chunk_mats):
+        m1 = min(n, m0 + chunk_mats)
+        flint_nvfp4_dequant(codes[m0 * cpm:m1 * cpm], scales[m0 * spm:m1 * spm], m1 - m0, rows, cols,
+                            ts[m0:m1].clone(), tmp[: m1 - m0])
+        out[m0:m1].copy_(tmp[: m1 - m0])
+    return out
+
+
+def pack_moe_layer(router: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor,
+                   gscale: torch.Tensor, sh_gate=None, sh_up=None, sh_down=None, sh_gscale=None,
+                   layout: str = "interleaved", device="cuda") -> PackedMoeLayer:
+    """Upload a layer given in source format (see gen.MoeLayerSource) and
+    repack it on the GPU with flint_moe_repack."""
+    E, I, nbh, _ = gate.shape
+    H = nbh * 64
+    SI = 0 if sh_gate is None else sh_gate.shape[1]
+    lay = SRC_LAYOUT_CODES[layout]
+    dev = torch.device(device)
+    gu_c = _empty_u8(2 * E * I * H // 2, dev)
+    gu_s = _empty_u8(2 * E * I * H // 16, dev)
+    d_c = _empty_u8(E * H * I // 2, dev)
+    d_s = _empty_u8(E * H * I // 16, dev)
+    g_dev, u_dev, dn_dev = gate.to(dev), up.to(dev), down.to(dev)
+    flint_moe_repack(g_dev, E, I, H, lay, gu_c, gu_s, 2)
+    flint_moe_repack(u_dev, E, I, H, lay, gu_c[I * H // 2:], gu_s[I * H // 16:], 2)
+    flint_moe_repack(dn_dev, E, H, I, lay, d_c, d_s, 1)
+    layer = PackedMoeLayer(H, E, I, SI, router.to(dev).contiguous(), gu_c, gu_s, d_c, d_s,
+                           gscale.to(dev, torch.float32).contiguous())
+    if SI:
+        sgc = _empty_u8(2 * SI * H // 2, dev)
+        sgs = _empty_u8(2 * SI * H // 16, dev)
+        sdc = _empty_u8(H * SI // 2, dev)
+        sds = _empty_u8(H * SI // 16, dev)
+        flint_moe_repack(sh_gate.to(dev), 1, SI, H, lay, sgc, sgs, 1)
+        flint_moe_repack(sh_up.to(dev), 1, SI, H, lay, sgc[SI * H // 2:], sgs[SI * H // 16:], 1)
+        flint_moe_repack(sh_down.to(dev), 1, H, SI, lay, sdc, sds, 1)
+        sg = torch.zeros(4, dtype=torch.float32, device=dev)   # 16-byte aligned [3] (+pad)
+        sg[:3] = sh_gscale.reshape(-1).to(dev, torch.float32)
+        layer.sh_gu_codes, layer.sh_gu_scales = sgc, sgs
+        layer.sh_d_codes, layer.sh_d_scales = sdc, sds
+        layer.sh_gscale = sg
+    return layer
+
+
+class DecodeRunner:
+    """Holds a zero-filled workspace and calls flint_moe_decode for a layer."""
+
+    def __init__(self, layer: PackedMoeLayer, top_k: int, flags: int = 0, rms_eps: float = 1e-6):
+        self.layer = layer
+        self.shape = layer.shape(top_k, flags, rms_eps)
+        self.cweights = layer.weights()
+        self.ws_bytes = flint_moe_workspace_bytes(self.shape, MAX_DECODE_BATCH)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=layer.router.device)
+
+    def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, topk_idx=None,
+                 topk_w=None, gamma=None, stream=None):
+        B = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        flint_moe_decode(self.shape, self.cweights, x, B, out, topk_idx, topk_w, gamma, self.ws,
+                         self.ws_bytes, stream)
+        return out
+
+    def stage(self, stage: int, x, out, topk_idx=None, topk_w=None, gamma=None, stream=None):
+        flint_moe_decode_stage(stage, self.shape, self.cweights, x, x.shape[0], out, topk_idx,
+                               topk_w, gamma, self.ws, self.ws_bytes, stream)
