@@ -19,6 +19,8 @@ Reported (one JSON line):
   cpu_baseline the float64 NumPy oracle on a bounded sample of the same
                workload, on the host, one thread
   batch8       the same layer at batch 8 (up to 48 distinct experts)
+  decode_step  the 49-sublayer decode step (47 MoE + 2 dense, RMSNorm,
+               residual) at batch 1, NVFP4 and BF16 weights
 The timed loops replay HIP graphs of the layer calls, so host launch cost is
 not on the clock.
 """
@@ -151,6 +153,70 @@ class Bench:
         return res
 
 
+def bench_step(args, dev, batch=1, n_moe=47, n_dense=2, reps=20):
+    """The decode step over the MoE part of the model: 47 MoE sublayers
+    (Flint shape, own seeded weights, 21.4 GB NVFP4) and 2 dense SwiGLU
+    sublayers (intermediate 5632), pre-norm RMSNorm, residual in place; then
+    the same step with BF16 weights (the exact dequantisation, 76 GB)."""
+    shape = gen.SHAPE_FLINT
+    layers, gmo, dl, gde = [], [], [], []
+    for l in range(n_moe):
+        src = gen.moe_layer_source(shape, gen.seed_for(args.seed, "step-moe", l), dev)
+        layers.append(fm.pack_moe_layer(src.router, src.gate, src.up, src.down, src.gscale,
+                                        src.sh_gate, src.sh_up, src.sh_down, src.sh_gscale,
+                                        src.layout, dev))
+        gmo.append(gen.rmsnorm_gamma(gen.seed_for(args.seed, "step-gm", l), shape.hidden, dev))
+        del src
+    for l in range(n_dense):
+        g, u, d, ts = gen.dense_mlp_source(shape.hidden, gen.DENSE_INTER,
+                                           gen.seed_for(args.seed, "step-dense", l), dev)
+        dl.append(fm.pack_dense_mlp(g, u, d, ts, device=dev))
+        gde.append(gen.rmsnorm_gamma(gen.seed_for(args.seed, "step-gd", l), shape.hidden, dev))
+    torch.cuda.synchronize()
+    eb = expert_bytes(shape)
+    dense_bytes = sum(D.gu_codes.numel() + D.gu_scales.numel() + D.d_codes.numel() + D.d_scales.numel()
+                      for D in dl)
+    out = {}
+    for wbf16 in (False, True):
+        if wbf16:
+            for L in layers:
+                L.add_bf16()
+            for D in dl:
+                D.add_bf16()
+            torch.cuda.synchronize()
+        step = fm.DecodeStep(layers, gmo, dl, gde, shape.top_k, wbf16=wbf16)
+        x0 = gen.activations(gen.seed_for(args.seed, "step-x"), batch, shape.hidden, dev)
+        x = x0.clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(x)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                step(x)
+        g.replay()
+        x.copy_(x0)
+        secs = timed(g) / reps
+        idx = step.topk_idx[:, :batch * shape.top_k].view(n_moe, batch * shape.top_k).cpu()
+        distinct = [len(set(idx[l].tolist())) for l in range(n_moe)]
+        mult = 2.0 / (0.5 + 1.0 / 16) if wbf16 else 1.0      # bf16 bytes per weight vs nvfp4
+        nb = sum(mult * (d * (eb["gate_up"] + eb["down"]) + eb["sh_gate_up"] + eb["sh_down"])
+                 + shape.n_experts * shape.hidden * 2 + 4 * batch * shape.hidden for d in distinct)
+        nb += mult * dense_bytes
+        key = "bf16" if wbf16 else "nvfp4"
+        out[key] = {"us_per_step": round(secs * 1e6, 2), "tokens_per_s": round(batch / secs, 1),
+                    "tb_s": round(nb / secs / 1e12, 4), "bytes_per_step": int(nb)}
+        print(f"[bench] decode step {key}: {secs * 1e6:.1f} us/step, {batch / secs:.0f} tok/s, "
+              f"{nb / secs / 1e12:.3f} TB/s", file=sys.stderr, flush=True)
+        del g, step
+    out.update({"layers": n_moe + n_dense, "moe_layers": n_moe, "dense_layers": n_dense, "batch": batch,
+                "dense_inter": gen.DENSE_INTER})
+    return out
+
+
 def timed(graph, reps=1):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -198,6 +264,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch8", action="store_true")
+    ap.add_argument("--no-step", action="store_true", help="skip the 49-layer decode step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -271,6 +338,10 @@ def main():
                           "distinct_experts": round(r8["distinct"], 2),
                           "stage_us": [round(v, 3) for v in r8["stage_us"]],
                           "gate_up_frac": round(gu8 / HBM_PEAK_GBS, 4)}
+    if not args.no_step:
+        del layers
+        torch.cuda.empty_cache()
+        line["decode_step"] = bench_step(args, dev)
     if not args.no_cpu:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(src0, shape, args.cpu_seconds)

@@ -19,7 +19,7 @@ import torch
 
 import gen
 import w4a16_moe_decode_amd as fm
-from oracle import moe
+from oracle import formats, moe
 
 GAP_EXEMPT = 1e-5
 REL_TOL = 1e-2
@@ -33,6 +33,23 @@ def oracle_experts(src: gen.MoeLayerSource) -> moe.ExpertSet:
         gen.numpy_f64(src.router), u8(src.gate), u8(src.up), u8(src.down), src.gscale.numpy(),
         u8(src.sh_gate) if sh else None, u8(src.sh_up) if sh else None,
         u8(src.sh_down) if sh else None, src.sh_gscale.numpy(), src.layout)
+
+
+def oracle_experts_lazy(src: gen.MoeLayerSource) -> moe.ExpertSet:
+    """Oracle expert set over a source layer that may live on the GPU: an
+    expert's bytes are copied to the host only when the oracle asks for it."""
+    gs = src.gscale.cpu().numpy().astype(np.float64)
+    sg = src.sh_gscale.cpu().numpy().astype(np.float64).reshape(3)
+    dec = lambda t, g: formats.decode_source_matrix(t.cpu().numpy(), src.layout, g)
+
+    def load(e):
+        if e is None:
+            if src.sh_gate is None:
+                return None
+            return dec(src.sh_gate[0], sg[0]), dec(src.sh_up[0], sg[1]), dec(src.sh_down[0], sg[2])
+        return dec(src.gate[e], gs[e, 0]), dec(src.up[e], gs[e, 1]), dec(src.down[e], gs[e, 2])
+
+    return moe.ExpertSet(router=gen.numpy_f64(src.router), n_experts=src.router.shape[0], _loader=load)
 
 
 def pack(src: gen.MoeLayerSource, device="cuda") -> fm.PackedMoeLayer:
@@ -54,6 +71,28 @@ def compare_outputs(got: np.ndarray, want: np.ndarray, what: str = "out"):
             continue
         assert err <= REL_TOL * scale, f"{what}[{t}]: max|d|={err:.4g} > {REL_TOL}*{scale:.4g}"
         cos = float(g @ w / (np.linalg.norm(g) * np.linalg.norm(w) + 1e-300))
+        assert cos >= COS_MIN, f"{what}[{t}]: cosine {cos:.6f}"
+
+
+def bf16_ulp(v):
+    """Spacing of bfloat16 values at |v| (8 significant bits)."""
+    a = np.maximum(np.abs(np.asarray(v, dtype=np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(int) - 7)
+
+
+def compare_residual(got_out: np.ndarray, want_out: np.ndarray, x_in: np.ndarray, what: str):
+    """A sublayer that updates the residual, x_out = BF16(x_in + y): the
+    update y is held to the output bar, plus one BF16 ulp of x_out, since a
+    last-bit difference in y can move the rounding of the sum by one ulp."""
+    got_out, want_out, x_in = (np.atleast_2d(a) for a in (got_out, want_out, x_in))
+    assert np.all(np.isfinite(got_out)), f"{what}: non-finite GPU values"
+    for t in range(want_out.shape[0]):
+        dg, dw = got_out[t] - x_in[t], want_out[t] - x_in[t]
+        scale = np.max(np.abs(dw))
+        err = np.abs(got_out[t] - want_out[t])
+        allow = REL_TOL * scale + bf16_ulp(want_out[t])
+        assert np.all(err <= allow), f"{what}[{t}]: max excess {np.max(err - allow):.4g}"
+        cos = float(dg @ dw / (np.linalg.norm(dg) * np.linalg.norm(dw) + 1e-300))
         assert cos >= COS_MIN, f"{what}[{t}]: cosine {cos:.6f}"
 
 

@@ -348,3 +348,96 @@ class DecodeRunner:
     def stage(self, stage: int, x, out, topk_idx=None, topk_w=None, gamma=None, stream=None):
         flint_moe_decode_stage(stage, self.shape, self.cweights, x, x.shape[0], out, topk_idx,
                                topk_w, gamma, self.ws, self.ws_bytes, stream)
+
+
+@dataclasses.dataclass
+class PackedDenseMlp:
+    """A dense SwiGLU MLP in the packed layout: gate/up pair [2][I][H] and
+    down [H][I], their FP32 tensor scales, and optional BF16 copies."""
+
+    hidden: int
+    inter: int
+    gu_codes: torch.Tensor
+    gu_scales: torch.Tensor
+    d_codes: torch.Tensor
+    d_scales: torch.Tensor
+    gu_gscale: torch.Tensor      # f32 [4]: gate, up, 0, 0
+    d_gscale: torch.Tensor       # f32 [4]: down, 0, 0, 0
+    gu_bf16: Optional[torch.Tensor] = None
+    d_bf16: Optional[torch.Tensor] = None
+
+    def add_bf16(self):
+        dev = self.gu_codes.device
+        H, I = self.hidden, self.inter
+        self.gu_bf16 = _dequant_bf16(self.gu_codes, self.gu_scales, 2, I, H, self.gu_gscale[:2].clone(), dev)
+        self.d_bf16 = _dequant_bf16(self.d_codes, self.d_scales, 1, H, I, self.d_gscale[:1].clone(), dev)
+        return self
+
+
+def pack_dense_mlp(gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor, gscale: torch.Tensor,
+                   layout: str = "interleaved", device="cuda") -> PackedDenseMlp:
+    """Repack a dense MLP given in source format (gate/up [1][I][H/64][36],
+    down [1][H][I/64][36], gscale [1][3]) on the GPU."""
+    dev = torch.device(device)
+    _, I, nbh, _ = gate.shape
+    H = nbh * 64
+    gu_c = _empty_u8(2 * I * H // 2, dev)
+    gu_s = _empty_u8(2 * I * H // 16, dev)
+    repack_matrices(gate.to(dev), layout, gu_c, gu_s)
+    repack_matrices(up.to(dev), layout, gu_c[I * H // 2:], gu_s[I * H // 16:])
+    d_c, d_s = repack_matrices(down.to(dev), layout)
+    g = gscale.reshape(-1).to(dev, torch.float32)
+    gg = torch.zeros(4, dtype=torch.float32, device=dev)
+    gg[:2] = g[:2]
+    gd = torch.zeros(4, dtype=torch.float32, device=dev)
+    gd[:1] = g[2:3]
+    return PackedDenseMlp(H, I, gu_c, gu_s, d_c, d_s, gg, gd)
+
+
+class DecodeStep:
+    """One decode step over a stack of pre-norm residual sublayers: the MoE
+    sublayers (flint_moe_decode with PRE_RMSNORM | RESIDUAL, updating the
+    residual in place), then the dense SwiGLU sublayers (flint_dense_gemv:
+    gate/up with the fused RMSNorm, then down with the residual epilogue).
+    Every call enqueues kernels only, so a step can be captured in a graph."""
+
+    def __init__(self, moe_layers, moe_gammas, dense_layers, dense_gammas, top_k: int,
+                 flags: int = 0, wbf16: bool = False, rms_eps: float = 1e-6, max_batch: int = 8):
+        self.moe_layers, self.moe_gammas = moe_layers, moe_gammas
+        self.dense_layers, self.dense_gammas = dense_layers, dense_gammas
+        self.wbf16 = wbf16
+        self.eps = rms_eps
+        f = flags | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | (FLINT_W_BF16 if wbf16 else 0)
+        self.shapes = [L.shape(top_k, f, rms_eps) for L in moe_layers]
+        self.cweights = [L.weights() for L in moe_layers]
+        dev = moe_layers[0].router.device if moe_layers else dense_layers[0].gu_codes.device
+        ws = max([flint_moe_workspace_bytes(s, max_batch) for s in self.shapes] + [256])
+        self.ws_bytes = ws
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev)
+        self.h = [torch.empty((max_batch, d.inter), dtype=torch.bfloat16, device=dev)
+                  for d in dense_layers]
+        K = top_k
+        self.topk_idx = torch.zeros((len(moe_layers), max_batch * K), dtype=torch.int32, device=dev)
+        self.topk_w = torch.zeros((len(moe_layers), max_batch * K), dtype=torch.float32, device=dev)
+
+    def __call__(self, x: torch.Tensor, record=None, stream=None):
+        """Runs the step on x [B][H] (BF16, updated in place).  If ``record``
+        is a list, a copy of the residual entering each sublayer is appended
+        (for per-layer checks; not for graph capture)."""
+        B = x.shape[0]
+        for i, (L, g) in enumerate(zip(self.moe_layers, self.moe_gammas)):
+            if record is not None:
+                record.append(x.clone())
+            flint_moe_decode(self.shapes[i], self.cweights[i], x, B, x, self.topk_idx[i], self.topk_w[i],
+                             g, self.ws, self.ws_bytes, stream)
+        fl = FLINT_W_BF16 if self.wbf16 else 0
+        for j, (d, g) in enumerate(zip(self.dense_layers, self.dense_gammas)):
+            if record is not None:
+                record.append(x.clone())
+            h = self.h[j][:B]
+            flint_dense_gemv(d.gu_codes, d.gu_scales, d.gu_gscale, d.gu_bf16, d.inter, d.hidden,
+                             fl | FLINT_PRE_RMSNORM, x, B, h, FLINT_EPI_SWIGLU, gamma=g,
+                             rms_eps=self.eps, stream=stream)
+            flint_dense_gemv(d.d_codes, d.d_scales, d.d_gscale, d.d_bf16, d.hidden, d.inter, fl, h, B, x,
+                             FLINT_EPI_RESIDUAL, aux=x, stream=stream)
+        return x
