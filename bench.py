@@ -21,6 +21,8 @@ Reported (one JSON line):
   batch8       the same layer at batch 8 (up to 48 distinct experts)
   decode_step  the 49-sublayer decode step (47 MoE + 2 dense, RMSNorm,
                residual) at batch 1, NVFP4 and BF16 weights
+  prefill      8,192 tokens through one layer: TFLOP/s against the BF16
+               MFMA peak, for i.i.d. and for skewed (correlated) tokens
 The timed loops replay HIP graphs of the layer calls, so host launch cost is
 not on the clock.
 """
@@ -217,6 +219,50 @@ def bench_step(args, dev, batch=1, n_moe=47, n_dense=2, reps=20):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(shape: gen.MoeShape, T: int) -> float:
+    H, E, I, SI, K = shape.hidden, shape.n_experts, shape.inter, shape.shared_inter, shape.top_k
+    return 2.0 * T * (H * E + K * 3 * I * H + 3 * SI * H)
+
+
+def bench_prefill(layer, shape, seed, T=8192, reps=5):
+    """The 8,192-token prefill through one Flint-shaped layer (NVFP4), for
+    i.i.d. tokens and for correlated tokens whose routing is skewed."""
+    out = {}
+    runner = fm.PrefillRunner(layer, shape.top_k, T, 0)
+    dev = layer.router.device
+    idx = torch.zeros((T, shape.top_k), dtype=torch.int32, device=dev)
+    w = torch.zeros((T, shape.top_k), dtype=torch.float32, device=dev)
+    for kind in ("iid", "correlated"):
+        x = gen.activations(gen.seed_for(seed, "prefill", kind), T, shape.hidden, dev, kind)
+        y = torch.empty_like(x)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            runner(x, y, idx, w)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                runner(x, y, idx, w)
+        g.replay()
+        secs = timed(g) / reps
+        hist = torch.bincount(idx.reshape(-1).long(), minlength=shape.n_experts).float()
+        fl = prefill_flops(shape, T)
+        out[kind] = {"us": round(secs * 1e6, 1), "tflops": round(fl / secs / 1e12, 1),
+                     "frac_mfma_peak": round(fl / secs / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "hist_max_over_mean": round(float(hist.max() / hist.mean()), 2)}
+        print(f"[bench] prefill {kind}: {secs * 1e6:.1f} us, {fl / secs / 1e12:.1f} TFLOP/s, "
+              f"hist max/mean {out[kind]['hist_max_over_mean']}", file=sys.stderr, flush=True)
+        del g
+    out.update({"tokens": T, "gflop": round(prefill_flops(shape, T) / 1e9, 2),
+                "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "dtype": "bf16 mfma (nvfp4 weights dequantised in LDS)"})
+    return out
+
+
 def timed(graph, reps=1):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -265,6 +311,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="skip the 49-layer decode step")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 8,192-token prefill")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -338,6 +385,8 @@ def main():
                           "distinct_experts": round(r8["distinct"], 2),
                           "stage_us": [round(v, 3) for v in r8["stage_us"]],
                           "gate_up_frac": round(gu8 / HBM_PEAK_GBS, 4)}
+    if not args.no_prefill:
+        line["prefill"] = bench_prefill(layers[0], shape, args.seed)
     if not args.no_step:
         del layers
         torch.cuda.empty_cache()

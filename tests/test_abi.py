@@ -47,7 +47,9 @@ def test_packed_and_workspace_sizes():
     ws = fm.flint_moe_workspace_bytes(s, 8)
     # at least the h buffer: (min(8*6, 256) + 1) slots x 8 tokens x 512 x 2 bytes
     assert ws >= 49 * 8 * 512 * 2
-    assert fm.flint_moe_workspace_bytes(s, 1) == ws
+    # decode needs the same layout for any batch; prefill grows with tokens
+    assert fm.flint_moe_workspace_bytes(s, 1) <= ws
+    assert fm.flint_moe_workspace_bytes(s, 8192) > 8192 * 6 * 2048 * 4
     bad = fm.FlintMoeShape(2048, 256, 500, 512, 6, 0, 1e-6)
     assert fm.lib().flint_moe_workspace_bytes(ctypes.byref(bad), 1) == -fm.FLINT_ERR_UNSUPPORTED
 

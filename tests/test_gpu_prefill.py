@@ -1,0 +1,113 @@
+"""Prefill MoE layer (flint_moe_prefill: router GEMM, top-k, stable
+permutation by expert, grouped GEMMs on MFMA, combine) on the GPU against
+the oracle's per-token definition.  Routing is checked for every token;
+outputs for every token at small sizes and for a sample of tokens at the
+8,192-token size."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import w4a16_moe_decode_amd as fm
+from _parity import check_routing, compare_outputs, oracle_experts, pack
+from oracle import bf16 as obf
+from oracle import moe
+
+pytestmark = pytest.mark.gpu
+
+TINY = gen.SHAPE_TINY
+FLINT = gen.SHAPE_FLINT
+
+
+def run_prefill(shape, src, layer, T, seed, flags=0, x_kind="iid", sample=None, wbf16=False):
+    x = gen.activations(gen.seed_for(seed, "px", T), T, shape.hidden, "cpu", x_kind)
+    gamma = gen.rmsnorm_gamma(gen.seed_for(seed, "pg"), shape.hidden)
+    f = flags | (fm.FLINT_W_BF16 if wbf16 else 0)
+    runner = fm.PrefillRunner(layer, shape.top_k, T, f)
+    idx = torch.full((T, shape.top_k), -1, dtype=torch.int32, device="cuda")
+    wts = torch.zeros((T, shape.top_k), dtype=torch.float32, device="cuda")
+    out = runner(x.cuda(), topk_idx=idx, topk_w=wts, gamma=gamma.cuda())
+    torch.cuda.synchronize()
+    ex = oracle_experts(src)
+    xo = gen.numpy_f64(x)
+    renorm = bool(flags & fm.FLINT_RENORM)
+    xin = moe.rmsnorm(xo, gen.numpy_f64(gamma)) if flags & fm.FLINT_PRE_RMSNORM else xo
+    # routing of every token
+    r = moe.route(xin, ex.router, shape.top_k, renorm)
+    forced = check_routing(idx.cpu().numpy(), wts.cpu().numpy(), r, renorm)
+    toks = np.arange(T) if sample is None else np.asarray(sample)
+    want, _ = moe.moe_layer(xin[toks], ex, shape.top_k, renorm, forced_idx=forced[toks])
+    if flags & fm.FLINT_RESIDUAL:
+        want = obf.round_bf16(xo[toks] + want)
+    compare_outputs(gen.numpy_f64(out)[toks], want)
+    return idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [1, 7, 64, 130, 333])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_tiny_prefill(T, renorm):
+    src = gen.moe_layer_source(TINY, 31)
+    run_prefill(TINY, src, pack(src), T, 32, fm.FLINT_RENORM if renorm else 0)
+
+
+@pytest.mark.parametrize("shape,T", [
+    (gen.MoeShape(hidden=576, n_experts=40, inter=192, shared_inter=320, top_k=5), 97),
+    (gen.MoeShape(hidden=256, n_experts=16, inter=64, shared_inter=0, top_k=8), 150),
+    (gen.MoeShape(hidden=64, n_experts=1, inter=64, shared_inter=64, top_k=1), 5),
+])
+def test_ragged_prefill(shape, T):
+    src = gen.moe_layer_source(shape, 33)
+    layer = pack(src)
+    run_prefill(shape, src, layer, T, 34)
+    layer.add_bf16()
+    run_prefill(shape, src, layer, T, 35, wbf16=True)
+
+
+def test_prefill_norm_residual_and_skew():
+    src = gen.moe_layer_source(TINY, 36)
+    idx = run_prefill(TINY, src, pack(src), 300, 37, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL,
+                      x_kind="correlated")
+    h = np.bincount(idx.reshape(-1), minlength=TINY.n_experts)
+    assert h.sum() == 300 * TINY.top_k and h.max() > 2 * h.mean()   # skewed histogram
+
+
+@pytest.fixture(scope="module")
+def flint():
+    src = gen.moe_layer_source(FLINT, 200, "cpu")
+    return src, pack(src)
+
+
+def test_flint_prefill_1024(flint):
+    src, layer = flint
+    run_prefill(FLINT, src, layer, 1024, 38, sample=np.arange(0, 1024, 7))
+
+
+@pytest.mark.parametrize("x_kind", ["iid", "correlated"])
+def test_flint_prefill_8192(flint, x_kind):
+    src, layer = flint
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(8192, 48, replace=False))
+    idx = run_prefill(FLINT, src, layer, 8192, 39, fm.FLINT_RENORM, x_kind=x_kind, sample=sample)
+    h = np.bincount(idx.reshape(-1), minlength=FLINT.n_experts)
+    assert h.sum() == 8192 * FLINT.top_k
+
+
+def test_prefill_matches_decode(flint):
+    """Prefill of a few tokens equals decode of the same tokens (same
+    definition; only fp32 summation order may differ)."""
+    src, layer = flint
+    x = gen.activations(40, 8, FLINT.hidden).cuda()
+    d = fm.DecodeRunner(layer, FLINT.top_k, 0)(x)
+    p = fm.PrefillRunner(layer, FLINT.top_k, 8, 0)(x)
+    torch.cuda.synchronize()
+    compare_outputs(gen.numpy_f64(p), gen.numpy_f64(d), "prefill vs decode")
+
+
+def test_prefill_bit_reproducible(flint):
+    src, layer = flint
+    x = gen.activations(41, 700, FLINT.hidden).cuda()
+    r = fm.PrefillRunner(layer, FLINT.top_k, 700, 0)
+    a = r(x).clone()
+    b = r(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

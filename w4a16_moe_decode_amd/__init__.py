@@ -441,3 +441,28 @@ class DecodeStep:
             flint_dense_gemv(d.d_codes, d.d_scales, d.d_gscale, d.d_bf16, d.hidden, d.inter, fl, h, B, x,
                              FLINT_EPI_RESIDUAL, aux=x, stream=stream)
         return x
+
+
+class PrefillRunner:
+    """Holds a workspace for up to ``max_tokens`` tokens and calls
+    flint_moe_prefill for a layer."""
+
+    def __init__(self, layer: PackedMoeLayer, top_k: int, max_tokens: int, flags: int = 0,
+                 rms_eps: float = 1e-6):
+        self.layer = layer
+        self.shape = layer.shape(top_k, flags, rms_eps)
+        self.cweights = layer.weights()
+        self.max_tokens = max_tokens
+        self.ws_bytes = flint_moe_workspace_bytes(self.shape, max_tokens)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=layer.router.device)
+
+    def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, topk_idx=None, topk_w=None,
+                 gamma=None, stream=None):
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"{T} tokens > workspace capacity {self.max_tokens}")
+        if out is None:
+            out = torch.empty_like(x)
+        flint_moe_prefill(self.shape, self.cweights, x, T, out, topk_idx, topk_w, gamma, self.ws,
+                          self.ws_bytes, stream)
+        return out

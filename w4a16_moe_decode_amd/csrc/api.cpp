@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "common.hpp"
+#include "prefill_ws.hpp"
 
 namespace flint {
 
@@ -100,6 +101,10 @@ int to_status(hipError_t e) { return e == hipSuccess ? FLINT_OK : FLINT_ERR_DEVI
 
 int decode_max_slots(const flint_moe_shape& s, int batch);
 
+int64_t prefill_ws_bytes(const flint_moe_shape& s, int T) {
+  return carve_prefill_ws(nullptr, s, T).bytes;
+}
+
 int64_t decode_ws_bytes(const flint_moe_shape& s, int max_batch) {
   DecodeWs ws = carve_decode_ws(nullptr, s, max_batch);
   return ws.bytes;
@@ -168,8 +173,10 @@ int64_t flint_moe_workspace_bytes(const flint_moe_shape* shape, int32_t max_toke
   const int st = check_shape(shape);
   if (st != FLINT_OK) return -(int64_t)st;
   if (max_tokens <= 0) return -(int64_t)FLINT_ERR_INVALID_ARG;
-  if (max_tokens > FLINT_MAX_DECODE_BATCH) return -(int64_t)FLINT_ERR_UNSUPPORTED;
-  return decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH);
+  const int64_t pre = prefill_ws_bytes(*shape, max_tokens);
+  if (max_tokens > FLINT_MAX_DECODE_BATCH) return pre;
+  const int64_t dec = decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH);
+  return dec > pre ? dec : pre;
 }
 
 int32_t flint_moe_repack(const void* src, int64_t n_mats, int32_t rows, int32_t cols,
@@ -272,9 +279,26 @@ int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_moe_weights*
                           const void* x, int32_t n_tokens, void* out, int32_t* topk_idx,
                           float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
                           void* stream) {
-  (void)shape; (void)weights; (void)x; (void)n_tokens; (void)out; (void)topk_idx; (void)topk_w;
-  (void)gamma; (void)ws; (void)ws_bytes; (void)stream;
-  return FLINT_ERR_UNSUPPORTED;
+  int st = check_shape(shape);
+  if (st != FLINT_OK) return st;
+  st = check_weights(shape, weights);
+  if (st != FLINT_OK) return st;
+  if (n_tokens <= 0) return FLINT_ERR_INVALID_ARG;
+  if (n_tokens > (1 << 22)) return FLINT_ERR_UNSUPPORTED;
+  FLINT_NEED(x);
+  FLINT_NEED(out);
+  if (out == x && !(shape->flags & FLINT_RESIDUAL)) return FLINT_ERR_INVALID_ARG;
+  if (shape->flags & FLINT_PRE_RMSNORM) FLINT_NEED(gamma);
+  if (topk_idx && !aligned4(topk_idx)) return FLINT_ERR_ALIGNMENT;
+  if (topk_w && !aligned4(topk_w)) return FLINT_ERR_ALIGNMENT;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return FLINT_ERR_ALIGNMENT;
+  if (ws_bytes < prefill_ws_bytes(*shape, n_tokens)) return FLINT_ERR_WORKSPACE;
+  PrefillWs w = carve_prefill_ws(ws, *shape, n_tokens);
+  LayerArgs a = make_args(shape, weights, x, n_tokens < 8 ? n_tokens : 8, out, gamma);
+  a.topk_idx = topk_idx ? topk_idx : w.idx;
+  a.topk_w = topk_w ? topk_w : w.wgt;
+  return to_status(launch_prefill(a, w, n_tokens, static_cast<hipStream_t>(stream)));
 }
 
 int32_t flint_dense_gemv(const void* codes, const void* scales, const float* gscale,

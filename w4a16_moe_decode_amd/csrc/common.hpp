@@ -29,6 +29,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// float64 -> BF16 bits, round to nearest even, directly from the double
+// (no intermediate float rounding).  For finite values in float's range.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double d) {
+  uint64_t b = (uint64_t)__double_as_longlong(d);
+  b += 0x0fffffffffffull + ((b >> 45) & 1ull);           // half of bit 45, ties to even
+  b &= ~0x1fffffffffffull;
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)b)) >> 16);
+}
+
+// RMSNorm's first rounding, BF16(x / rms), with rms = sqrt(mean(x^2) + eps)
+// in float64: x / rms is then rounded once, from float64, like the
+// definition; the second step (times gamma) is exact in float32.
+__device__ __forceinline__ float rms_scale_bf16(float x, double rms) {
+  return bf16_bits_to_f32(f64_to_bf16_bits((double)x / rms));
+}
+
 // SiLU(z) = z / (1 + e^-z) in fp32 (expf: the HIP device function).
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
@@ -148,6 +164,13 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum of a double over the 64 lanes of a wave (fixed order), all lanes.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 // Maximum over the wave of 64-bit keys, every lane ends with the result.
 // In-row steps use DPP; the four row maxima are combined with readlane.
 template <int CTRL>
@@ -238,6 +261,10 @@ hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bo
                           hipStream_t st);
 hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int dense_epilogue,
                        const uint16_t* dense_in, const uint16_t* aux, hipStream_t st);
+
+struct PrefillWs;
+PrefillWs carve_prefill_ws(void* base, const flint_moe_shape& s, int T);
+hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStream_t st);
 
 hipError_t launch_repack(const uint8_t* src, int64_t n_mats, int rows, int cols, int layout,
                          uint8_t* codes, uint8_t* scales, int64_t mat_stride, hipStream_t st);

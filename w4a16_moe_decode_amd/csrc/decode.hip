@@ -40,7 +40,7 @@ constexpr int kMaxB = FLINT_MAX_DECODE_BATCH;
 // error word in the workspace and still exits.
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-template <int BT, int NIT>
+template <int BT, int NIT, bool NORM>
 __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
   __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
   __shared__ float s_w[FLINT_MAX_EXPERTS][kMaxB];
@@ -49,13 +49,13 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = a.H, B = a.B, E = a.E;
-  const bool norm = (a.flags & FLINT_PRE_RMSNORM) != 0;
+  constexpr bool norm = NORM;
   const int e = blockIdx.x * 4 + wave;
   const int er = e < E ? e : E - 1;          // surplus waves recompute the last expert
   const uint32_t epoch = *ws.epoch + 1u;
 
   // all tokens' activations are fetched up front when they fit in registers
-  constexpr bool kHoist = NIT <= 4;
+  constexpr bool kHoist = NORM ? NIT * BT <= 16 : NIT <= 4;
   constexpr int XT = kHoist ? BT : 1;
   uint4 wv[NIT], gv[NIT], xv[XT][NIT];
   auto load_token = [&](uint4* dst, int t) {
@@ -83,26 +83,27 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
     uint4* xt = xv[kHoist ? t : 0];
     if constexpr (!kHoist) load_token(xt, t);
     if (norm) {
-      float ss = 0.f;
+      double ss = 0.0;
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         const uint32_t q[4] = {xt[i].x, xt[i].y, xt[i].z, xt[i].w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          ss = fmaf(bf16_lo(q[m]), bf16_lo(q[m]), ss);
-          ss = fmaf(bf16_hi(q[m]), bf16_hi(q[m]), ss);
+          const double lo = bf16_lo(q[m]), hi = bf16_hi(q[m]);
+          ss = fma(lo, lo, ss);
+          ss = fma(hi, hi, ss);
         }
       }
-      ss = group_sum<64>(ss);
-      const float r = 1.0f / sqrtf(ss / (float)H + a.eps);
+      ss = wave_sum_f64(ss);
+      const double rms = sqrt(ss / (double)H + (double)a.eps);
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         uint32_t q[4] = {xt[i].x, xt[i].y, xt[i].z, xt[i].w};
         const uint32_t g4[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float lo = round_bf16(round_bf16(bf16_lo(q[m]) * r) * bf16_lo(g4[m]));
-          const float hi = round_bf16(round_bf16(bf16_hi(q[m]) * r) * bf16_hi(g4[m]));
+          const float lo = round_bf16(rms_scale_bf16(bf16_lo(q[m]), rms) * bf16_lo(g4[m]));
+          const float hi = round_bf16(rms_scale_bf16(bf16_hi(q[m]), rms) * bf16_hi(g4[m]));
           q[m] = pack_bf16x2(lo, hi);
         }
         xt[i] = make_uint4(q[0], q[1], q[2], q[3]);
@@ -240,16 +241,16 @@ __device__ __forceinline__ DChunk<WF> decode_chunk(uint4 c, uint32_t sc) {
   }
 }
 
-// x chunk with RMSNorm applied on the fly: BF16(BF16(x * r) * gamma)
+// x chunk with RMSNorm applied on the fly: BF16(BF16(x / rms) * gamma)
 template <int WF>
 __device__ __forceinline__ XChunk<WF> load_x_norm(const uint16_t* row, const uint16_t* gamma, int j,
-                                                  float r) {
+                                                  double rms) {
   XChunk<WF> x = load_x<WF>(row, j);
   const XChunk<WF> g = load_x<WF>(gamma, j);
 #pragma unroll
   for (int m = 0; m < Fmt<WF>::VALS / 2; ++m) {
-    const float lo = round_bf16(round_bf16(bf16_lo(x.v[m]) * r) * bf16_lo(g.v[m]));
-    const float hi = round_bf16(round_bf16(bf16_hi(x.v[m]) * r) * bf16_hi(g.v[m]));
+    const float lo = round_bf16(rms_scale_bf16(bf16_lo(x.v[m]), rms) * bf16_lo(g.v[m]));
+    const float hi = round_bf16(rms_scale_bf16(bf16_hi(x.v[m]), rms) * bf16_hi(g.v[m]));
     x.v[m] = pack_bf16x2(lo, hi);
   }
   return x;
@@ -308,15 +309,15 @@ __global__ __launch_bounds__(64 * NW) void gate_up_kernel(LayerArgs a, DecodeWs 
   }
   const uint16_t* xsrc = NORM ? a.x : ((a.flags & FLINT_PRE_RMSNORM) && !dense ? ws.xn : a.x);
 
-  float rinv[BT];
+  double rinv[BT];      // RMS of each token (only with NORM)
 #pragma unroll
-  for (int t = 0; t < BT; ++t) rinv[t] = 1.f;
+  for (int t = 0; t < BT; ++t) rinv[t] = 1.0;
   if constexpr (NORM) {
     const int niter = (H + 511) / 512;
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
       if ((mask >> t) & 1u) {
-        float ss = 0.f;
+        double ss = 0.0;
         for (int i = 0; i < niter; ++i) {
           const int col = 8 * (lane + 64 * i);
           if (col < H) {
@@ -324,14 +325,14 @@ __global__ __launch_bounds__(64 * NW) void gate_up_kernel(LayerArgs a, DecodeWs 
             const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
-              ss = fmaf(lo, lo, ss);
-              ss = fmaf(hi, hi, ss);
+              const double lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
+              ss = fma(lo, lo, ss);
+              ss = fma(hi, hi, ss);
             }
           }
         }
-        ss = group_sum<64>(ss);
-        rinv[t] = 1.0f / sqrtf(ss / (float)H + a.eps);
+        ss = wave_sum_f64(ss);
+        rinv[t] = sqrt(ss / (double)H + (double)a.eps);
       }
     }
   }
@@ -638,18 +639,24 @@ hipError_t down_dispatch_g(const LayerArgs& a, const DecodeWs& ws, bool dense, i
   }
 }
 
-template <int BT>
-hipError_t route_dispatch(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
+template <int BT, bool NORM>
+hipError_t route_dispatch_n(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
   const int nit = (a.H + 511) / 512;
   dim3 grid((a.E + 3) / 4), block(256);
   switch (nit) {
-    case 1: hipLaunchKernelGGL((route_kernel<BT, 1>), grid, block, 0, st, a, ws); break;
-    case 2: hipLaunchKernelGGL((route_kernel<BT, 2>), grid, block, 0, st, a, ws); break;
-    case 3: hipLaunchKernelGGL((route_kernel<BT, 3>), grid, block, 0, st, a, ws); break;
-    case 4: hipLaunchKernelGGL((route_kernel<BT, 4>), grid, block, 0, st, a, ws); break;
-    default: hipLaunchKernelGGL((route_kernel<BT, 8>), grid, block, 0, st, a, ws); break;
+    case 1: hipLaunchKernelGGL((route_kernel<BT, 1, NORM>), grid, block, 0, st, a, ws); break;
+    case 2: hipLaunchKernelGGL((route_kernel<BT, 2, NORM>), grid, block, 0, st, a, ws); break;
+    case 3: hipLaunchKernelGGL((route_kernel<BT, 3, NORM>), grid, block, 0, st, a, ws); break;
+    case 4: hipLaunchKernelGGL((route_kernel<BT, 4, NORM>), grid, block, 0, st, a, ws); break;
+    default: hipLaunchKernelGGL((route_kernel<BT, 8, NORM>), grid, block, 0, st, a, ws); break;
   }
   return hipGetLastError();
+}
+
+template <int BT>
+hipError_t route_dispatch(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
+  return (a.flags & FLINT_PRE_RMSNORM) ? route_dispatch_n<BT, true>(a, ws, st)
+                                       : route_dispatch_n<BT, false>(a, ws, st);
 }
 
 }  // namespace

@@ -1,0 +1,663 @@
+// Prefill MoE layer (any number of tokens) for gfx950.
+//
+// "Day-0 Support for Flint on vLLM", "Optimizations": the small-batch MoE
+// change is also the largest gain for an 8,192-token prefill, running on the
+// same packed NVFP4 weights as the large-batch kernel.  Per token the result
+// is the decode layer's: out_t = BF16(sum_k w_tk E_idx(xn_t) + E_shared(xn_t)),
+// with the same rounding points (g, u, SiLU(g), SiLU(g)*u, the output).
+// Grouping tokens by expert only changes the fp32 summation order.
+//
+// Stages (one kernel each):
+//   norm      xn = BF16(BF16(x * rsqrt(mean x^2 + eps)) * gamma)   (optional)
+//   router    logits[T][E] = xn . W_r^T, BF16 MFMA with fp32 accumulation
+//   topk      per token: top-k by descending logit (ties: lower index),
+//             sigmoid weights; per 64-token chunk a token bitmask per expert
+//   scan      per-expert counts -> offsets; per (chunk, expert) bases;
+//             the tile list (group, first row) of the grouped GEMMs
+//   scatter   stable permutation of (token, slot) pairs by (expert, token)
+//   gate_up   grouped GEMM per expert (shared expert = last group, all
+//             tokens): rows gathered from xn, NVFP4 weight tiles decoded
+//             into LDS as exact BF16, MFMA, then SiLU(g) * u -> h (BF16)
+//   down      grouped GEMM h . W_d^T -> y (fp32, tensor scale applied)
+//   combine   out_t = BF16(sum_k w_tk y[pos(t,k)] + y[shared row of t])
+//             (+ residual)
+#include "common.hpp"
+#include "prefill_ws.hpp"
+
+namespace flint {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDS_STRIDE = BK + 8;        // bf16 per LDS row (16 B of padding)
+constexpr int CHUNK = 64;                 // tokens per top-k / scatter chunk
+
+// ---------------------------------------------------------- tile loaders --
+
+// A tile: BM rows x BK columns of BF16, one row pointer per tile row.  256
+// threads, 8 per row (16 B each), 4 passes of 32 rows.
+struct ARegs { uint4 v[4]; };
+struct Rows { const uint16_t* p[4]; };   // source row of each of this thread's 4 segments
+
+__device__ __forceinline__ void load_a(ARegs& r, const Rows& rows, int k0) {
+  const int seg = threadIdx.x & 7;
+  r.v[0] = *reinterpret_cast<const uint4*>(rows.p[0] + k0 + seg * 8);
+  r.v[1] = *reinterpret_cast<const uint4*>(rows.p[1] + k0 + seg * 8);
+  r.v[2] = *reinterpret_cast<const uint4*>(rows.p[2] + k0 + seg * 8);
+  r.v[3] = *reinterpret_cast<const uint4*>(rows.p[3] + k0 + seg * 8);
+}
+__device__ __forceinline__ void store_a(const ARegs& r, uint16_t* lds) {
+  const int t = threadIdx.x, seg = t & 7;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = p * 32 + (t >> 3);
+    *reinterpret_cast<uint4*>(lds + row * LDS_STRIDE + seg * 8) = r.v[p];
+  }
+}
+
+// B tile from NVFP4: BN weight rows x BK columns; two threads per row, each
+// 32 codes (16 B) and their two scale bytes, decoded to exact BF16
+// (E2M1 x UE4M3 has at most 6 significant bits).
+struct BRegsNv { uint4 c; uint32_t s; };
+
+__device__ __forceinline__ void load_b_nv(BRegsNv& r, const uint8_t* codes_row, const uint8_t* scales_row,
+                                          int k0) {
+  const int half = threadIdx.x & 1;
+  r.c = *reinterpret_cast<const uint4*>(codes_row + k0 / 2 + half * 16);
+  r.s = *reinterpret_cast<const uint16_t*>(scales_row + k0 / 16 + half * 2);
+}
+__device__ __forceinline__ void store_b_nv(const BRegsNv& r, uint16_t* lds) {
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const DChunk<FMT_NVFP4> d = decode_nvfp4(r.c, r.s);
+  uint32_t o[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float s = m < 8 ? d.s0 : d.s1;
+    // the product is exact in BF16, so taking the top 16 bits loses nothing
+    const uint32_t lo = __float_as_uint((float)d.w[m].x * s) >> 16;
+    const uint32_t hi = __float_as_uint((float)d.w[m].y * s) & 0xffff0000u;
+    o[m] = lo | hi;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(lds + row * LDS_STRIDE + half * 32);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
+  dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+}
+
+// B tile from BF16 weights (router; W16A16): same pattern as the A tile.
+__device__ __forceinline__ void load_b_bf(ARegs& r, const Rows& rows, int k0) { load_a(r, rows, k0); }
+
+// ------------------------------------------------------------- MFMA core --
+// 4 waves in 2 x 2; wave (wm, wn) owns rows 64wm..64wm+63 and columns
+// 64wn..64wn+63 of the tile as 2 x 2 MFMA 32x32x16 blocks.  Operand layout
+// (measured on gfx950): A lane l holds A[l%32][8(l/32) .. +7], B lane l holds
+// B[8(l/32) .. +7][l%32]; result element i of lane l is C[8(i/4) + 4(l/32) +
+// i%4][l%32].
+struct Acc { f32x16 c[2][2]; };
+
+__device__ __forceinline__ void mfma_tile(Acc& acc, const uint16_t* la, const uint16_t* lb) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8_t a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 64 * wm + 32 * i + (lane & 31);
+      a[i] = *reinterpret_cast<const bf16x8_t*>(la + row * LDS_STRIDE + kk * 16 + 8 * (lane >> 5));
+      const int col = 64 * wn + 32 * i + (lane & 31);
+      b[i] = *reinterpret_cast<const bf16x8_t*>(lb + col * LDS_STRIDE + kk * 16 + 8 * (lane >> 5));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void acc_zero(Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc.c[i][j][e] = 0.f;
+}
+
+// tile-local (row, col) of result element e of block (i, j) for this lane
+__device__ __forceinline__ int acc_row(int i, int e) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  return 64 * (wave >> 1) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+}
+__device__ __forceinline__ int acc_col(int j) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  return 64 * (wave & 1) + 32 * j + (lane & 31);
+}
+
+// ---------------------------------------------------------- workspaces ----
+}  // namespace
+
+
+
+int prefill_max_tiles(const flint_moe_shape& s, int T) {
+  const int pairs = T * s.top_k;
+  return (pairs + BM - 1) / BM + s.n_experts + (s.shared_inter > 0 ? (T + BM - 1) / BM + 1 : 0);
+}
+
+PrefillWs carve_prefill_ws(void* base, const flint_moe_shape& s, int T) {
+  auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
+  const int E = s.n_experts, K = s.top_k, H = s.hidden;
+  const int C = (T + CHUNK - 1) / CHUNK;
+  const int imax = s.inter > s.shared_inter ? s.inter : s.shared_inter;
+  const int64_t rows = (int64_t)T * K + (s.shared_inter > 0 ? T : 0);
+  char* b = static_cast<char*>(base);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off = up(off + bytes);
+    return p;
+  };
+  PrefillWs w;
+  w.max_tiles = prefill_max_tiles(s, T);
+  w.xn = reinterpret_cast<uint16_t*>(take((int64_t)T * H * 2));
+  w.logits = reinterpret_cast<float*>(take((int64_t)T * E * 4));
+  w.idx = reinterpret_cast<int32_t*>(take((int64_t)T * K * 4));
+  w.wgt = reinterpret_cast<float*>(take((int64_t)T * K * 4));
+  w.cmask = reinterpret_cast<uint64_t*>(take((int64_t)C * E * 8));
+  w.cbase = reinterpret_cast<int32_t*>(take((int64_t)C * E * 4));
+  w.counts = reinterpret_cast<int32_t*>(take((int64_t)(E + 1) * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((int64_t)(E + 2) * 4));
+  w.ntiles = reinterpret_cast<int32_t*>(take(4));
+  w.tiles = reinterpret_cast<int2*>(take((int64_t)w.max_tiles * 8));
+  w.perm_tok = reinterpret_cast<int32_t*>(take((int64_t)T * K * 4));
+  w.perm_w = reinterpret_cast<float*>(take((int64_t)T * K * 4));
+  w.pos = reinterpret_cast<int32_t*>(take((int64_t)T * K * 4));
+  w.h = reinterpret_cast<uint16_t*>(take(rows * imax * 2));
+  w.y = reinterpret_cast<float*>(take(rows * H * 4));
+  w.bytes = off;
+  return w;
+}
+
+namespace {
+
+// ------------------------------------------------------------------ norm --
+// One wave per token; the mean of squares, its square root and x / rms are
+// taken in float64, x / rms is rounded to BF16 once from float64.
+__global__ __launch_bounds__(256) void prefill_norm_kernel(LayerArgs a, PrefillWs ws, int T) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int H = a.H;
+  const uint16_t* xr = a.x + (size_t)t * H;
+  double ss = 0.0;
+  for (int c = 8 * lane; c < H; c += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const double lo = bf16_lo(q[m]), hi = bf16_hi(q[m]);
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+  }
+  ss = wave_sum_f64(ss);
+  const double rms = sqrt(ss / (double)H + (double)a.eps);
+  for (int c = 8 * lane; c < H; c += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+    const uint4 g = *reinterpret_cast<const uint4*>(a.gamma + c);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[m] = pack_bf16x2(round_bf16(rms_scale_bf16(bf16_lo(q[m]), rms) * bf16_lo(gq[m])),
+                         round_bf16(rms_scale_bf16(bf16_hi(q[m]), rms) * bf16_hi(gq[m])));
+    *reinterpret_cast<uint4*>(ws.xn + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ---------------------------------------------------------------- router --
+// logits[T][E] = xn . W_r^T.  Grid (token tiles, expert tiles).
+__global__ __launch_bounds__(256) void prefill_router_kernel(LayerArgs a, PrefillWs ws, int T,
+                                                             const uint16_t* xin) {
+  __shared__ uint16_t la[2][BM * LDS_STRIDE];
+  __shared__ uint16_t lb[2][BN * LDS_STRIDE];
+  const int H = a.H, E = a.E;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int t = threadIdx.x;
+  Rows arow, brow;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = p * 32 + (t >> 3);
+    const int tok = m0 + r < T ? m0 + r : T - 1;
+    arow.p[p] = xin + (size_t)tok * H;
+    const int e = n0 + r < E ? n0 + r : E - 1;
+    brow.p[p] = a.router + (size_t)e * H;
+  }
+  Acc acc;
+  acc_zero(acc);
+  ARegs ra, rb;
+  load_a(ra, arow, 0);
+  load_b_bf(rb, brow, 0);
+  store_a(ra, la[0]);
+  store_a(rb, lb[0]);
+  __syncthreads();
+  const int nk = H / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // the next stage's tile (the last iteration re-reads its own stage and
+    // stores it into the idle buffer, which nothing reads afterwards)
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
+    load_a(ra, arow, kn);
+    load_b_bf(rb, brow, kn);
+    mfma_tile(acc, la[cur], lb[cur]);
+    store_a(ra, la[cur ^ 1]);
+    store_a(rb, lb[cur ^ 1]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = m0 + acc_row(i, e), c = n0 + acc_col(j);
+        if (r < T && c < E) ws.logits[(size_t)r * E + c] = acc.c[i][j][e];
+      }
+}
+
+// ------------------------------------------------------------------ topk --
+// One workgroup per chunk of 64 tokens, one wave per token at a time.
+__global__ __launch_bounds__(256) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
+  __shared__ unsigned long long s_mask[FLINT_MAX_EXPERTS];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E, K = a.K;
+  const int c = blockIdx.x;
+  s_mask[threadIdx.x] = 0ull;
+  __syncthreads();
+  const bool renorm = (a.flags & FLINT_RENORM) != 0;
+  for (int j = wave; j < CHUNK; j += 4) {
+    const int t = c * CHUNK + j;
+    if (t >= T) break;
+    uint64_t key[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ex = lane + 64 * q;
+      key[q] = ex < E ? (((uint64_t)float_order_key(ws.logits[(size_t)t * E + ex]) << 32) |
+                         (uint32_t)~(uint32_t)ex)
+                      : 0ull;
+    }
+    float my_s = 0.f, ssum = 0.f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      uint64_t m = key[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) m = key[q] > m ? key[q] : m;
+      m = wave_max_u64(m);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (key[q] == m) key[q] = 0ull;
+      const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
+      ssum += sg;
+      if (lane == k) { my_s = sg; my_e = (int)~(uint32_t)m; }
+    }
+    if (lane < K) {
+      a.topk_idx[(size_t)t * K + lane] = my_e;
+      a.topk_w[(size_t)t * K + lane] = renorm ? my_s / ssum : my_s;
+      atomicOr(&s_mask[my_e], 1ull << j);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < E) ws.cmask[(size_t)c * E + threadIdx.x] = s_mask[threadIdx.x];
+}
+
+// ------------------------------------------------------------------ scan --
+// One workgroup: per-expert counts and offsets, per-chunk bases, tile list.
+__global__ __launch_bounds__(256) void prefill_scan_kernel(LayerArgs a, PrefillWs ws, int T) {
+  __shared__ int s_part[4];
+  const int E = a.E, C = (T + CHUNK - 1) / CHUNK;
+  const int e = threadIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool has_sh = a.SI > 0;
+  int cnt = 0;
+  if (e < E)
+    for (int c = 0; c < C; ++c) {
+      ws.cbase[(size_t)c * E + e] = cnt;
+      cnt += __popcll(ws.cmask[(size_t)c * E + e]);
+    }
+  // exclusive scan of counts over experts (256 threads = 4 waves)
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_part[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_part[w];
+  const int offset = before + incl - cnt;
+  if (e < E) {
+    ws.counts[e] = cnt;
+    ws.offsets[e] = offset;
+    for (int c = 0; c < C; ++c) ws.cbase[(size_t)c * E + e] += offset;
+  }
+  const int total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  if (threadIdx.x == 0) {
+    ws.offsets[E] = total;
+    ws.counts[E] = has_sh ? T : 0;
+  }
+  // tile list: routed groups in expert order, then the shared group
+  const int nt = e < E ? (cnt + BM - 1) / BM : 0;
+  int tincl = nt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(tincl, off, 64);
+    if (lane >= off) tincl += v;
+  }
+  __syncthreads();
+  if (lane == 63) s_part[wave] = tincl;
+  __syncthreads();
+  int tbefore = 0;
+  for (int w = 0; w < wave; ++w) tbefore += s_part[w];
+  const int tfirst = tbefore + tincl - nt;
+  for (int i = 0; i < nt; ++i) ws.tiles[tfirst + i] = make_int2(e, i * BM);
+  const int routed_tiles = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  const int sh_tiles = has_sh ? (T + BM - 1) / BM : 0;
+  for (int i = threadIdx.x; i < sh_tiles; i += 256) ws.tiles[routed_tiles + i] = make_int2(E, i * BM);
+  if (threadIdx.x == 0) *ws.ntiles = routed_tiles + sh_tiles;
+}
+
+// --------------------------------------------------------------- scatter --
+// Permuted position of pair (t, k) with expert e: the expert's offset, plus
+// the pairs of e in earlier chunks, plus the earlier tokens of this chunk
+// routed to e.  Stable by (expert, token).
+__global__ __launch_bounds__(256) void prefill_scatter_kernel(LayerArgs a, PrefillWs ws, int T) {
+  const int E = a.E, K = a.K;
+  const int c = blockIdx.x;
+  for (int q = threadIdx.x; q < CHUNK * K; q += 256) {
+    const int j = q / K, k = q - j * K;
+    const int t = c * CHUNK + j;
+    if (t >= T) continue;
+    const int e = a.topk_idx[(size_t)t * K + k];
+    const uint64_t before = ws.cmask[(size_t)c * E + e] & ((1ull << j) - 1ull);
+    const int p = ws.cbase[(size_t)c * E + e] + __popcll(before);
+    ws.perm_tok[p] = t;
+    ws.perm_w[p] = a.topk_w[(size_t)t * K + k];
+    ws.pos[(size_t)t * K + k] = p;
+  }
+}
+
+// --------------------------------------------------------------- gate/up --
+// Grouped GEMM, grid (tiles, column tiles).  A tile rows are the tile's
+// tokens (gathered xn rows); the B tile interleaves gate and up rows
+// (tile row 2i = gate row i0+i, 2i+1 = up row i0+i), so the result columns
+// alternate g and u and each lane's partner lane (lane ^ 1) holds the other
+// half of its pair.
+template <int WF>
+__global__ __launch_bounds__(256) void prefill_gate_up_kernel(LayerArgs a, PrefillWs ws, int T,
+                                                              const uint16_t* xin) {
+  __shared__ uint16_t la[2][BM * LDS_STRIDE];
+  __shared__ uint16_t lb[2][BN * LDS_STRIDE];
+  if ((int)blockIdx.x >= *ws.ntiles) return;
+  const int2 tile = ws.tiles[blockIdx.x];
+  const int g = tile.x, m0 = tile.y;
+  const int E = a.E, K = a.K, H = a.H;
+  const bool shared = g == E;
+  const int inter = shared ? a.SI : a.I;
+  const int i0 = blockIdx.y * (BN / 2);
+  if (i0 >= inter) return;
+  const int cnt = shared ? T : ws.counts[g];
+  const int base = shared ? 0 : ws.offsets[g];
+  const int imax = a.I > a.SI ? a.I : a.SI;
+  const int t = threadIdx.x;
+
+  Rows arow;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = m0 + p * 32 + (t >> 3);
+    const int rr = r < cnt ? r : cnt - 1;
+    const int tok = shared ? rr : ws.perm_tok[base + rr];
+    arow.p[p] = xin + (size_t)tok * H;
+  }
+  // this thread's B row: tile row t/2 (NVFP4: two threads per row)
+  const int brow_t = t >> 1;
+  const int bi = i0 + (brow_t >> 1), bup = brow_t & 1;
+  const int bic = bi < inter ? bi : inter - 1;
+  const uint8_t* bcodes = nullptr;
+  const uint8_t* bscales = nullptr;
+  Rows bbf;
+  float gs_g = 1.f, gs_u = 1.f;
+  if constexpr (WF == FMT_NVFP4) {
+    const size_t mc = (size_t)inter * H / 2, ms = (size_t)inter * H / 16;
+    const uint8_t* c0 = shared ? a.sh_gu_codes : a.gu_codes + (size_t)(2 * g) * mc;
+    const uint8_t* s0 = shared ? a.sh_gu_scales : a.gu_scales + (size_t)(2 * g) * ms;
+    bcodes = c0 + bup * mc + (size_t)bic * (H / 2);
+    bscales = s0 + bup * ms + (size_t)bic * (H / 16);
+    const float* gsp = shared ? a.sh_gscale : a.gscale + 3 * g;
+    gs_g = gsp[0];
+    gs_u = gsp[1];
+  } else {
+    const size_t mb = (size_t)inter * H;
+    const uint16_t* w0 = shared ? a.sh_gu_bf16 : a.gu_bf16 + (size_t)(2 * g) * mb;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = p * 32 + (t >> 3);           // tile row of this thread's 16-B segment
+      const int ii = i0 + (r >> 1);
+      const int iic = ii < inter ? ii : inter - 1;
+      bbf.p[p] = w0 + (r & 1) * mb + (size_t)iic * H;
+    }
+  }
+
+  Acc acc;
+  acc_zero(acc);
+  ARegs ra, rbb;
+  BRegsNv rbn;
+  load_a(ra, arow, 0);
+  if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, 0);
+  else load_b_bf(rbb, bbf, 0);
+  store_a(ra, la[0]);
+  if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[0]);
+  else store_a(rbb, lb[0]);
+  __syncthreads();
+  const int nk = H / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
+    load_a(ra, arow, kn);
+    if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, kn);
+    else load_b_bf(rbb, bbf, kn);
+    mfma_tile(acc, la[cur], lb[cur]);
+    store_a(ra, la[cur ^ 1]);
+    if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[cur ^ 1]);
+    else store_a(rbb, lb[cur ^ 1]);
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const bool even = (lane & 1) == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float mine = acc.c[i][j][e];
+        const float other = dpp_f<0xB1>(mine);       // partner lane ^ 1
+        const int r = m0 + acc_row(i, e);
+        const int col = acc_col(j);
+        const int ii = i0 + (col >> 1);
+        if (even && r < cnt && ii < inter) {
+          const float gv = round_bf16(mine * gs_g);
+          const float uv = round_bf16(other * gs_u);
+          const float av = round_bf16(silu_f32(gv));
+          const size_t row = shared ? (size_t)T * K + r : (size_t)base + r;
+          ws.h[row * imax + ii] = f32_to_bf16_bits(av * uv);
+        }
+      }
+}
+
+// ------------------------------------------------------------------ down --
+// Grouped GEMM h . W_d^T -> y (fp32), grid (tiles, column tiles of H).
+template <int WF>
+__global__ __launch_bounds__(256) void prefill_down_kernel(LayerArgs a, PrefillWs ws, int T) {
+  __shared__ uint16_t la[2][BM * LDS_STRIDE];
+  __shared__ uint16_t lb[2][BN * LDS_STRIDE];
+  if ((int)blockIdx.x >= *ws.ntiles) return;
+  const int2 tile = ws.tiles[blockIdx.x];
+  const int g = tile.x, m0 = tile.y;
+  const int E = a.E, K = a.K, H = a.H;
+  const bool shared = g == E;
+  const int inter = shared ? a.SI : a.I;
+  const int n0 = blockIdx.y * BN;
+  const int cnt = shared ? T : ws.counts[g];
+  const size_t base = shared ? (size_t)T * K : (size_t)ws.offsets[g];
+  const int imax = a.I > a.SI ? a.I : a.SI;
+  const int t = threadIdx.x;
+
+  Rows arow;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = m0 + p * 32 + (t >> 3);
+    const int rr = r < cnt ? r : cnt - 1;
+    arow.p[p] = ws.h + (base + rr) * imax;
+  }
+  const int bn = n0 + (t >> 1);
+  const int bnc = bn < H ? bn : H - 1;
+  const uint8_t* bcodes = nullptr;
+  const uint8_t* bscales = nullptr;
+  Rows bbf;
+  float gd = 1.f;
+  if constexpr (WF == FMT_NVFP4) {
+    const uint8_t* c0 = shared ? a.sh_d_codes : a.d_codes + (size_t)g * H * (inter / 2);
+    const uint8_t* s0 = shared ? a.sh_d_scales : a.d_scales + (size_t)g * H * (inter / 16);
+    bcodes = c0 + (size_t)bnc * (inter / 2);
+    bscales = s0 + (size_t)bnc * (inter / 16);
+    gd = shared ? a.sh_gscale[2] : a.gscale[3 * g + 2];
+  } else {
+    const uint16_t* w0 = shared ? a.sh_d_bf16 : a.d_bf16 + (size_t)g * H * inter;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = n0 + p * 32 + (t >> 3);
+      bbf.p[p] = w0 + (size_t)(r < H ? r : H - 1) * inter;
+    }
+  }
+  Acc acc;
+  acc_zero(acc);
+  ARegs ra, rbb;
+  BRegsNv rbn;
+  load_a(ra, arow, 0);
+  if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, 0);
+  else load_b_bf(rbb, bbf, 0);
+  store_a(ra, la[0]);
+  if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[0]);
+  else store_a(rbb, lb[0]);
+  __syncthreads();
+  const int nk = inter / BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
+    load_a(ra, arow, kn);
+    if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, kn);
+    else load_b_bf(rbb, bbf, kn);
+    mfma_tile(acc, la[cur], lb[cur]);
+    store_a(ra, la[cur ^ 1]);
+    if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[cur ^ 1]);
+    else store_a(rbb, lb[cur ^ 1]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = m0 + acc_row(i, e), c = n0 + acc_col(j);
+        if (r < cnt && c < H) ws.y[(base + r) * H + c] = acc.c[i][j][e] * gd;
+      }
+}
+
+// --------------------------------------------------------------- combine --
+// One workgroup per token; 8 columns per thread per pass.
+__global__ __launch_bounds__(256) void prefill_combine_kernel(LayerArgs a, PrefillWs ws, int T) {
+  const int t = blockIdx.x;
+  const int H = a.H, K = a.K;
+  const bool has_sh = a.SI > 0;
+  const bool resid = (a.flags & FLINT_RESIDUAL) != 0;
+  int p[FLINT_MAX_TOP_K];
+  float w[FLINT_MAX_TOP_K];
+#pragma unroll
+  for (int k = 0; k < FLINT_MAX_TOP_K; ++k) {
+    p[k] = k < K ? ws.pos[(size_t)t * K + k] : 0;
+    w[k] = k < K ? a.topk_w[(size_t)t * K + k] : 0.f;
+  }
+  for (int c = 8 * threadIdx.x; c < H; c += 8 * 256) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int k = 0; k < FLINT_MAX_TOP_K; ++k) {
+      if (k < K) {
+        const float4* yr = reinterpret_cast<const float4*>(ws.y + (size_t)p[k] * H + c);
+        const float4 v0 = yr[0], v1 = yr[1];
+        acc[0] = fmaf(w[k], v0.x, acc[0]); acc[1] = fmaf(w[k], v0.y, acc[1]);
+        acc[2] = fmaf(w[k], v0.z, acc[2]); acc[3] = fmaf(w[k], v0.w, acc[3]);
+        acc[4] = fmaf(w[k], v1.x, acc[4]); acc[5] = fmaf(w[k], v1.y, acc[5]);
+        acc[6] = fmaf(w[k], v1.z, acc[6]); acc[7] = fmaf(w[k], v1.w, acc[7]);
+      }
+    }
+    if (has_sh) {
+      const float4* yr = reinterpret_cast<const float4*>(ws.y + ((size_t)T * K + t) * H + c);
+      const float4 v0 = yr[0], v1 = yr[1];
+      acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+      acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    }
+    uint32_t xr[4] = {0, 0, 0, 0};
+    if (resid) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (size_t)t * H + c);
+      xr[0] = xv.x; xr[1] = xv.y; xr[2] = xv.z; xr[3] = xv.w;
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float lo = round_bf16(acc[2 * q]), hi = round_bf16(acc[2 * q + 1]);
+      if (resid) {
+        lo = bf16_lo(xr[q]) + lo;
+        hi = bf16_hi(xr[q]) + hi;
+      }
+      o[q] = pack_bf16x2(lo, hi);
+    }
+    *reinterpret_cast<uint4*>(a.out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStream_t st) {
+  const bool norm = (a.flags & FLINT_PRE_RMSNORM) != 0;
+  const bool bf = (a.flags & FLINT_W_BF16) != 0;
+  const uint16_t* xin = norm ? ws.xn : a.x;
+  const int C = (T + CHUNK - 1) / CHUNK;
+  const int imax = a.I > a.SI ? a.I : a.SI;
+  if (norm) hipLaunchKernelGGL(prefill_norm_kernel, dim3((T + 3) / 4), dim3(256), 0, st, a, ws, T);
+  hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
+                     st, a, ws, T, xin);
+  hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(256), 0, st, a, ws, T);
+  hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
+  const dim3 ggu(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2));
+  const dim3 gdn(ws.max_tiles, (a.H + BN - 1) / BN);
+  if (bf) {
+    hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_BF16>, ggu, dim3(256), 0, st, a, ws, T, xin);
+    hipLaunchKernelGGL(prefill_down_kernel<FMT_BF16>, gdn, dim3(256), 0, st, a, ws, T);
+  } else {
+    hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_NVFP4>, ggu, dim3(256), 0, st, a, ws, T, xin);
+    hipLaunchKernelGGL(prefill_down_kernel<FMT_NVFP4>, gdn, dim3(256), 0, st, a, ws, T);
+  }
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3(T), dim3(256), 0, st, a, ws, T);
+  return hipGetLastError();
+}
+
+}  // namespace flint
