@@ -69,6 +69,9 @@ extern "C" {
 #define FLINT_PRE_RMSNORM  0x4u  /* input is the residual x: the layer first
                                     computes xn = RMSNorm(x) * gamma */
 #define FLINT_RESIDUAL     0x8u  /* out = BF16(x + BF16(layer(xn))) */
+#define FLINT_SPLIT        0x10u /* decode: always run the three-kernel path
+                                    (by default a batch-1 NVFP4 call with
+                                    hidden 2048 or 4096 runs as one launch) */
 
 /* source NVFP4 super-block byte orders accepted by the repack */
 #define FLINT_SRC_INTERLEAVED   0  /* 4 x [scale byte, 8 code bytes]          */
@@ -90,7 +93,8 @@ extern "C" {
  *   inter         I, routed expert intermediate, multiple of 64
  *   shared_inter  SI, shared expert intermediate, multiple of 64; 0 = none
  *   top_k         K, 1..min(8, E)
- *   flags         FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL
+ *   flags         FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL |
+ *                 FLINT_SPLIT
  *   rms_eps       RMSNorm epsilon (used with FLINT_PRE_RMSNORM)
  * Sizes: [D0] "Model architecture" (hidden 2048; 256 experts, sigmoid top-6,
  * one shared expert); the expert intermediate is not printed on the pages. */
@@ -214,8 +218,13 @@ FLINT_API int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int
  *   topk_w    (device) float [batch][K] or NULL; the combine weights
  *   gamma     (device) BF16 [H], required with FLINT_PRE_RMSNORM
  *   ws        (device) workspace of at least flint_moe_workspace_bytes(shape, batch)
- * Enqueues three kernels: route (RMSNorm, router GEMV, top-k, expert set),
- * gate/up (+SiLU*up), down (weighted combine, shared expert, residual). */
+ * Batch 1 with NVFP4 weights and hidden 2048 or 4096 (I, SI <= 2048) runs
+ * as one launch of a persistent grid (one workgroup per compute unit) whose
+ * phases hand data over through epoch-tagged words in the workspace; every
+ * other call, and any call with FLINT_SPLIT, enqueues three kernels: route
+ * (RMSNorm, router GEMV, top-k, expert set), gate/up (+SiLU*up), down
+ * (weighted combine, shared expert, residual).  Both give the same result
+ * up to fp32 summation order. */
 FLINT_API int32_t flint_moe_decode(const flint_moe_shape* shape, const flint_moe_weights* weights,
                          const void* x, int32_t batch, void* out, int32_t* topk_idx,
                          float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,

@@ -33,6 +33,7 @@ FLINT_RENORM = 0x1
 FLINT_W_BF16 = 0x2
 FLINT_PRE_RMSNORM = 0x4
 FLINT_RESIDUAL = 0x8
+FLINT_SPLIT = 0x10
 
 FLINT_SRC_INTERLEAVED = 0
 FLINT_SRC_SCALES_FIRST = 1
@@ -324,6 +325,13 @@ def pack_moe_layer(router: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, d
         layer.sh_d_codes, layer.sh_d_scales = sdc, sds
         layer.sh_gscale = sg
     return layer
+
+
+def decode_error_word(runner) -> int:
+    """The decode workspace's hand-off error word (1 if a bounded wait ever
+    timed out; it stays 0 in normal operation).  It is the third 256-byte
+    field of the workspace (after the ticket and the epoch)."""
+    return int(runner.ws[512:516].view(torch.int32).item())
 
 
 class DecodeRunner:

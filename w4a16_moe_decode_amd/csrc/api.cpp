@@ -28,7 +28,7 @@ int check_shape(const flint_moe_shape* s) {
   if (s->hidden > 4096) return FLINT_ERR_UNSUPPORTED;
   if (s->n_experts > FLINT_MAX_EXPERTS) return FLINT_ERR_UNSUPPORTED;
   if (s->top_k > FLINT_MAX_TOP_K || s->top_k > s->n_experts) return FLINT_ERR_UNSUPPORTED;
-  if (s->flags & ~(FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL))
+  if (s->flags & ~(FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | FLINT_SPLIT))
     return FLINT_ERR_UNSUPPORTED;
   if ((s->flags & FLINT_PRE_RMSNORM) && !(s->rms_eps >= 0.0f)) return FLINT_ERR_INVALID_ARG;
   return FLINT_OK;
@@ -126,7 +126,9 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
   w.ticket = reinterpret_cast<uint32_t*>(take(4));
   w.epoch = reinterpret_cast<uint32_t*>(take(4));
   w.error = reinterpret_cast<uint32_t*>(take(4));
-  w.logit_words = reinterpret_cast<uint64_t*>(take((int64_t)B * s.n_experts * 8));
+  // 64 copies of every hand-off word for the single-launch path (its readers
+  // each take their own copy); the three-kernel path uses the first [B][E]
+  w.logit_words = reinterpret_cast<uint64_t*>(take((int64_t)64 * B * s.n_experts * 8));
   w.xn = reinterpret_cast<uint16_t*>(take((int64_t)B * s.hidden * 2));
   w.idx = reinterpret_cast<int32_t*>(take((int64_t)B * FLINT_MAX_TOP_K * 4));
   w.wgt = reinterpret_cast<float*>(take((int64_t)B * FLINT_MAX_TOP_K * 4));
@@ -134,6 +136,7 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
   w.slot_expert = reinterpret_cast<int32_t*>(take((int64_t)S * 4));
   w.slot_mask = reinterpret_cast<uint32_t*>(take((int64_t)S * 4));
   w.slot_w = reinterpret_cast<float*>(take((int64_t)S * B * 4));
+  w.h_words = reinterpret_cast<uint64_t*>(take((int64_t)64 * (FLINT_MAX_TOP_K + 1) * (imax / 2) * 8));
   w.h = reinterpret_cast<uint16_t*>(take((int64_t)S * B * imax * 2));
   w.bytes = off;
   return w;
@@ -252,6 +255,8 @@ static int32_t decode_common(int32_t stage, const flint_moe_shape* shape,
   a.topk_w = topk_w ? topk_w : w.wgt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (stage < 0 && !(shape->flags & FLINT_SPLIT) && fused_decode_supported(a))
+    return to_status(launch_fused_decode(a, w, s));
   if (stage < 0 || stage == 0) e = launch_route(a, w, s);
   if (e == hipSuccess && (stage < 0 || stage == 1)) e = launch_gate_up(a, w, false, false, s);
   if (e == hipSuccess && (stage < 0 || stage == 2)) e = launch_down(a, w, false, 0, nullptr, nullptr, s);

@@ -197,6 +197,39 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return m;
 }
 
+// Maximum over the wave of a 32-bit value (DPP max steps within rows, then
+// the four row maxima), the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Wave maximum of 64-bit keys (order key << 32 | inverted index) whose high
+// halves are usually distinct: the high half is reduced with 32-bit steps,
+// and the low half only among the lanes that hold the maximal high half.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  const uint32_t mhi = wave_max_u32(hi);
+  const bool at = hi == mhi;
+  const unsigned long long bal = __ballot(at);
+  uint32_t mlo;
+  if (__popcll(bal) == 1) {
+    mlo = __builtin_amdgcn_readlane((uint32_t)key, __ffsll((long long)bal) - 1);
+  } else {
+    mlo = wave_max_u32(at ? (uint32_t)key : 0u);
+  }
+  return ((uint64_t)mhi << 32) | mlo;
+}
+
 // Order-preserving map of a float to uint32 (larger float -> larger key);
 // NaN is treated as -inf.
 __device__ __forceinline__ uint32_t float_order_key(float f) {
@@ -223,6 +256,7 @@ struct DecodeWs {
   int32_t* slot_expert;  // [S] routed expert of routed slot r (ascending)
   uint32_t* slot_mask;   // [S] bit t set = token t routed to routed slot r
   float* slot_w;         // [S][8] combine weight of token t at routed slot r
+  uint64_t* h_words;     // [K+1][Imax/2] (epoch << 32) | two BF16 of h, single-launch path
   uint16_t* h;           // [S][8][Imax] BF16 SiLU(g)*u per slot and token; slot 0
                          // is the shared expert when there is one, routed
                          // slot r is slot r + (shared ? 1 : 0)
@@ -257,6 +291,8 @@ struct LayerArgs {
 };
 
 hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
+bool fused_decode_supported(const LayerArgs& a);
+hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm_on_the_fly,
                           hipStream_t st);
 hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int dense_epilogue,

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
       uint64_t m = key[0];
 #pragma unroll
       for (int j = 1; j < 4; ++j) m = key[j] > m ? key[j] : m;
-      m = wave_max_u64(m);
+      m = wave_max_key(m);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (key[j] == m) key[j] = 0ull;

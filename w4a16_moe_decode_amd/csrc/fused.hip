@@ -1,0 +1,536 @@
+// Single-launch decode MoE layer for one token (batch 1), NVFP4 weights.
+//
+// The same layer as the three-kernel path (decode.hip) -- RMSNorm (opt.),
+// router GEMV, sigmoid top-k, gate/up GEMV + SiLU*up, down GEMV + weighted
+// combine + shared expert (+ residual) -- run by one persistent grid of
+// workgroups so that the dependent steps overlap instead of paying a launch
+// and a cold start each.  This is the low-latency decode path of "Day-0
+// Support for Flint on vLLM" ("Optimizations", last bullet and the paragraph
+// after the list: routing and the expert combine fused into neighbouring
+// GEMV kernels, the next kernel's weight loads overlapping the previous
+// one), built on one GPU without inter-kernel launches:
+//
+//   phase 1  router logits (one expert per workgroup, a quarter row per
+//            wave) and the shared expert's gate/up rows, loaded together
+//   phase 2  every workgroup waits for all logits, selects the top-k itself
+//            and issues the loads of its own down rows of all selected
+//            experts (they do not depend on h)
+//   phase 3  routed gate/up rows (work dealt round-robin over all waves)
+//   phase 4  every workgroup waits for the h values it needs, then computes
+//            its output rows: weighted combine of the selected experts and
+//            the shared expert, one BF16 rounding (+ residual)
+//
+// Hand-offs between workgroups use 64-bit words (launch epoch << 32 |
+// payload) written and read with agent-scope atomics: data and ready flag
+// are one word, so no release fence (a whole-L2 write-back on this GPU) is
+// needed.  Every wait is bounded: if a word does not arrive (it cannot while
+// all workgroups are resident) the kernel records an error and still exits.
+// The grid never exceeds the number of compute units, one workgroup each.
+#include "common.hpp"
+
+namespace flint {
+namespace {
+
+constexpr uint32_t kFusedSpin = 1u << 20;
+
+__device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch, uint32_t* err) {
+  uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t spin = 0; (uint32_t)(w >> 32) != epoch && spin < kFusedSpin; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
+    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if ((uint32_t)(w >> 32) != epoch) *err = 1u;
+  return w;
+}
+
+// Batched wait: all U words are loaded at once, then only the ones that do
+// not carry the epoch yet are loaded again.  Entries with ok[u] false are
+// skipped.
+template <int U>
+__device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* const (&p)[U],
+                                           const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    w[u] = ok[u] ? __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : ((uint64_t)epoch << 32);
+  for (uint32_t spin = 0; spin < kFusedSpin; ++spin) {
+    bool ready = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) ready = ready && (uint32_t)(w[u] >> 32) == epoch;
+    if (ready) return;
+    __builtin_amdgcn_s_sleep(8);     // back off: every workgroup is polling
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if ((uint32_t)(w[u] >> 32) != epoch)
+        w[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  *err = 1u;
+}
+
+__device__ __forceinline__ void put_word(uint64_t* p, uint32_t epoch, uint32_t payload) {
+  __hip_atomic_store(p, ((uint64_t)epoch << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Hand-off words are published in kReplicas copies (lanes 0..kReplicas-1 of
+// the writing wave each store one); workgroup g reads copy g % kReplicas.
+// Every workgroup needs every word: one copy per XCD keeps the readers of a
+// line to the workgroups of one XCD without multiplying the stores much.
+constexpr int kReplicas = 8;
+
+__device__ __forceinline__ void put_word_all(uint64_t* base, size_t stride, size_t idx, uint32_t epoch,
+                                             uint32_t payload) {
+  const int lane = threadIdx.x & 63;
+  if (lane < kReplicas) put_word(base + (size_t)lane * stride + idx, epoch, payload);
+}
+
+struct GURows {            // gate and up rows of one selected expert
+  const uint8_t* gc; const uint8_t* gs;
+  const uint8_t* uc; const uint8_t* us;
+  float g_scale, u_scale;
+  int inter;
+};
+
+__device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert /* -1 = shared */) {
+  GURows r;
+  const int H = a.H;
+  if (expert < 0) {
+    r.inter = a.SI;
+    const size_t mc = (size_t)a.SI * H / 2, ms = (size_t)a.SI * H / 16;
+    r.gc = a.sh_gu_codes; r.uc = a.sh_gu_codes + mc;
+    r.gs = a.sh_gu_scales; r.us = a.sh_gu_scales + ms;
+    r.g_scale = a.sh_gscale[0]; r.u_scale = a.sh_gscale[1];
+  } else {
+    r.inter = a.I;
+    const size_t mc = (size_t)a.I * H / 2, ms = (size_t)a.I * H / 16;
+    r.gc = a.gu_codes + (size_t)(2 * expert) * mc; r.uc = r.gc + mc;
+    r.gs = a.gu_scales + (size_t)(2 * expert) * ms; r.us = r.gs + ms;
+    r.g_scale = a.gscale[3 * expert]; r.u_scale = a.gscale[3 * expert + 1];
+  }
+  return r;
+}
+
+// x chunk j (32 columns) of the layer input, RMS-normalised when asked
+__device__ __forceinline__ XChunk<FMT_NVFP4> input_chunk(const LayerArgs& a, int j, bool norm, double rms) {
+  XChunk<FMT_NVFP4> x = load_x<FMT_NVFP4>(a.x, j);
+  if (norm) {
+    const XChunk<FMT_NVFP4> g = load_x<FMT_NVFP4>(a.gamma, j);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float lo = round_bf16(rms_scale_bf16(bf16_lo(x.v[m]), rms) * bf16_lo(g.v[m]));
+      const float hi = round_bf16(rms_scale_bf16(bf16_hi(x.v[m]), rms) * bf16_hi(g.v[m]));
+      x.v[m] = pack_bf16x2(lo, hi);
+    }
+  }
+  return x;
+}
+
+// the 8 input columns c0..c0+7 (a 16-byte segment), RMS-normalised when asked
+__device__ __forceinline__ uint4 input_8(const LayerArgs& a, int c0, bool norm, double rms) {
+  uint4 v = *reinterpret_cast<const uint4*>(a.x + c0);
+  if (norm) {
+    const uint4 g = *reinterpret_cast<const uint4*>(a.gamma + c0);
+    uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      q[m] = pack_bf16x2(round_bf16(rms_scale_bf16(bf16_lo(q[m]), rms) * bf16_lo(gq[m])),
+                         round_bf16(rms_scale_bf16(bf16_hi(q[m]), rms) * bf16_hi(gq[m])));
+    v = make_uint4(q[0], q[1], q[2], q[3]);
+  }
+  return v;
+}
+
+// One gate/up item: rows 2p and 2p+1 of a selected expert, a whole wave per
+// row (H/32 chunks of 32 columns per row, NCH per lane).  Returns the packed
+// BF16 pair h[2p], h[2p+1] (valid in every lane).
+template <int NCH>
+struct GUItem {
+  uint4 c[2][2][NCH];       // [row][gate|up][chunk]
+  uint32_t s[2][2][NCH];
+};
+
+template <int NCH>
+__device__ __forceinline__ void gu_load(GUItem<NCH>& it, const GURows& R, int p, int H) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = 2 * p + rr;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int j = lane + 64 * c;
+      it.c[rr][0][c] = reinterpret_cast<const uint4*>(R.gc + (size_t)row * (H / 2))[j];
+      it.s[rr][0][c] = reinterpret_cast<const uint16_t*>(R.gs + (size_t)row * (H / 16))[j];
+      it.c[rr][1][c] = reinterpret_cast<const uint4*>(R.uc + (size_t)row * (H / 2))[j];
+      it.s[rr][1][c] = reinterpret_cast<const uint16_t*>(R.us + (size_t)row * (H / 16))[j];
+    }
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ uint32_t gu_finish(const GUItem<NCH>& it, const GURows& R,
+                                              const XChunk<FMT_NVFP4>* xc) {
+  float acc[2][2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s += chunk_dot(decode_nvfp4(it.c[rr][m][c], it.s[rr][m][c]), xc[c]);
+      acc[rr][m] = group_sum<64>(s);
+    }
+  float h[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const float gv = round_bf16(acc[rr][0] * R.g_scale);
+    const float uv = round_bf16(acc[rr][1] * R.u_scale);
+    h[rr] = round_bf16(silu_f32(gv)) * uv;
+  }
+  return pack_bf16x2(h[0], h[1]);
+}
+
+// Down rows of one workgroup: GPW = 64/GD rows per wave-wide load, DW
+// row-sets per workgroup (DW * GPW rows), chunk steps of GD lanes.
+template <int NCH, int GD, int DW, int MAXS>
+__global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, DecodeWs ws) {
+  constexpr int GPW = 64 / GD;
+  constexpr int DROWS = DW * GPW;                 // output rows per workgroup
+  constexpr int IMAXW = 2048 / 2;                 // h words per slot held in LDS (I <= 2048)
+  __shared__ float s_logit_part[4];
+  __shared__ int s_exp[MAXS];
+  __shared__ float s_w[MAXS];
+  __shared__ int s_nU;
+  __shared__ int s_sel[FLINT_MAX_TOP_K];
+  __shared__ uint32_t s_h[MAXS][IMAXW];           // h of every slot, packed BF16 pairs
+  __shared__ float s_red[4][DROWS];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = gridDim.x, NWV = 4 * G, gw = blockIdx.x * 4 + wave;
+  const int H = a.H, E = a.E, K = a.K, I = a.I, SI = a.SI;
+  const bool has_sh = SI > 0;
+  const int sh = has_sh ? 1 : 0;
+  const uint32_t epoch = *ws.epoch + 1u;
+  const bool norm = (a.flags & FLINT_PRE_RMSNORM) != 0;
+  const int hstride = (I > SI ? I : SI) / 2;
+  const size_t lstride = E, hrep = (size_t)(FLINT_MAX_TOP_K + 1) * hstride;
+  uint64_t* lw_all = ws.logit_words;              // [kReplicas][E]
+  uint64_t* hw_all = ws.h_words;                  // [kReplicas][slot][hstride] tagged h pairs
+  const int rep = blockIdx.x % kReplicas;
+  const uint64_t* lw = lw_all + (size_t)rep * lstride;   // this workgroup's copies
+  const uint64_t* hw = hw_all + (size_t)rep * hrep;
+
+  // ---- RMS of the token (every wave, from L2) -------------------------------
+  double rms = 1.0;
+  if (norm) {
+    double ss = 0.0;
+    for (int c = 8 * lane; c < H; c += 512) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a.x + c);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const double lo = bf16_lo(q[m]), hi = bf16_hi(q[m]);
+        ss = fma(lo, lo, ss);
+        ss = fma(hi, hi, ss);
+      }
+    }
+    rms = sqrt(wave_sum_f64(ss) / (double)H + (double)a.eps);
+  }
+  XChunk<FMT_NVFP4> xc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) xc[c] = input_chunk(a, lane + 64 * c, norm, rms);
+
+  // ---- phase 1: router quarter rows + shared expert gate/up ------------------
+  // expert e is owned by workgroup e % G; its 4 waves take a quarter each
+  const int qlen = H / 4;                          // columns per quarter
+  const int nsh_items = has_sh ? SI / 2 : 0;
+  // shared items are dealt workgroup-major (item j -> wave j % 4 of workgroup
+  // j / 4 when there are fewer items than waves, spread over all workgroups)
+  const int sh_stride = nsh_items > 0 && nsh_items < NWV ? NWV / nsh_items : 1;
+  const int sh_first = (gw % sh_stride == 0) ? gw / sh_stride : nsh_items;
+  GUItem<NCH> shit;
+  const bool my_sh = sh_first < nsh_items;
+  GURows Rsh;
+  if (has_sh) Rsh = gu_rows(a, -1);
+  if (my_sh) gu_load<NCH>(shit, Rsh, sh_first, H);
+  for (int e = blockIdx.x; e < E; e += G) {
+    float part = 0.f;
+    for (int c0 = wave * qlen + 8 * lane; c0 < (wave + 1) * qlen; c0 += 512) {
+      const uint4 w = *reinterpret_cast<const uint4*>(a.router + (size_t)e * H + c0);
+      const uint4 xq = input_8(a, c0, norm, rms);
+      part = dot2_bf16(w.x, xq.x, part);
+      part = dot2_bf16(w.y, xq.y, part);
+      part = dot2_bf16(w.z, xq.z, part);
+      part = dot2_bf16(w.w, xq.w, part);
+    }
+    part = group_sum<64>(part);
+    if (lane == 0) s_logit_part[wave] = part;
+    __syncthreads();
+    if (wave == 0) {
+      const float l = s_logit_part[0] + s_logit_part[1] + s_logit_part[2] + s_logit_part[3];
+      put_word_all(lw_all, lstride, e, epoch, __float_as_uint(l));
+    }
+    __syncthreads();
+  }
+  if (my_sh) put_word_all(hw_all, hrep, sh_first, epoch, gu_finish<NCH>(shit, Rsh, xc));
+  if (sh_stride == 1)
+    for (int it = gw + NWV; it < nsh_items; it += NWV) {   // shared experts wider than the grid
+      gu_load<NCH>(shit, Rsh, it, H);
+      put_word_all(hw_all, hrep, it, epoch, gu_finish<NCH>(shit, Rsh, xc));
+    }
+
+  // ---- phase 2: top-k (every workgroup, wave 0) and down-row prefetch --------
+  if (wave == 0) {
+    uint64_t key[4];
+    {
+      uint64_t wd[4];
+      const uint64_t* ptr[4];
+      bool ok[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ex = lane + 64 * q;
+        ok[q] = ex < E;
+        ptr[q] = lw + (ex < E ? ex : 0);
+      }
+      poll_words<4>(wd, ptr, ok, epoch, ws.error);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ex = lane + 64 * q;
+        key[q] = ok[q] ? (((uint64_t)float_order_key(__uint_as_float((uint32_t)wd[q])) << 32) |
+                          (uint32_t)~(uint32_t)ex)
+                       : 0ull;
+      }
+    }
+    // each lane sorts its four keys (descending); a round then takes the
+    // wave maximum of the lanes' heads and the winning lane pops its head
+#define FLINT_CSWAP(i, j) { const uint64_t hi_ = key[i] > key[j] ? key[i] : key[j]; \
+                            const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
+    FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
+#undef FLINT_CSWAP
+    float my_s = 0.f, ssum = 0.f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+      const uint64_t m = wave_max_key(key[0]);
+      if (key[0] == m) { key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull; }
+      const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
+      ssum += sg;
+      if (lane == k) { my_s = sg; my_e = (int)~(uint32_t)m; }
+    }
+    const float w = (a.flags & FLINT_RENORM) ? my_s / ssum : my_s;
+    // routed slots in ascending expert order: rank of each selected expert
+    if (lane < K) s_sel[lane] = my_e;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (lane < K) {
+      int rank = 0;
+      for (int kk = 0; kk < K; ++kk) rank += s_sel[kk] < my_e ? 1 : 0;
+      s_exp[sh + rank] = my_e;
+      s_w[sh + rank] = w;
+      if (blockIdx.x == 0) {
+        a.topk_idx[lane] = my_e;
+        a.topk_w[lane] = w;
+      }
+    }
+    if (lane == 0) {
+      s_nU = K;
+      if (has_sh) { s_exp[0] = -1; s_w[0] = 1.f; }
+    }
+  }
+  __syncthreads();
+  const int nU = s_nU, S = nU + sh;
+
+  // this workgroup's output rows and their down-row loads (all slots)
+  const int n0 = blockIdx.x * DROWS;
+  const int ncs = (I > SI ? I : SI) / 32;          // chunk steps of the widest slot
+  const int dch = (ncs + GD - 1) / GD;
+  // items (slot, chunk step) dealt to the 4 waves; at most MAXI per wave
+  constexpr int MAXI = (MAXS * 2 + 3) / 4;
+  uint4 draw[MAXI][DW];
+  uint32_t dsc[MAXI][DW];
+  const int grp = lane / GD, li = lane % GD;
+  const int total = S * dch;
+#pragma unroll
+  for (int u = 0; u < MAXI; ++u) {
+    const int it = wave + 4 * u;
+    const int s = it < total ? it / dch : 0, c = it - s * dch;
+    const int e = s_exp[s < S ? s : 0];
+    const int inter = e < 0 ? SI : I;
+    const int j = li + GD * c;
+    const bool ok = it < total && j < inter / 32;
+    const uint8_t* codes = e < 0 ? a.sh_d_codes : a.d_codes + (size_t)e * H * (inter / 2);
+    const uint8_t* scales = e < 0 ? a.sh_d_scales : a.d_scales + (size_t)e * H * (inter / 16);
+#pragma unroll
+    for (int rw = 0; rw < DW; ++rw) {
+      const int n = n0 + rw * GPW + grp;
+      draw[u][rw] = make_uint4(0, 0, 0, 0);
+      dsc[u][rw] = 0;
+      if (ok && n < H) {
+        draw[u][rw] = reinterpret_cast<const uint4*>(codes + (size_t)n * (inter / 2))[j];
+        dsc[u][rw] = reinterpret_cast<const uint16_t*>(scales + (size_t)n * (inter / 16))[j];
+      }
+    }
+  }
+
+  // ---- phase 3: routed gate/up items (round-robin over all waves) ------------
+  {
+    const int ipw = I / 2;                         // items per routed slot
+    const int nitems = nU * ipw;
+    for (int it0 = gw; it0 < nitems; it0 += 2 * NWV) {
+      GUItem<NCH> A, B;
+      const int itB = it0 + NWV;
+      const int rA = it0 / ipw, pA = it0 - rA * ipw;
+      const GURows RA = gu_rows(a, s_exp[sh + rA]);
+      gu_load<NCH>(A, RA, pA, H);
+      const bool hasB = itB < nitems;
+      const int rB = hasB ? itB / ipw : rA, pB = hasB ? itB - rB * ipw : pA;
+      const GURows RB = gu_rows(a, s_exp[sh + rB]);
+      if (hasB) gu_load<NCH>(B, RB, pB, H);
+      put_word_all(hw_all, hrep, (size_t)(sh + rA) * hstride + pA, epoch, gu_finish<NCH>(A, RA, xc));
+      if (hasB)
+        put_word_all(hw_all, hrep, (size_t)(sh + rB) * hstride + pB, epoch, gu_finish<NCH>(B, RB, xc));
+    }
+  }
+
+  // ---- phase 4: wait for h, down + combine -----------------------------------
+  {
+    // every (slot, word) pair, 8 per thread per batch
+    const int per = hstride;                         // words per slot (widest slot)
+    const int nw = S * per;
+    for (int q0 = threadIdx.x; q0 < nw; q0 += 8 * 256) {
+      uint64_t wd[8];
+      const uint64_t* ptr[8];
+      bool ok[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + 256 * u;
+        const int sl = q / per, wq = q - sl * per;
+        const int inter = (q < nw && s_exp[sl] < 0) ? SI : I;
+        ok[u] = q < nw && wq < inter / 2;
+        ptr[u] = hw + (ok[u] ? (size_t)sl * hstride + wq : 0);
+      }
+      poll_words<8>(wd, ptr, ok, epoch, ws.error);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + 256 * u;
+        if (ok[u]) s_h[q / per][q % per] = (uint32_t)wd[u];
+      }
+    }
+  }
+  // residual of this thread's output row, fetched early
+  const bool resid = (a.flags & FLINT_RESIDUAL) != 0;
+  float xres = 0.f;
+  if (resid && threadIdx.x < DROWS && n0 + (int)threadIdx.x < H) xres = bf16_bits_to_f32(a.x[n0 + threadIdx.x]);
+  __syncthreads();
+
+  float acc[DW];
+#pragma unroll
+  for (int rw = 0; rw < DW; ++rw) acc[rw] = 0.f;
+#pragma unroll
+  for (int u = 0; u < MAXI; ++u) {
+    const int it = wave + 4 * u;
+    if (it >= total) break;
+    const int s = it / dch, c = it - s * dch;
+    const int e = s_exp[s];
+    const int inter = e < 0 ? SI : I;
+    const int j = li + GD * c;
+    if (j >= inter / 32) continue;
+    XChunk<FMT_NVFP4> hx;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) hx.v[m] = s_h[s][16 * j + m];
+    const float f = s_w[s] * (e < 0 ? a.sh_gscale[2] : a.gscale[3 * e + 2]);
+#pragma unroll
+    for (int rw = 0; rw < DW; ++rw) acc[rw] = fmaf(f, chunk_dot(decode_nvfp4(draw[u][rw], dsc[u][rw]), hx), acc[rw]);
+  }
+#pragma unroll
+  for (int rw = 0; rw < DW; ++rw) {
+    const float v = group_sum<GD>(acc[rw]);
+    if (li == 0) s_red[wave][rw * GPW + grp] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < DROWS) {
+    const int n = n0 + threadIdx.x;
+    if (n < H) {
+      const float v = s_red[0][threadIdx.x] + s_red[1][threadIdx.x] + s_red[2][threadIdx.x] + s_red[3][threadIdx.x];
+      float o = round_bf16(v);
+      if (resid) o = xres + o;
+      a.out[n] = f32_to_bf16_bits(o);
+    }
+  }
+
+  // ---- the last workgroup to finish advances the epoch --------------------------
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == (uint32_t)G - 1) {
+      *ws.epoch = epoch;
+      __hip_atomic_store(ws.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+int g_num_cu = 0;
+
+struct FusedConfig { int G, gd, dw, nch; };
+
+int num_cu() {
+  if (g_num_cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_num_cu = n;
+  }
+  return g_num_cu;
+}
+
+// Grid and tiling of the fused path for this shape; false when the shape is
+// outside what the kernel holds (the three-kernel path then runs instead).
+bool fused_config(const LayerArgs& a, FusedConfig& c) {
+  if (a.B != 1 || (a.flags & FLINT_W_BF16)) return false;
+  if (a.H % 2048 || a.H > 4096) return false;
+  if (a.I > 2048 || a.SI > 2048 || a.K > FLINT_MAX_TOP_K) return false;
+  c.nch = a.H / 2048;
+  c.G = num_cu();
+  const int need = (a.H + 7) / 8;             // at most 8 output rows per workgroup
+  if (c.G > need) c.G = need;
+  const int rows_per_wg = (a.H + c.G - 1) / c.G;
+  const int red = a.SI > 0 && a.SI < a.I ? a.SI : a.I;
+  c.gd = 8;
+  while (c.gd < red / 32 && c.gd < 64) c.gd <<= 1;
+  c.dw = (rows_per_wg * c.gd + 63) / 64;
+  if (c.dw > 2) return false;
+  // every (slot, chunk step) item of the down rows must fit the prefetch
+  const int ncs = (a.I > a.SI ? a.I : a.SI) / 32;
+  const int dch = (ncs + c.gd - 1) / c.gd;
+  const int S = a.K + (a.SI > 0 ? 1 : 0);
+  constexpr int MAXI = ((FLINT_MAX_TOP_K + 1) * 2 + 3) / 4;
+  if (S * dch > 4 * MAXI) return false;
+  return true;
+}
+
+}  // namespace
+
+bool fused_decode_supported(const LayerArgs& a) {
+  FusedConfig c;
+  return fused_config(a, c);
+}
+
+hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
+  FusedConfig c;
+  if (!fused_config(a, c)) return hipErrorInvalidConfiguration;
+  constexpr int MAXS = FLINT_MAX_TOP_K + 1;
+#define FLINT_FUSED(NCH_, GD_, DW_)                                                              \
+  hipLaunchKernelGGL((fused_decode_b1_kernel<NCH_, GD_, DW_, MAXS>), dim3(c.G), dim3(256), 0, st, a, ws)
+#define FLINT_FUSED_GD(NCH_)                                                    \
+  switch (c.gd) {                                                               \
+    case 8: if (c.dw <= 1) FLINT_FUSED(NCH_, 8, 1); else FLINT_FUSED(NCH_, 8, 2); break;    \
+    case 16: if (c.dw <= 1) FLINT_FUSED(NCH_, 16, 1); else FLINT_FUSED(NCH_, 16, 2); break; \
+    case 32: if (c.dw <= 1) FLINT_FUSED(NCH_, 32, 1); else FLINT_FUSED(NCH_, 32, 2); break; \
+    default: if (c.dw <= 1) FLINT_FUSED(NCH_, 64, 1); else FLINT_FUSED(NCH_, 64, 2); break; \
+  }
+  if (c.nch == 1) { FLINT_FUSED_GD(1) } else { FLINT_FUSED_GD(2) }
+#undef FLINT_FUSED_GD
+#undef FLINT_FUSED
+  return hipGetLastError();
+}
+
+}  // namespace flint

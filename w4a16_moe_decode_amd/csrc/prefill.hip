@@ -271,36 +271,46 @@ __global__ __launch_bounds__(256) void prefill_router_kernel(LayerArgs a, Prefil
 }
 
 // ------------------------------------------------------------------ topk --
-// One workgroup per chunk of 64 tokens, one wave per token at a time.
-__global__ __launch_bounds__(256) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
+// One workgroup of 16 waves per chunk of 64 tokens, 4 tokens per wave, all
+// their logits fetched before the selection.  Writes the chunk's token
+// bitmask per expert and its pair count per expert.
+__global__ __launch_bounds__(1024) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
   __shared__ unsigned long long s_mask[FLINT_MAX_EXPERTS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
   const int c = blockIdx.x;
-  s_mask[threadIdx.x] = 0ull;
+  if (threadIdx.x < FLINT_MAX_EXPERTS) s_mask[threadIdx.x] = 0ull;
   __syncthreads();
   const bool renorm = (a.flags & FLINT_RENORM) != 0;
-  for (int j = wave; j < CHUNK; j += 4) {
-    const int t = c * CHUNK + j;
-    if (t >= T) break;
-    uint64_t key[4];
+  constexpr int TPW = CHUNK / 16;
+  uint64_t key[TPW][4];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = c * CHUNK + wave * TPW + u;
+    const int tt = t < T ? t : T - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int ex = lane + 64 * q;
-      key[q] = ex < E ? (((uint64_t)float_order_key(ws.logits[(size_t)t * E + ex]) << 32) |
-                         (uint32_t)~(uint32_t)ex)
-                      : 0ull;
+      key[u][q] = ex < E ? (((uint64_t)float_order_key(ws.logits[(size_t)tt * E + ex]) << 32) |
+                            (uint32_t)~(uint32_t)ex)
+                         : 0ull;
     }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int j = wave * TPW + u;
+    const int t = c * CHUNK + j;
+    if (t >= T) break;
     float my_s = 0.f, ssum = 0.f;
     int my_e = 0;
     for (int k = 0; k < K; ++k) {
-      uint64_t m = key[0];
+      uint64_t m = key[u][0];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) m = key[q] > m ? key[q] : m;
-      m = wave_max_u64(m);
+      for (int q = 1; q < 4; ++q) m = key[u][q] > m ? key[u][q] : m;
+      m = wave_max_key(m);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (key[q] == m) key[q] = 0ull;
+        if (key[u][q] == m) key[u][q] = 0ull;
       const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
       ssum += sg;
       if (lane == k) { my_s = sg; my_e = (int)~(uint32_t)m; }
@@ -312,22 +322,39 @@ __global__ __launch_bounds__(256) void prefill_topk_kernel(LayerArgs a, PrefillW
     }
   }
   __syncthreads();
-  if (threadIdx.x < E) ws.cmask[(size_t)c * E + threadIdx.x] = s_mask[threadIdx.x];
+  if (threadIdx.x < E) {
+    const uint64_t m = s_mask[threadIdx.x];
+    ws.cmask[(size_t)c * E + threadIdx.x] = m;
+    ws.cbase[(size_t)c * E + threadIdx.x] = __popcll(m);
+  }
 }
 
 // ------------------------------------------------------------------ scan --
-// One workgroup: per-expert counts and offsets, per-chunk bases, tile list.
+// One workgroup: per-expert counts and offsets, per-chunk bases (the counts
+// the top-k kernel left in cbase are replaced by exclusive prefixes), tile
+// list.  Loads are issued 16 chunks at a time.
 __global__ __launch_bounds__(256) void prefill_scan_kernel(LayerArgs a, PrefillWs ws, int T) {
   __shared__ int s_part[4];
   const int E = a.E, C = (T + CHUNK - 1) / CHUNK;
   const int e = threadIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool has_sh = a.SI > 0;
   int cnt = 0;
-  if (e < E)
-    for (int c = 0; c < C; ++c) {
-      ws.cbase[(size_t)c * E + e] = cnt;
-      cnt += __popcll(ws.cmask[(size_t)c * E + e]);
+  if (e < E) {
+    for (int c0 = 0; c0 < C; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = c0 + u < C ? ws.cbase[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int here = cnt;
+        cnt += v[u];
+        v[u] = here;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c0 + u < C) ws.cbase[(size_t)(c0 + u) * E + e] = v[u];
     }
+  }
   // exclusive scan of counts over experts (256 threads = 4 waves)
   int incl = cnt;
 #pragma unroll
@@ -343,7 +370,14 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(LayerArgs a, PrefillW
   if (e < E) {
     ws.counts[e] = cnt;
     ws.offsets[e] = offset;
-    for (int c = 0; c < C; ++c) ws.cbase[(size_t)c * E + e] += offset;
+    for (int c0 = 0; c0 < C; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = c0 + u < C ? ws.cbase[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c0 + u < C) ws.cbase[(size_t)(c0 + u) * E + e] = v[u] + offset;
+    }
   }
   const int total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   if (threadIdx.x == 0) {
@@ -644,7 +678,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   if (norm) hipLaunchKernelGGL(prefill_norm_kernel, dim3((T + 3) / 4), dim3(256), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
                      st, a, ws, T, xin);
-  hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
+  hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(256), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
   const dim3 ggu(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2));
