@@ -200,7 +200,6 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   __shared__ int s_exp[MAXS];
   __shared__ float s_w[MAXS];
   __shared__ int s_nU;
-  __shared__ int s_sel[FLINT_MAX_TOP_K];
   __shared__ uint32_t s_h[MAXS][IMAXW];           // h of every slot, packed BF16 pairs
   __shared__ float s_red[4][DROWS];
 
@@ -245,8 +244,10 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   const int nsh_items = has_sh ? SI / 2 : 0;
   // shared items are dealt workgroup-major (item j -> wave j % 4 of workgroup
   // j / 4 when there are fewer items than waves, spread over all workgroups)
+  // (wave 0 of each workgroup is left free to start polling the logits)
   const int sh_stride = nsh_items > 0 && nsh_items < NWV ? NWV / nsh_items : 1;
-  const int sh_first = (gw % sh_stride == 0) ? gw / sh_stride : nsh_items;
+  const int sh_off = sh_stride > 1 ? 1 : 0;
+  const int sh_first = (gw % sh_stride == sh_off) ? gw / sh_stride : nsh_items;
   GUItem<NCH> shit;
   const bool my_sh = sh_first < nsh_items;
   GURows Rsh;
@@ -306,23 +307,23 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
                             const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
     FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
 #undef FLINT_CSWAP
-    float my_s = 0.f, ssum = 0.f;
-    int my_e = 0;
+    // K rounds; lane k keeps the k-th selected key
+    uint64_t my_key = 0ull;
     for (int k = 0; k < K; ++k) {
       const uint64_t m = wave_max_key(key[0]);
       if (key[0] == m) { key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull; }
-      const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
-      ssum += sg;
-      if (lane == k) { my_s = sg; my_e = (int)~(uint32_t)m; }
+      if (lane == k) my_key = m;
     }
+    const int my_e = (int)~(uint32_t)my_key;
+    const float my_s = lane < K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
+    float ssum = 0.f;
+    for (int k = 0; k < K; ++k)                   // selection order, like the split path
+      ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
     const float w = (a.flags & FLINT_RENORM) ? my_s / ssum : my_s;
     // routed slots in ascending expert order: rank of each selected expert
-    if (lane < K) s_sel[lane] = my_e;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    int rank = 0;
+    for (int k = 0; k < K; ++k) rank += __builtin_amdgcn_readlane(my_e, k) < my_e ? 1 : 0;
     if (lane < K) {
-      int rank = 0;
-      for (int kk = 0; kk < K; ++kk) rank += s_sel[kk] < my_e ? 1 : 0;
       s_exp[sh + rank] = my_e;
       s_w[sh + rank] = w;
       if (blockIdx.x == 0) {
