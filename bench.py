@@ -30,6 +30,7 @@ not on the clock.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -301,6 +302,36 @@ def cpu_baseline(layer_src, shape, budget_s: float):
             "us_per_layer": el / n * 1e6}
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_decode_b1_flint_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_moe_decode_amd", "csrc", f) for f in ("fused.hip", "common.hpp")]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the single-launch layer from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
+    counter's reading for a plain copy of known size), or None when the
+    kernel's source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256_16", "").strip() != kernel_source_digest():
+        return None
+    return {"bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
+            "read_bytes": float(kv["read_bytes_per_launch"]),
+            "write_bytes": float(kv["write_bytes_per_launch"]),
+            "algorithmic_bytes_per_launch": float(kv["algorithmic_bytes_per_launch"])}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +344,9 @@ def main():
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="skip the 49-layer decode step")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8,192-token prefill")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="first run a plain elementwise copy (fp32 negate) of this many MiB three "
+                         "times, so that a counter run can scale FETCH_SIZE / WRITE_SIZE by it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -324,6 +358,13 @@ def main():
     fm.lib()
     dev = torch.device("cuda:0")
     shape = gen.SHAPE_FLINT
+    if args.calibration_copy_mib > 0:
+        src = torch.ones(args.calibration_copy_mib << 18, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)     # reads and writes calibration_copy_mib MiB each
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] generating {args.copies} layer copies on the GPU", file=sys.stderr, flush=True)
     layers, src0 = build_copies(shape, args.copies, args.seed, dev)
 
@@ -352,6 +393,7 @@ def main():
     # batch 1 runs as one kernel launch per layer: the dominant (only) kernel
     # is the single-launch layer, timed by the graph of back-to-back calls
     achieved = r1["nbytes"] / r1["secs"] / 1e9
+    traffic = measured_traffic()
     line = {
         "metric": METRIC,
         "value": round(r1["nbytes"] / r1["secs"] / 1e12, 4),
@@ -376,7 +418,9 @@ def main():
                                 "down": round(r1["stage_us"][2], 3)},
         "roofline": {"bound": "hbm", "kernel": "fused_decode_b1_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "traffic_read_write": [traffic["read_bytes"], traffic["write_bytes"]] if traffic else None,
+                     "algorithmic_bytes_per_launch": round(r1["nbytes"] / args.steps)},
     }
     if 8 in res:
         r8 = res[8]
