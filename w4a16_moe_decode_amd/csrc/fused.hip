@@ -242,9 +242,10 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   // expert e is owned by workgroup e % G; its 4 waves take a quarter each
   const int qlen = H / 4;                          // columns per quarter
   const int nsh_items = has_sh ? SI / 2 : 0;
-  // shared items are dealt workgroup-major (item j -> wave j % 4 of workgroup
-  // j / 4 when there are fewer items than waves, spread over all workgroups)
-  // (wave 0 of each workgroup is left free to start polling the logits)
+  // shared items are spread over all workgroups, one per sh_stride waves;
+  // when there are fewer items than waves, wave 0 of each workgroup gets
+  // none, so it can start polling the logits as soon as its router rows are
+  // published
   const int sh_stride = nsh_items > 0 && nsh_items < NWV ? NWV / nsh_items : 1;
   const int sh_off = sh_stride > 1 ? 1 : 0;
   const int sh_first = (gw % sh_stride == sh_off) ? gw / sh_stride : nsh_items;
@@ -339,6 +340,22 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   __syncthreads();
   const int nU = s_nU, S = nU + sh;
 
+  // ---- phase 3: routed gate/up items (round-robin over all waves) ------------
+  // The first round's loads (items gw and gw + NWV) are issued before the
+  // down-row prefetch: loads complete in order, so finishing these items then
+  // waits only on their own rows while the prefetch stays in flight.
+  const int ipw = I / 2;                           // items per routed slot
+  const int nitems = nU * ipw;
+  GUItem<NCH> A, B;
+  const int itB = gw + NWV;
+  const bool hasA = gw < nitems, hasB = itB < nitems;
+  const int rA = hasA ? gw / ipw : 0, pA = hasA ? gw - rA * ipw : 0;
+  const int rB = hasB ? itB / ipw : 0, pB = hasB ? itB - rB * ipw : 0;
+  const GURows RA = gu_rows(a, s_exp[sh + rA]);
+  const GURows RB = gu_rows(a, s_exp[sh + rB]);
+  if (hasA) gu_load<NCH>(A, RA, pA, H);
+  if (hasB) gu_load<NCH>(B, RB, pB, H);
+
   // this workgroup's output rows and their down-row loads (all slots)
   const int n0 = blockIdx.x * DROWS;
   const int ncs = (I > SI ? I : SI) / 32;          // chunk steps of the widest slot
@@ -359,36 +376,36 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
     const bool ok = it < total && j < inter / 32;
     const uint8_t* codes = e < 0 ? a.sh_d_codes : a.d_codes + (size_t)e * H * (inter / 2);
     const uint8_t* scales = e < 0 ? a.sh_d_scales : a.d_scales + (size_t)e * H * (inter / 16);
+    // every lane loads: a masked-off lane reads the first chunk of routed
+    // expert 0 (always present) and phase 4 skips its item, so no load is
+    // conditional and the compiler need not wait on one to merge a default
 #pragma unroll
     for (int rw = 0; rw < DW; ++rw) {
       const int n = n0 + rw * GPW + grp;
-      draw[u][rw] = make_uint4(0, 0, 0, 0);
-      dsc[u][rw] = 0;
-      if (ok && n < H) {
-        draw[u][rw] = reinterpret_cast<const uint4*>(codes + (size_t)n * (inter / 2))[j];
-        dsc[u][rw] = reinterpret_cast<const uint16_t*>(scales + (size_t)n * (inter / 16))[j];
-      }
+      const bool okr = ok && n < H;
+      const uint8_t* cp = okr ? codes + (size_t)n * (inter / 2) + 16 * j : a.d_codes;
+      const uint8_t* sp = okr ? scales + (size_t)n * (inter / 16) + 2 * j : a.d_scales;
+      draw[u][rw] = *reinterpret_cast<const uint4*>(cp);
+      dsc[u][rw] = *reinterpret_cast<const uint16_t*>(sp);
     }
   }
 
-  // ---- phase 3: routed gate/up items (round-robin over all waves) ------------
-  {
-    const int ipw = I / 2;                         // items per routed slot
-    const int nitems = nU * ipw;
-    for (int it0 = gw; it0 < nitems; it0 += 2 * NWV) {
-      GUItem<NCH> A, B;
-      const int itB = it0 + NWV;
-      const int rA = it0 / ipw, pA = it0 - rA * ipw;
-      const GURows RA = gu_rows(a, s_exp[sh + rA]);
-      gu_load<NCH>(A, RA, pA, H);
-      const bool hasB = itB < nitems;
-      const int rB = hasB ? itB / ipw : rA, pB = hasB ? itB - rB * ipw : pA;
-      const GURows RB = gu_rows(a, s_exp[sh + rB]);
-      if (hasB) gu_load<NCH>(B, RB, pB, H);
-      put_word_all(hw_all, hrep, (size_t)(sh + rA) * hstride + pA, epoch, gu_finish<NCH>(A, RA, xc));
-      if (hasB)
-        put_word_all(hw_all, hrep, (size_t)(sh + rB) * hstride + pB, epoch, gu_finish<NCH>(B, RB, xc));
-    }
+  if (hasA) put_word_all(hw_all, hrep, (size_t)(sh + rA) * hstride + pA, epoch, gu_finish<NCH>(A, RA, xc));
+  if (hasB) put_word_all(hw_all, hrep, (size_t)(sh + rB) * hstride + pB, epoch, gu_finish<NCH>(B, RB, xc));
+  // further rounds, for layers with more routed items than twice the waves
+  for (int it0 = gw + 2 * NWV; it0 < nitems; it0 += 2 * NWV) {
+    GUItem<NCH> C, D;
+    const int itD = it0 + NWV;
+    const int rC = it0 / ipw, pC = it0 - rC * ipw;
+    const GURows RC = gu_rows(a, s_exp[sh + rC]);
+    gu_load<NCH>(C, RC, pC, H);
+    const bool hasD = itD < nitems;
+    const int rD = hasD ? itD / ipw : rC, pD = hasD ? itD - rD * ipw : pC;
+    const GURows RD = gu_rows(a, s_exp[sh + rD]);
+    if (hasD) gu_load<NCH>(D, RD, pD, H);
+    put_word_all(hw_all, hrep, (size_t)(sh + rC) * hstride + pC, epoch, gu_finish<NCH>(C, RC, xc));
+    if (hasD)
+      put_word_all(hw_all, hrep, (size_t)(sh + rD) * hstride + pD, epoch, gu_finish<NCH>(D, RD, xc));
   }
 
   // ---- phase 4: wait for h, down + combine -----------------------------------
@@ -457,15 +474,12 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
     }
   }
 
-  // ---- the last workgroup to finish advances the epoch --------------------------
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == (uint32_t)G - 1) {
-      *ws.epoch = epoch;
-      __hip_atomic_store(ws.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  // ---- advance the epoch for the next launch -----------------------------------
+  // The grid is no wider than E, so every workgroup published at least one
+  // router logit, tagged with the epoch it read at its start, and workgroup 0
+  // has seen all of them before its top-k: no workgroup of this launch can
+  // still be about to read the old value.  No ticket round trip is needed.
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ws.epoch = epoch;
 }
 
 int g_num_cu = 0;
@@ -493,6 +507,7 @@ bool fused_config(const LayerArgs& a, FusedConfig& c) {
   c.G = num_cu();
   const int need = (a.H + 7) / 8;             // at most 8 output rows per workgroup
   if (c.G > need) c.G = need;
+  if (c.G > a.E) c.G = a.E;                   // every workgroup owns a router row
   const int rows_per_wg = (a.H + c.G - 1) / c.G;
   const int red = a.SI > 0 && a.SI < a.I ? a.SI : a.I;
   c.gd = 8;
