@@ -303,7 +303,7 @@ def cpu_baseline(layer_src, shape, budget_s: float):
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_decode_b1_flint_hbm_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_moe_decode_amd", "csrc", f) for f in ("fused.hip", "common.hpp")]
+KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_moe_decode_amd", "csrc", f) for f in ("fused.hip", "fused_common.hpp", "common.hpp")]
 
 
 def kernel_source_digest() -> str:

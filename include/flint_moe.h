@@ -71,7 +71,17 @@ extern "C" {
 #define FLINT_RESIDUAL     0x8u  /* out = BF16(x + BF16(layer(xn))) */
 #define FLINT_SPLIT        0x10u /* decode: always run the three-kernel path
                                     (by default a batch-1 NVFP4 call with
-                                    hidden 2048 or 4096 runs as one launch) */
+                                    hidden 2048 or 4096 runs as one launch; see
+                                    flint_moe_decode_path) */
+#define FLINT_SINGLE_BATCH 0x20u /* decode, batch 2..8: run as one launch when
+                                    the shape allows (slower than the three
+                                    kernels on MI355X at present: one wave per
+                                    SIMD leaves its VALU latency exposed) */
+
+/* decode paths reported by flint_moe_decode_path */
+#define FLINT_PATH_SPLIT        0  /* three kernels: route, gate/up, down    */
+#define FLINT_PATH_SINGLE_ONE   1  /* one launch, batch 1                    */
+#define FLINT_PATH_SINGLE_BATCH 2  /* one launch, batch 2..8                 */
 
 /* source NVFP4 super-block byte orders accepted by the repack */
 #define FLINT_SRC_INTERLEAVED   0  /* 4 x [scale byte, 8 code bytes]          */
@@ -218,27 +228,37 @@ FLINT_API int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int
  *   topk_w    (device) float [batch][K] or NULL; the combine weights
  *   gamma     (device) BF16 [H], required with FLINT_PRE_RMSNORM
  *   ws        (device) workspace of at least flint_moe_workspace_bytes(shape, batch)
- * Batch 1 with NVFP4 weights and hidden 2048 or 4096 (I, SI <= 2048) runs
- * as one launch of a persistent grid (one workgroup per compute unit) whose
- * phases hand data over through epoch-tagged words in the workspace; every
- * other call, and any call with FLINT_SPLIT, enqueues three kernels: route
- * (RMSNorm, router GEMV, top-k, expert set), gate/up (+SiLU*up), down
- * (weighted combine, shared expert, residual).  Both give the same result
- * up to fp32 summation order. */
+ * With NVFP4 weights and hidden 2048 or 4096 (I, SI <= 2048) a batch-1 call
+ * is one launch of a persistent grid (one workgroup per compute unit) whose
+ * phases hand data over through epoch-tagged words in the workspace; so is a
+ * batch 2..8 call with FLINT_SINGLE_BATCH when also batch * (K + 1) *
+ * max(I, SI) <= 32768.  Every other call, and any call with FLINT_SPLIT,
+ * enqueues three kernels: route (RMSNorm, router GEMV, top-k, expert set),
+ * gate/up (+SiLU*up), down (weighted combine, shared expert, residual).
+ * flint_moe_decode_path tells which.  All paths give the same result up to
+ * fp32 summation order. */
 FLINT_API int32_t flint_moe_decode(const flint_moe_shape* shape, const flint_moe_weights* weights,
                          const void* x, int32_t batch, void* out, int32_t* topk_idx,
                          float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
                          void* stream);
 
-/* One stage of flint_moe_decode, same arguments: stage 0 = route (router
- * GEMV and top-k), 1 = gate/up, 2 = down + combine.  Enqueuing stages 0, 1, 2 in order on one
- * stream with the same workspace is exactly flint_moe_decode; a stage reads
- * what the previous one left in the workspace.  For per-kernel timing and
- * for callers that interleave other work between stages. */
+/* One stage of the three-kernel path, same arguments as flint_moe_decode:
+ * stage 0 = route (router GEMV and top-k), 1 = gate/up, 2 = down + combine.
+ * Enqueuing stages 0, 1, 2 in order on one stream with the same workspace is
+ * exactly flint_moe_decode with FLINT_SPLIT; a stage reads what the previous
+ * one left in the workspace.  For per-kernel timing and for callers that
+ * interleave other work between stages. */
 FLINT_API int32_t flint_moe_decode_stage(int32_t stage, const flint_moe_shape* shape,
                                const flint_moe_weights* weights, const void* x, int32_t batch,
                                void* out, int32_t* topk_idx, float* topk_w, const void* gamma,
                                void* ws, int64_t ws_bytes, void* stream);
+
+/* Which kernels flint_moe_decode runs for this shape (flags included) and
+ * batch: FLINT_PATH_SPLIT, FLINT_PATH_SINGLE_ONE or FLINT_PATH_SINGLE_BATCH.
+ * Reads only the shape; enqueues nothing.  Returns -status for an invalid
+ * shape (-FLINT_ERR_INVALID_ARG, -FLINT_ERR_UNSUPPORTED) or a batch outside
+ * 1..8 (-FLINT_ERR_UNSUPPORTED). */
+FLINT_API int32_t flint_moe_decode_path(const flint_moe_shape* shape, int32_t batch);
 
 /* ----------------------------------------------------------------- prefill -- */
 

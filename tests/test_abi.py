@@ -124,3 +124,33 @@ def test_repack_and_dense_validation_codes():
              fm.FLINT_EPI_NONE, None, v(96), eps, None) == fm.FLINT_ERR_UNSUPPORTED
     assert d(None, None, None, None, 64, 64, fm.FLINT_W_BF16, v(64), 1, v(80), 0, None, None, eps,
              None) == fm.FLINT_ERR_INVALID_ARG
+
+
+def test_decode_path_rules():
+    """Which kernels a decode call runs: host logic only, nothing enqueued."""
+    flint = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
+    single = fm.FlintMoeShape(2048, 256, 512, 512, 6, fm.FLINT_SINGLE_BATCH, 1e-6)
+    assert fm.flint_moe_decode_path(flint, 1) == fm.FLINT_PATH_SINGLE_ONE
+    assert fm.flint_moe_decode_path(single, 1) == fm.FLINT_PATH_SINGLE_ONE
+    for b in range(2, 9):
+        assert fm.flint_moe_decode_path(flint, b) == fm.FLINT_PATH_SPLIT      # opt-in only
+        assert fm.flint_moe_decode_path(single, b) == fm.FLINT_PATH_SINGLE_BATCH
+    for flags in (fm.FLINT_SPLIT, fm.FLINT_W_BF16):
+        s = fm.FlintMoeShape(2048, 256, 512, 512, 6, flags, 1e-6)
+        assert fm.flint_moe_decode_path(s, 1) == fm.FLINT_PATH_SPLIT
+        assert fm.flint_moe_decode_path(s, 8) == fm.FLINT_PATH_SPLIT
+    tiny = fm.FlintMoeShape(512, 32, 128, 128, 4, 0, 1e-6)          # hidden not a multiple of 2048
+    assert fm.flint_moe_decode_path(tiny, 1) == fm.FLINT_PATH_SPLIT
+    # h of every (token, expert) pair must fit the LDS pool (16384 words):
+    # 3 * 9 * 1024 / 2 fits, 4 * 9 * 1024 / 2 does not
+    wide = fm.FlintMoeShape(2048, 48, 512, 1024, 8, fm.FLINT_SINGLE_BATCH, 1e-6)
+    assert fm.flint_moe_decode_path(wide, 1) == fm.FLINT_PATH_SINGLE_ONE
+    assert fm.flint_moe_decode_path(wide, 3) == fm.FLINT_PATH_SINGLE_BATCH
+    assert fm.flint_moe_decode_path(wide, 4) == fm.FLINT_PATH_SPLIT
+    for b in (0, 9):
+        with pytest.raises(fm.FlintError) as e:
+            fm.flint_moe_decode_path(flint, b)
+        assert e.value.status == fm.FLINT_ERR_UNSUPPORTED
+    with pytest.raises(fm.FlintError) as e:
+        fm.flint_moe_decode_path(fm.FlintMoeShape(2048, 256, 512, 512, 0, 0, 1e-6), 1)
+    assert e.value.status == fm.FLINT_ERR_INVALID_ARG

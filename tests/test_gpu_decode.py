@@ -86,18 +86,24 @@ def test_zero_input_routes_to_lowest_experts(flint_layer):
 
 
 def test_results_are_bit_reproducible_and_stages_compose(flint_layer):
-    """No float atomics: two runs give identical bits; running the three
-    stages by hand equals one decode call."""
+    """No float atomics: two runs give identical bits, on the single-launch
+    path and on the three-kernel one; running the three stages by hand equals
+    one three-kernel call."""
     _, layer = flint_layer
-    runner = fm.DecodeRunner(layer, FLINT.top_k, 0)
+    runner = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    split = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SPLIT)
+    assert fm.flint_moe_decode_path(runner.shape, 8) == fm.FLINT_PATH_SINGLE_BATCH
     x = gen.activations(7, 8, FLINT.hidden).cuda()
     a = runner(x)
     b = runner(x)
+    s1 = split(x)
+    s2 = split(x)
     c = torch.empty_like(x)
     for st in range(3):
-        runner.stage(st, x, c)
+        split.stage(st, x, c)
     torch.cuda.synchronize()
-    assert torch.equal(a, b) and torch.equal(a, c)
+    assert torch.equal(a, b)
+    assert torch.equal(s1, s2) and torch.equal(s1, c)
 
 
 def test_rotating_copies_and_workspace_reuse(flint_layer):

@@ -1,5 +1,6 @@
-"""The single-launch batch-1 decode path (hidden 2048 or 4096, NVFP4)
-against the oracle and against the three-kernel path (FLINT_SPLIT)."""
+"""The single-launch decode paths (batch 1, and batch 2..8; hidden 2048 or
+4096, NVFP4) against the oracle and against the three-kernel path
+(FLINT_SPLIT)."""
 import pytest
 import torch
 
@@ -12,19 +13,70 @@ pytestmark = pytest.mark.gpu
 FLINT = gen.SHAPE_FLINT
 
 
-@pytest.mark.parametrize("shape", [
+SHAPES = [
     FLINT,
     gen.MoeShape(hidden=4096, n_experts=64, inter=256, shared_inter=512, top_k=6),    # 2 chunks per lane
     gen.MoeShape(hidden=2048, n_experts=48, inter=512, shared_inter=1024, top_k=8),   # wide shared, K=8
     gen.MoeShape(hidden=2048, n_experts=300 // 2, inter=128, shared_inter=0, top_k=4),  # no shared
     gen.MoeShape(hidden=2048, n_experts=16, inter=2048, shared_inter=64, top_k=2),    # widest routed
-], ids=["flint", "h4096", "wide-shared-k8", "no-shared", "wide-routed"])
-@pytest.mark.parametrize("flags", [0, fm.FLINT_RENORM, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL])
+]
+SHAPE_IDS = ["flint", "h4096", "wide-shared-k8", "no-shared", "wide-routed"]
+FLAG_SETS = [0, fm.FLINT_RENORM, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
+@pytest.mark.parametrize("flags", FLAG_SETS)
 def test_fused_against_oracle(shape, flags):
     src = gen.moe_layer_source(shape, 500 + shape.hidden + shape.n_experts)
     layer = pack(src)
+    r = fm.DecodeRunner(layer, shape.top_k, flags)
+    # the widest routed expert needs more down-row items than the one-token
+    # kernel keeps in flight (3 slots x 8 chunk steps > 20): three kernels
+    want = fm.FLINT_PATH_SPLIT if shape.inter == 2048 else fm.FLINT_PATH_SINGLE_ONE
+    assert fm.flint_moe_decode_path(r.shape, 1) == want
     for seed in (1, 2):
-        run_decode_case(DecodeCase(shape, seed=seed, batch=1, flags=flags), src=src, layer=layer)
+        run_decode_case(DecodeCase(shape, seed=seed, batch=1, flags=flags), src=src, layer=layer,
+                        runner=r)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
+@pytest.mark.parametrize("flags", FLAG_SETS)
+def test_fused_batch_against_oracle(shape, flags):
+    """Batch 2..8 in one launch; the grid is wider than E for the small
+    expert counts, so the arrival words are exercised too."""
+    src = gen.moe_layer_source(shape, 510 + shape.hidden + shape.n_experts)
+    layer = pack(src)
+    flags |= fm.FLINT_SINGLE_BATCH
+    r = fm.DecodeRunner(layer, shape.top_k, flags)
+    for seed, batch in ((1, 2), (2, 5), (3, 8)):
+        path = fm.flint_moe_decode_path(r.shape, batch)
+        want = fm.FLINT_PATH_SINGLE_BATCH
+        pairs = batch * (shape.top_k + (1 if shape.shared_inter else 0))
+        if pairs * max(shape.inter, shape.shared_inter) > 32768:
+            want = fm.FLINT_PATH_SPLIT          # the h of every pair would not fit in LDS
+        assert path == want
+        run_decode_case(DecodeCase(shape, seed=seed, batch=batch, flags=flags), src=src, layer=layer,
+                        runner=r)
+    assert fm.decode_error_word(r) == 0
+
+
+def test_fused_batch_matches_split_and_is_reproducible():
+    src = gen.moe_layer_source(FLINT, 603)
+    layer = pack(src)
+    fused = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    split = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SPLIT)
+    for i, b in enumerate([2, 3, 4, 6, 7, 8]):
+        x = gen.activations(710 + i, b, FLINT.hidden, "cpu", "correlated" if i % 2 else "iid").cuda()
+        ia = torch.empty((b, FLINT.top_k), dtype=torch.int32, device="cuda")
+        ib = torch.empty_like(ia)
+        a = fused(x, topk_idx=ia)
+        a2 = fused(x)
+        c = split(x, topk_idx=ib)
+        torch.cuda.synchronize()
+        assert torch.equal(a, a2)
+        assert torch.equal(ia, ib)
+        compare_outputs(a.cpu().float().numpy(), c.cpu().float().numpy(), "fused vs split")
+    assert fm.decode_error_word(fused) == 0
 
 
 def test_fused_matches_split_and_is_reproducible():
@@ -43,22 +95,25 @@ def test_fused_matches_split_and_is_reproducible():
 
 
 def test_fused_and_split_share_a_workspace():
-    """Batch-1 (single launch) and batch-8 (three kernels) calls alternate on
+    """Batch-1 and batch-n single launches and three-kernel calls alternate on
     one workspace; the launch epoch keeps their hand-off words apart."""
     src = gen.moe_layer_source(FLINT, 601)
     layer = pack(src)
-    r = fm.DecodeRunner(layer, FLINT.top_k, 0)
-    for i, b in enumerate([1, 8, 1, 1, 3, 1]):
-        run_decode_case(DecodeCase(FLINT, seed=800 + i, batch=b), src=src, layer=layer, runner=r)
+    r = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    s = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SPLIT)
+    s.ws = r.ws
+    for i, (b, runner) in enumerate([(1, r), (8, r), (1, s), (1, r), (3, s), (3, r), (1, r), (8, s), (2, r)]):
+        run_decode_case(DecodeCase(FLINT, seed=800 + i, batch=b), src=src, layer=layer, runner=runner)
     assert fm.decode_error_word(r) == 0
 
 
 def test_fused_error_word_stays_clear():
     src = gen.moe_layer_source(FLINT, 602)
     layer = pack(src)
-    r = fm.DecodeRunner(layer, FLINT.top_k, 0)
-    x = gen.activations(9, 1, FLINT.hidden).cuda()
-    for _ in range(20):
-        r(x)
+    r = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    for b in (1, 8):
+        x = gen.activations(9, b, FLINT.hidden).cuda()
+        for _ in range(20):
+            r(x)
     torch.cuda.synchronize()
     assert fm.decode_error_word(r) == 0

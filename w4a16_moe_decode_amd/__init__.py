@@ -34,6 +34,11 @@ FLINT_W_BF16 = 0x2
 FLINT_PRE_RMSNORM = 0x4
 FLINT_RESIDUAL = 0x8
 FLINT_SPLIT = 0x10
+FLINT_SINGLE_BATCH = 0x20
+
+FLINT_PATH_SPLIT = 0
+FLINT_PATH_SINGLE_ONE = 1
+FLINT_PATH_SINGLE_BATCH = 2
 
 FLINT_SRC_INTERLEAVED = 0
 FLINT_SRC_SCALES_FIRST = 1
@@ -49,7 +54,8 @@ MAX_DECODE_BATCH = 8
 EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
-    "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_prefill", "flint_dense_gemv",
+    "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_prefill",
+    "flint_dense_gemv",
 )
 
 
@@ -102,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.flint_moe_decode.argtypes = dec
         L.flint_moe_decode_stage.restype = i32
         L.flint_moe_decode_stage.argtypes = [i32] + dec
+        L.flint_moe_decode_path.restype = i32
+        L.flint_moe_decode_path.argtypes = [ctypes.POINTER(FlintMoeShape), i32]
         L.flint_moe_prefill.restype = i32
         L.flint_moe_prefill.argtypes = dec
         L.flint_dense_gemv.restype = i32
@@ -181,6 +189,13 @@ def flint_moe_decode_stage(stage, shape, weights, x, batch, out, topk_idx, topk_
     _check("flint_moe_decode_stage", lib().flint_moe_decode_stage(
         stage, ctypes.byref(shape), ctypes.byref(weights), _p(x), batch, _p(out), _p(topk_idx),
         _p(topk_w), _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+
+
+def flint_moe_decode_path(shape: FlintMoeShape, batch: int) -> int:
+    v = lib().flint_moe_decode_path(ctypes.byref(shape), int(batch))
+    if v < 0:
+        raise FlintError("flint_moe_decode_path", -v)
+    return v
 
 
 def flint_moe_prefill(shape, weights, x, n_tokens, out, topk_idx, topk_w, gamma, ws, ws_bytes,

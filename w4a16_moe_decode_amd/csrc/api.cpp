@@ -28,7 +28,8 @@ int check_shape(const flint_moe_shape* s) {
   if (s->hidden > 4096) return FLINT_ERR_UNSUPPORTED;
   if (s->n_experts > FLINT_MAX_EXPERTS) return FLINT_ERR_UNSUPPORTED;
   if (s->top_k > FLINT_MAX_TOP_K || s->top_k > s->n_experts) return FLINT_ERR_UNSUPPORTED;
-  if (s->flags & ~(FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | FLINT_SPLIT))
+  if (s->flags & ~(FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | FLINT_SPLIT |
+                   FLINT_SINGLE_BATCH))
     return FLINT_ERR_UNSUPPORTED;
   if ((s->flags & FLINT_PRE_RMSNORM) && !(s->rms_eps >= 0.0f)) return FLINT_ERR_INVALID_ARG;
   return FLINT_OK;
@@ -128,7 +129,9 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
   w.error = reinterpret_cast<uint32_t*>(take(4));
   // 64 copies of every hand-off word for the single-launch path (its readers
   // each take their own copy); the three-kernel path uses the first [B][E]
-  w.logit_words = reinterpret_cast<uint64_t*>(take((int64_t)64 * B * s.n_experts * 8));
+  // (after the single-launch paths' 8 x 8 x E words: one arrival word per
+  // workgroup beyond E, at most 256)
+  w.logit_words = reinterpret_cast<uint64_t*>(take(((int64_t)64 * B * s.n_experts + 256) * 8));
   w.xn = reinterpret_cast<uint16_t*>(take((int64_t)B * s.hidden * 2));
   w.idx = reinterpret_cast<int32_t*>(take((int64_t)B * FLINT_MAX_TOP_K * 4));
   w.wgt = reinterpret_cast<float*>(take((int64_t)B * FLINT_MAX_TOP_K * 4));
@@ -255,8 +258,11 @@ static int32_t decode_common(int32_t stage, const flint_moe_shape* shape,
   a.topk_w = topk_w ? topk_w : w.wgt;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (stage < 0 && !(shape->flags & FLINT_SPLIT) && fused_decode_supported(a))
-    return to_status(launch_fused_decode(a, w, s));
+  if (stage < 0 && !(shape->flags & FLINT_SPLIT)) {
+    if (fused_decode_supported(a)) return to_status(launch_fused_decode(a, w, s));
+    if ((a.flags & FLINT_SINGLE_BATCH) && fused_decode_bn_supported(a))
+      return to_status(launch_fused_decode_bn(a, w, s));
+  }
   if (stage < 0 || stage == 0) e = launch_route(a, w, s);
   if (e == hipSuccess && (stage < 0 || stage == 1)) e = launch_gate_up(a, w, false, false, s);
   if (e == hipSuccess && (stage < 0 || stage == 2)) e = launch_down(a, w, false, 0, nullptr, nullptr, s);
@@ -278,6 +284,20 @@ int32_t flint_moe_decode_stage(int32_t stage, const flint_moe_shape* shape,
   if (stage < 0 || stage > 2) return FLINT_ERR_INVALID_ARG;
   return decode_common(stage, shape, weights, x, batch, out, topk_idx, topk_w, gamma, ws, ws_bytes,
                        stream);
+}
+
+int32_t flint_moe_decode_path(const flint_moe_shape* shape, int32_t batch) {
+  const int st = check_shape(shape);
+  if (st != FLINT_OK) return -st;
+  if (batch < 1 || batch > FLINT_MAX_DECODE_BATCH) return -FLINT_ERR_UNSUPPORTED;
+  if (shape->flags & FLINT_SPLIT) return FLINT_PATH_SPLIT;
+  LayerArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
+  a.K = shape->top_k; a.B = batch; a.flags = shape->flags; a.eps = shape->rms_eps;
+  if (fused_decode_supported(a)) return FLINT_PATH_SINGLE_ONE;
+  if ((a.flags & FLINT_SINGLE_BATCH) && fused_decode_bn_supported(a)) return FLINT_PATH_SINGLE_BATCH;
+  return FLINT_PATH_SPLIT;
 }
 
 int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_moe_weights* weights,

@@ -293,6 +293,8 @@ struct LayerArgs {
 hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 bool fused_decode_supported(const LayerArgs& a);
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
+bool fused_decode_bn_supported(const LayerArgs& a);
+hipError_t launch_fused_decode_bn(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm_on_the_fly,
                           hipStream_t st);
 hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int dense_epilogue,

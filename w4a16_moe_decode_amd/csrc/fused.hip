@@ -26,88 +26,10 @@
 // needed.  Every wait is bounded: if a word does not arrive (it cannot while
 // all workgroups are resident) the kernel records an error and still exits.
 // The grid never exceeds the number of compute units, one workgroup each.
-#include "common.hpp"
+#include "fused_common.hpp"
 
 namespace flint {
 namespace {
-
-constexpr uint32_t kFusedSpin = 1u << 20;
-
-__device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch, uint32_t* err) {
-  uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (uint32_t spin = 0; (uint32_t)(w >> 32) != epoch && spin < kFusedSpin; ++spin) {
-    __builtin_amdgcn_s_sleep(1);
-    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if ((uint32_t)(w >> 32) != epoch) *err = 1u;
-  return w;
-}
-
-// Batched wait: all U words are loaded at once, then only the ones that do
-// not carry the epoch yet are loaded again.  Entries with ok[u] false are
-// skipped.
-template <int U>
-__device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* const (&p)[U],
-                                           const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    w[u] = ok[u] ? __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : ((uint64_t)epoch << 32);
-  for (uint32_t spin = 0; spin < kFusedSpin; ++spin) {
-    bool ready = true;
-#pragma unroll
-    for (int u = 0; u < U; ++u) ready = ready && (uint32_t)(w[u] >> 32) == epoch;
-    if (ready) return;
-    __builtin_amdgcn_s_sleep(8);     // back off: every workgroup is polling
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if ((uint32_t)(w[u] >> 32) != epoch)
-        w[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  *err = 1u;
-}
-
-__device__ __forceinline__ void put_word(uint64_t* p, uint32_t epoch, uint32_t payload) {
-  __hip_atomic_store(p, ((uint64_t)epoch << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Hand-off words are published in kReplicas copies (lanes 0..kReplicas-1 of
-// the writing wave each store one); workgroup g reads copy g % kReplicas.
-// Every workgroup needs every word: one copy per XCD keeps the readers of a
-// line to the workgroups of one XCD without multiplying the stores much.
-constexpr int kReplicas = 8;
-
-__device__ __forceinline__ void put_word_all(uint64_t* base, size_t stride, size_t idx, uint32_t epoch,
-                                             uint32_t payload) {
-  const int lane = threadIdx.x & 63;
-  if (lane < kReplicas) put_word(base + (size_t)lane * stride + idx, epoch, payload);
-}
-
-struct GURows {            // gate and up rows of one selected expert
-  const uint8_t* gc; const uint8_t* gs;
-  const uint8_t* uc; const uint8_t* us;
-  float g_scale, u_scale;
-  int inter;
-};
-
-__device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert /* -1 = shared */) {
-  GURows r;
-  const int H = a.H;
-  if (expert < 0) {
-    r.inter = a.SI;
-    const size_t mc = (size_t)a.SI * H / 2, ms = (size_t)a.SI * H / 16;
-    r.gc = a.sh_gu_codes; r.uc = a.sh_gu_codes + mc;
-    r.gs = a.sh_gu_scales; r.us = a.sh_gu_scales + ms;
-    r.g_scale = a.sh_gscale[0]; r.u_scale = a.sh_gscale[1];
-  } else {
-    r.inter = a.I;
-    const size_t mc = (size_t)a.I * H / 2, ms = (size_t)a.I * H / 16;
-    r.gc = a.gu_codes + (size_t)(2 * expert) * mc; r.uc = r.gc + mc;
-    r.gs = a.gu_scales + (size_t)(2 * expert) * ms; r.us = r.gs + ms;
-    r.g_scale = a.gscale[3 * expert]; r.u_scale = a.gscale[3 * expert + 1];
-  }
-  return r;
-}
 
 // x chunk j (32 columns) of the layer input, RMS-normalised when asked
 __device__ __forceinline__ XChunk<FMT_NVFP4> input_chunk(const LayerArgs& a, int j, bool norm, double rms) {
@@ -138,32 +60,6 @@ __device__ __forceinline__ uint4 input_8(const LayerArgs& a, int c0, bool norm, 
     v = make_uint4(q[0], q[1], q[2], q[3]);
   }
   return v;
-}
-
-// One gate/up item: rows 2p and 2p+1 of a selected expert, a whole wave per
-// row (H/32 chunks of 32 columns per row, NCH per lane).  Returns the packed
-// BF16 pair h[2p], h[2p+1] (valid in every lane).
-template <int NCH>
-struct GUItem {
-  uint4 c[2][2][NCH];       // [row][gate|up][chunk]
-  uint32_t s[2][2][NCH];
-};
-
-template <int NCH>
-__device__ __forceinline__ void gu_load(GUItem<NCH>& it, const GURows& R, int p, int H) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int row = 2 * p + rr;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int j = lane + 64 * c;
-      it.c[rr][0][c] = reinterpret_cast<const uint4*>(R.gc + (size_t)row * (H / 2))[j];
-      it.s[rr][0][c] = reinterpret_cast<const uint16_t*>(R.gs + (size_t)row * (H / 16))[j];
-      it.c[rr][1][c] = reinterpret_cast<const uint4*>(R.uc + (size_t)row * (H / 2))[j];
-      it.s[rr][1][c] = reinterpret_cast<const uint16_t*>(R.us + (size_t)row * (H / 16))[j];
-    }
-  }
 }
 
 template <int NCH>
@@ -208,7 +104,6 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   const int H = a.H, E = a.E, K = a.K, I = a.I, SI = a.SI;
   const bool has_sh = SI > 0;
   const int sh = has_sh ? 1 : 0;
-  const uint32_t epoch = *ws.epoch + 1u;
   const bool norm = (a.flags & FLINT_PRE_RMSNORM) != 0;
   const int hstride = (I > SI ? I : SI) / 2;
   const size_t lstride = E, hrep = (size_t)(FLINT_MAX_TOP_K + 1) * hstride;
@@ -237,6 +132,9 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   XChunk<FMT_NVFP4> xc[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) xc[c] = input_chunk(a, lane + 64 * c, norm, rms);
+  // the launch epoch: a vector load, so that waiting for it holds up neither
+  // the kernel arguments nor the loads above
+  const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
 
   // ---- phase 1: router quarter rows + shared expert gate/up ------------------
   // expert e is owned by workgroup e % G; its 4 waves take a quarter each
@@ -273,6 +171,7 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
     }
     __syncthreads();
   }
+  announce_arrival(ws, E, epoch);
   if (my_sh) put_word_all(hw_all, hrep, sh_first, epoch, gu_finish<NCH>(shit, Rsh, xc));
   if (sh_stride == 1)
     for (int it = gw + NWV; it < nsh_items; it += NWV) {   // shared experts wider than the grid
@@ -284,16 +183,17 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   if (wave == 0) {
     uint64_t key[4];
     {
-      uint64_t wd[4];
-      const uint64_t* ptr[4];
-      bool ok[4];
+      uint64_t wd[8];
+      const uint64_t* ptr[8];
+      bool ok[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int ex = lane + 64 * q;
         ok[q] = ex < E;
         ptr[q] = lw + (ex < E ? ex : 0);
       }
-      poll_words<4>(wd, ptr, ok, epoch, ws.error);
+      arrival_slots(ws, E, G, ptr + 4, ok + 4);   // workgroup 0 only
+      poll_words<8>(wd, ptr, ok, epoch, ws.error);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int ex = lane + 64 * q;
@@ -351,8 +251,8 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   const bool hasA = gw < nitems, hasB = itB < nitems;
   const int rA = hasA ? gw / ipw : 0, pA = hasA ? gw - rA * ipw : 0;
   const int rB = hasB ? itB / ipw : 0, pB = hasB ? itB - rB * ipw : 0;
-  const GURows RA = gu_rows(a, s_exp[sh + rA]);
-  const GURows RB = gu_rows(a, s_exp[sh + rB]);
+  const GURows RA = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rA]));
+  const GURows RB = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rB]));
   if (hasA) gu_load<NCH>(A, RA, pA, H);
   if (hasB) gu_load<NCH>(B, RB, pB, H);
 
@@ -370,7 +270,7 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   for (int u = 0; u < MAXI; ++u) {
     const int it = wave + 4 * u;
     const int s = it < total ? it / dch : 0, c = it - s * dch;
-    const int e = s_exp[s < S ? s : 0];
+    const int e = __builtin_amdgcn_readfirstlane(s_exp[s < S ? s : 0]);
     const int inter = e < 0 ? SI : I;
     const int j = li + GD * c;
     const bool ok = it < total && j < inter / 32;
@@ -397,11 +297,11 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
     GUItem<NCH> C, D;
     const int itD = it0 + NWV;
     const int rC = it0 / ipw, pC = it0 - rC * ipw;
-    const GURows RC = gu_rows(a, s_exp[sh + rC]);
+    const GURows RC = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rC]));
     gu_load<NCH>(C, RC, pC, H);
     const bool hasD = itD < nitems;
     const int rD = hasD ? itD / ipw : rC, pD = hasD ? itD - rD * ipw : pC;
-    const GURows RD = gu_rows(a, s_exp[sh + rD]);
+    const GURows RD = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rD]));
     if (hasD) gu_load<NCH>(D, RD, pD, H);
     put_word_all(hw_all, hrep, (size_t)(sh + rC) * hstride + pC, epoch, gu_finish<NCH>(C, RC, xc));
     if (hasD)
@@ -447,7 +347,7 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
     const int it = wave + 4 * u;
     if (it >= total) break;
     const int s = it / dch, c = it - s * dch;
-    const int e = s_exp[s];
+    const int e = __builtin_amdgcn_readfirstlane(s_exp[s]);
     const int inter = e < 0 ? SI : I;
     const int j = li + GD * c;
     if (j >= inter / 32) continue;
@@ -475,27 +375,14 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   }
 
   // ---- advance the epoch for the next launch -----------------------------------
-  // The grid is no wider than E, so every workgroup published at least one
-  // router logit, tagged with the epoch it read at its start, and workgroup 0
-  // has seen all of them before its top-k: no workgroup of this launch can
-  // still be about to read the old value.  No ticket round trip is needed.
+  // Every workgroup published a router logit or an arrival word tagged with
+  // the epoch it read at its start, and workgroup 0 has seen all of them
+  // before its top-k: no workgroup of this launch can still be about to read
+  // the old value.  No ticket round trip is needed.
   if (blockIdx.x == 0 && threadIdx.x == 0) *ws.epoch = epoch;
 }
 
-int g_num_cu = 0;
-
 struct FusedConfig { int G, gd, dw, nch; };
-
-int num_cu() {
-  if (g_num_cu == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    g_num_cu = n;
-  }
-  return g_num_cu;
-}
 
 // Grid and tiling of the fused path for this shape; false when the shape is
 // outside what the kernel holds (the three-kernel path then runs instead).
@@ -504,10 +391,10 @@ bool fused_config(const LayerArgs& a, FusedConfig& c) {
   if (a.H % 2048 || a.H > 4096) return false;
   if (a.I > 2048 || a.SI > 2048 || a.K > FLINT_MAX_TOP_K) return false;
   c.nch = a.H / 2048;
-  c.G = num_cu();
+  c.G = device_num_cu();
   const int need = (a.H + 7) / 8;             // at most 8 output rows per workgroup
   if (c.G > need) c.G = need;
-  if (c.G > a.E) c.G = a.E;                   // every workgroup owns a router row
+  if (c.G > a.E + kMaxArrivals) c.G = a.E + kMaxArrivals;
   const int rows_per_wg = (a.H + c.G - 1) / c.G;
   const int red = a.SI > 0 && a.SI < a.I ? a.SI : a.I;
   c.gd = 8;

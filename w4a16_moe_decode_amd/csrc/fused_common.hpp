@@ -1,0 +1,149 @@
+// Pieces shared by the single-launch decode kernels (fused.hip: one token,
+// fused_bn.hip: 2..8 tokens): the epoch-tagged hand-off words, the gate/up
+// row pairs of a selected expert and their loads, and the CU count.
+#pragma once
+#include "common.hpp"
+
+namespace flint {
+namespace {
+
+constexpr uint32_t kFusedSpin = 1u << 20;
+
+__device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch, uint32_t* err) {
+  uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t spin = 0; (uint32_t)(w >> 32) != epoch && spin < kFusedSpin; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
+    w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if ((uint32_t)(w >> 32) != epoch) *err = 1u;
+  return w;
+}
+
+// Batched wait: all U words are loaded at once, then only the ones that do
+// not carry the epoch yet are loaded again.  Entries with ok[u] false are
+// skipped.
+template <int U>
+__device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* const (&p)[U],
+                                           const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    w[u] = ok[u] ? __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : ((uint64_t)epoch << 32);
+  for (uint32_t spin = 0; spin < kFusedSpin; ++spin) {
+    bool ready = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) ready = ready && (uint32_t)(w[u] >> 32) == epoch;
+    if (ready) return;
+    __builtin_amdgcn_s_sleep(8);     // back off: every workgroup is polling
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if ((uint32_t)(w[u] >> 32) != epoch)
+        w[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  *err = 1u;
+}
+
+__device__ __forceinline__ void put_word(uint64_t* p, uint32_t epoch, uint32_t payload) {
+  __hip_atomic_store(p, ((uint64_t)epoch << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Hand-off words are published in kReplicas copies (lanes 0..kReplicas-1 of
+// the writing wave each store one); workgroup g reads copy g % kReplicas.
+// Every workgroup needs every word: one copy per XCD keeps the readers of a
+// line to the workgroups of one XCD without multiplying the stores much.
+constexpr int kReplicas = 8;
+
+__device__ __forceinline__ void put_word_all(uint64_t* base, size_t stride, size_t idx, uint32_t epoch,
+                                             uint32_t payload) {
+  const int lane = threadIdx.x & 63;
+  if (lane < kReplicas) put_word(base + (size_t)lane * stride + idx, epoch, payload);
+}
+
+struct GURows {            // gate and up rows of one selected expert
+  const uint8_t* gc; const uint8_t* gs;
+  const uint8_t* uc; const uint8_t* us;
+  float g_scale, u_scale;
+  int inter;
+};
+
+__device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert /* -1 = shared */) {
+  GURows r;
+  const int H = a.H;
+  if (expert < 0) {
+    r.inter = a.SI;
+    const size_t mc = (size_t)a.SI * H / 2, ms = (size_t)a.SI * H / 16;
+    r.gc = a.sh_gu_codes; r.uc = a.sh_gu_codes + mc;
+    r.gs = a.sh_gu_scales; r.us = a.sh_gu_scales + ms;
+    r.g_scale = a.sh_gscale[0]; r.u_scale = a.sh_gscale[1];
+  } else {
+    r.inter = a.I;
+    const size_t mc = (size_t)a.I * H / 2, ms = (size_t)a.I * H / 16;
+    r.gc = a.gu_codes + (size_t)(2 * expert) * mc; r.uc = r.gc + mc;
+    r.gs = a.gu_scales + (size_t)(2 * expert) * ms; r.us = r.gs + ms;
+    r.g_scale = a.gscale[3 * expert]; r.u_scale = a.gscale[3 * expert + 1];
+  }
+  return r;
+}
+
+// One gate/up item: rows 2p and 2p+1 of a selected expert, a whole wave per
+// row (H/32 chunks of 32 columns per row, NCH per lane).  Returns the packed
+// BF16 pair h[2p], h[2p+1] (valid in every lane).
+template <int NCH>
+struct GUItem {
+  uint4 c[2][2][NCH];       // [row][gate|up][chunk]
+  uint32_t s[2][2][NCH];
+};
+
+template <int NCH>
+__device__ __forceinline__ void gu_load(GUItem<NCH>& it, const GURows& R, int p, int H) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = 2 * p + rr;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int j = lane + 64 * c;
+      it.c[rr][0][c] = reinterpret_cast<const uint4*>(R.gc + (size_t)row * (H / 2))[j];
+      it.s[rr][0][c] = reinterpret_cast<const uint16_t*>(R.gs + (size_t)row * (H / 16))[j];
+      it.c[rr][1][c] = reinterpret_cast<const uint4*>(R.uc + (size_t)row * (H / 2))[j];
+      it.s[rr][1][c] = reinterpret_cast<const uint16_t*>(R.us + (size_t)row * (H / 16))[j];
+    }
+  }
+}
+
+// Workgroups that own no router row (a grid wider than E) announce with a
+// word of their own that they have read the launch epoch; workgroup 0 waits
+// for these words (with the logits) before it may advance the epoch at its
+// end.  They sit after the logit words of 8 tokens x kReplicas copies.
+constexpr int kMaxArrivals = 256;               // grid width - E is capped to this
+__device__ __forceinline__ uint64_t* arrival_words(const DecodeWs& ws, int E) {
+  return ws.logit_words + (size_t)FLINT_MAX_DECODE_BATCH * kReplicas * E;
+}
+__device__ __forceinline__ void announce_arrival(const DecodeWs& ws, int E, uint32_t epoch) {
+  if ((int)blockIdx.x >= E && threadIdx.x == 0) put_word(arrival_words(ws, E) + (blockIdx.x - E), epoch, 0u);
+}
+// the four arrival words lane `lane` polls in workgroup 0 (none elsewhere)
+__device__ __forceinline__ void arrival_slots(const DecodeWs& ws, int E, int G, const uint64_t** p, bool* ok) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = lane + 64 * q;
+    ok[q] = blockIdx.x == 0 && b < G - E;
+    p[q] = arrival_words(ws, E) + (ok[q] ? b : 0);
+  }
+}
+
+inline int device_num_cu() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    n_cu = n;
+  }
+  return n_cu;
+}
+
+}  // namespace
+}  // namespace flint
