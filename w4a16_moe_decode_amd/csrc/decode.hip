@@ -16,7 +16,7 @@
 // routing and the combine fused into the neighbouring GEMV kernels on the
 // path for up to 8 requests).  Each selected expert's weights are read once
 // per call and applied to every token routed to it.
-#include "common.hpp"
+#include "fused_common.hpp"
 
 namespace flint {
 namespace {
@@ -31,14 +31,14 @@ constexpr int kMaxB = FLINT_MAX_DECODE_BATCH;
 //
 // Hand-off without a cache-flushing fence: every logit is published as one
 // 64-bit atomic word (call epoch << 32 | logit bits).  The workgroup that
-// takes the last ticket polls each word until it carries this call's epoch
-// (data and "ready" flag are the same word, so no store ordering is relied
-// on), then selects the top-k of every token and writes the expert set.
+// takes the last ticket polls the words, all of a wave's two tokens at once,
+// until they carry this call's epoch (data and "ready" flag are the same
+// word, so no store ordering is relied on), then selects the top-k of every
+// token and writes the expert set.
 // It finally advances the epoch and returns the ticket to zero; both are
 // read again only by the next launch.  The poll is bounded: if a word never
 // arrives (it cannot, short of a hardware fault) the kernel records an
 // error word in the workspace and still exits.
-constexpr uint32_t kSpinLimit = 1u << 22;
 
 template <int BT, int NIT, bool NORM>
 __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
@@ -146,43 +146,47 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
   }
   __syncthreads();
   const bool renorm = (a.flags & FLINT_RENORM) != 0;
-  for (int t = wave; t < B; t += 4) {
-    uint64_t key[4];
+  {
+    // tokens wave and wave + 4: all their logit words polled at once
+    uint64_t wd[8];
+    const uint64_t* ptr[8];
+    bool ok[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ex = lane + 64 * j;
-      key[j] = 0ull;
-      if (ex < E) {
-        uint64_t wd = 0;
-        for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
-          wd = __hip_atomic_load(ws.logit_words + t * E + ex, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((uint32_t)(wd >> 32) == epoch) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if ((uint32_t)(wd >> 32) != epoch) *ws.error = 1u;
-        key[j] = ((uint64_t)float_order_key(__uint_as_float((uint32_t)wd)) << 32) | (uint32_t)~(uint32_t)ex;
+    for (int h = 0; h < 2; ++h) {
+      const int t = wave + 4 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ex = lane + 64 * q;
+        ok[4 * h + q] = t < B && ex < E;
+        ptr[4 * h + q] = ws.logit_words + (size_t)(t < B ? t : 0) * E + (ex < E ? ex : 0);
       }
     }
-    float my_s = 0.f, ssum = 0.f;
-    int my_e = 0;
-    for (int k = 0; k < a.K; ++k) {
-      uint64_t m = key[0];
+    poll_words<8>(wd, ptr, ok, epoch, ws.error);
 #pragma unroll
-      for (int j = 1; j < 4; ++j) m = key[j] > m ? key[j] : m;
-      m = wave_max_key(m);
+    for (int h = 0; h < 2; ++h) {
+      const int t = wave + 4 * h;
+      if (t >= B) break;                            // the same in every lane
+      uint64_t key[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (key[j] == m) key[j] = 0ull;
-      const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
-      ssum += sg;
-      if (lane == k) { my_s = sg; my_e = (int)~(uint32_t)m; }
-    }
-    if (lane < a.K) {
-      const float w = renorm ? my_s / ssum : my_s;
-      a.topk_idx[t * a.K + lane] = my_e;
-      a.topk_w[t * a.K + lane] = w;
-      atomicOr(&s_mask[my_e], 1u << t);
-      s_w[my_e][t] = w;
+      for (int q = 0; q < 4; ++q) {
+        const int ex = lane + 64 * q;
+        key[q] = ok[4 * h + q] ? (((uint64_t)float_order_key(__uint_as_float((uint32_t)wd[4 * h + q])) << 32) |
+                                  (uint32_t)~(uint32_t)ex)
+                               : 0ull;
+      }
+      const uint64_t my_key = select_topk(key, a.K);
+      const int my_e = (int)~(uint32_t)my_key;
+      const float my_s = lane < a.K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
+      float ssum = 0.f;
+      for (int k = 0; k < a.K; ++k)                 // selection order
+        ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+      if (lane < a.K) {
+        const float w = renorm ? my_s / ssum : my_s;
+        a.topk_idx[t * a.K + lane] = my_e;
+        a.topk_w[t * a.K + lane] = w;
+        atomicOr(&s_mask[my_e], 1u << t);
+        s_w[my_e][t] = w;
+      }
     }
   }
   __syncthreads();

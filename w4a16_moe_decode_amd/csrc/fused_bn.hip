@@ -113,23 +113,6 @@ __device__ __forceinline__ void gu_tokens(const GUItem<NCH>& it, float gsg_in, f
     put_word(hw_all + (size_t)(lane & (kReplicas - 1)) * hrep + (size_t)mypair * hstride + p, epoch, myword);
 }
 
-// top-k of one token from its four logit words per lane: lane k < K returns
-// the k-th selected key (descending logit, ties to the lower index)
-__device__ __forceinline__ uint64_t select_topk(uint64_t (&key)[4], int K) {
-  const int lane = threadIdx.x & 63;
-#define FLINT_CSWAP(i, j) { const uint64_t hi_ = key[i] > key[j] ? key[i] : key[j]; \
-                            const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
-  FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
-#undef FLINT_CSWAP
-  uint64_t mine = 0ull;
-  for (int k = 0; k < K; ++k) {
-    const uint64_t m = wave_max_key(key[0]);
-    if (key[0] == m) { key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull; }
-    if (lane == k) mine = m;
-  }
-  return mine;
-}
-
 struct DItem { uint4 raw[2]; uint32_t sc[2]; float gd; };
 
 template <int NCH, int GD, int DW>
