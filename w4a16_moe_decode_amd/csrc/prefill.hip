@@ -70,15 +70,23 @@ __device__ __forceinline__ void load_b_nv(BRegsNv& r, const uint8_t* codes_row, 
 }
 __device__ __forceinline__ void store_b_nv(const BRegsNv& r, uint16_t* lds) {
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const DChunk<FMT_NVFP4> d = decode_nvfp4(r.c, r.s);
+  // two codes -> two exact fp32 values, times the UE4M3 scale of their 16
+  // columns (exact: at most 6 significant bits), packed to BF16 with round to
+  // nearest even (exact as well)
+  const float s0 = e4m3_to_f32<0>(r.s), s1 = e4m3_to_f32<1>(r.s);
+  const uint32_t q[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
   uint32_t o[16];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const float s = m < 8 ? d.s0 : d.s1;
-    // the product is exact in BF16, so taking the top 16 bits loses nothing
-    const uint32_t lo = __float_as_uint((float)d.w[m].x * s) >> 16;
-    const uint32_t hi = __float_as_uint((float)d.w[m].y * s) & 0xffff0000u;
-    o[m] = lo | hi;
+  for (int i = 0; i < 4; ++i) {
+    const float s = i < 2 ? s0 : s1;               // columns 0..15, then 16..31
+    const f32x2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 0);
+    const f32x2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 1);
+    const f32x2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 2);
+    const f32x2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[i], 1.0f, 3);
+    o[4 * i + 0] = pack_bf16x2_rne(f0.x * s, f0.y * s);
+    o[4 * i + 1] = pack_bf16x2_rne(f1.x * s, f1.y * s);
+    o[4 * i + 2] = pack_bf16x2_rne(f2.x * s, f2.y * s);
+    o[4 * i + 3] = pack_bf16x2_rne(f3.x * s, f3.y * s);
   }
   uint4* dst = reinterpret_cast<uint4*>(lds + row * LDS_STRIDE + half * 32);
   dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -136,6 +144,67 @@ __device__ __forceinline__ int acc_row(int i, int e) {
 __device__ __forceinline__ int acc_col(int j) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   return 64 * (wave & 1) + 32 * j + (lane & 31);
+}
+
+// ------------------------------------------------------------- K loop ---
+// Software pipeline: a ring of kStages register sets, the loads of step
+// kt + kStages issued at step kt, so a load has kStages - 1 MFMA steps to
+// arrive; LDS is double-buffered (the tile of step kt + 1 is stored while
+// step kt is multiplied).  Every load is unconditional (rows and steps past
+// the end are clamped to valid ones), so each store waits for its own set.
+constexpr int kStages = 4;
+
+// Register ring of one GEMM's operands: A rows of BF16, B rows of NVFP4
+// (WF = FMT_NVFP4) or of BF16.
+template <int WF>
+struct TileRing {
+  Rows arow, bbf;
+  const uint8_t* bcodes;
+  const uint8_t* bscales;
+  ARegs ra[kStages];
+  ARegs rbb[kStages];
+  BRegsNv rbn[kStages];
+  template <int S>
+  __device__ __forceinline__ void load(int k0) {
+    load_a(ra[S], arow, k0);
+    if constexpr (WF == FMT_NVFP4) load_b_nv(rbn[S], bcodes, bscales, k0);
+    else load_b_bf(rbb[S], bbf, k0);
+  }
+  template <int S>
+  __device__ __forceinline__ void store(uint16_t* la, uint16_t* lb) {
+    store_a(ra[S], la);
+    if constexpr (WF == FMT_NVFP4) store_b_nv(rbn[S], lb);
+    else store_a(rbb[S], lb);
+  }
+};
+
+template <int U, int WF>
+__device__ __forceinline__ void k_step(Acc& acc, uint16_t (&la)[2][BM * LDS_STRIDE],
+                                       uint16_t (&lb)[2][BN * LDS_STRIDE], TileRing<WF>& ring, int kt,
+                                       int nk) {
+  if (kt < nk) mfma_tile(acc, la[U & 1], lb[U & 1]);            // same in every lane
+  ring.template store<(U + 1) % kStages>(la[(U + 1) & 1], lb[(U + 1) & 1]);
+  const int kl = kt + kStages < nk ? kt + kStages : nk - 1;
+  ring.template load<U>(kl * BK);
+  __syncthreads();
+}
+
+template <int WF>
+__device__ __forceinline__ void gemm_k_loop(Acc& acc, uint16_t (&la)[2][BM * LDS_STRIDE],
+                                            uint16_t (&lb)[2][BN * LDS_STRIDE], TileRing<WF>& ring, int nk) {
+  static_assert(kStages == 4, "the ring is unrolled for four stages");
+  ring.template load<0>(0);
+  ring.template load<1>((1 < nk ? 1 : nk - 1) * BK);
+  ring.template load<2>((2 < nk ? 2 : nk - 1) * BK);
+  ring.template load<3>((3 < nk ? 3 : nk - 1) * BK);
+  ring.template store<0>(la[0], lb[0]);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
+    k_step<0>(acc, la, lb, ring, kt0 + 0, nk);
+    k_step<1>(acc, la, lb, ring, kt0 + 1, nk);
+    k_step<2>(acc, la, lb, ring, kt0 + 2, nk);
+    k_step<3>(acc, la, lb, ring, kt0 + 3, nk);
+  }
 }
 
 // ---------------------------------------------------------- workspaces ----
@@ -229,36 +298,18 @@ __global__ __launch_bounds__(256) void prefill_router_kernel(LayerArgs a, Prefil
   const int H = a.H, E = a.E;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const int t = threadIdx.x;
-  Rows arow, brow;
+  TileRing<FMT_BF16> ring;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = p * 32 + (t >> 3);
     const int tok = m0 + r < T ? m0 + r : T - 1;
-    arow.p[p] = xin + (size_t)tok * H;
+    ring.arow.p[p] = xin + (size_t)tok * H;
     const int e = n0 + r < E ? n0 + r : E - 1;
-    brow.p[p] = a.router + (size_t)e * H;
+    ring.bbf.p[p] = a.router + (size_t)e * H;
   }
   Acc acc;
   acc_zero(acc);
-  ARegs ra, rb;
-  load_a(ra, arow, 0);
-  load_b_bf(rb, brow, 0);
-  store_a(ra, la[0]);
-  store_a(rb, lb[0]);
-  __syncthreads();
-  const int nk = H / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // the next stage's tile (the last iteration re-reads its own stage and
-    // stores it into the idle buffer, which nothing reads afterwards)
-    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
-    load_a(ra, arow, kn);
-    load_b_bf(rb, brow, kn);
-    mfma_tile(acc, la[cur], lb[cur]);
-    store_a(ra, la[cur ^ 1]);
-    store_a(rb, lb[cur ^ 1]);
-    __syncthreads();
-  }
+  gemm_k_loop(acc, la, lb, ring, H / BK);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -449,28 +500,27 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(LayerArgs a, Prefi
   const int imax = a.I > a.SI ? a.I : a.SI;
   const int t = threadIdx.x;
 
-  Rows arow;
+  TileRing<WF> ring;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = m0 + p * 32 + (t >> 3);
     const int rr = r < cnt ? r : cnt - 1;
     const int tok = shared ? rr : ws.perm_tok[base + rr];
-    arow.p[p] = xin + (size_t)tok * H;
+    ring.arow.p[p] = xin + (size_t)tok * H;
   }
   // this thread's B row: tile row t/2 (NVFP4: two threads per row)
   const int brow_t = t >> 1;
   const int bi = i0 + (brow_t >> 1), bup = brow_t & 1;
   const int bic = bi < inter ? bi : inter - 1;
-  const uint8_t* bcodes = nullptr;
-  const uint8_t* bscales = nullptr;
-  Rows bbf;
+  ring.bcodes = nullptr;
+  ring.bscales = nullptr;
   float gs_g = 1.f, gs_u = 1.f;
   if constexpr (WF == FMT_NVFP4) {
     const size_t mc = (size_t)inter * H / 2, ms = (size_t)inter * H / 16;
     const uint8_t* c0 = shared ? a.sh_gu_codes : a.gu_codes + (size_t)(2 * g) * mc;
     const uint8_t* s0 = shared ? a.sh_gu_scales : a.gu_scales + (size_t)(2 * g) * ms;
-    bcodes = c0 + bup * mc + (size_t)bic * (H / 2);
-    bscales = s0 + bup * ms + (size_t)bic * (H / 16);
+    ring.bcodes = c0 + bup * mc + (size_t)bic * (H / 2);
+    ring.bscales = s0 + bup * ms + (size_t)bic * (H / 16);
     const float* gsp = shared ? a.sh_gscale : a.gscale + 3 * g;
     gs_g = gsp[0];
     gs_u = gsp[1];
@@ -482,55 +532,38 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(LayerArgs a, Prefi
       const int r = p * 32 + (t >> 3);           // tile row of this thread's 16-B segment
       const int ii = i0 + (r >> 1);
       const int iic = ii < inter ? ii : inter - 1;
-      bbf.p[p] = w0 + (r & 1) * mb + (size_t)iic * H;
+      ring.bbf.p[p] = w0 + (r & 1) * mb + (size_t)iic * H;
     }
   }
 
   Acc acc;
   acc_zero(acc);
-  ARegs ra, rbb;
-  BRegsNv rbn;
-  load_a(ra, arow, 0);
-  if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, 0);
-  else load_b_bf(rbb, bbf, 0);
-  store_a(ra, la[0]);
-  if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[0]);
-  else store_a(rbb, lb[0]);
-  __syncthreads();
-  const int nk = H / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
-    load_a(ra, arow, kn);
-    if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, kn);
-    else load_b_bf(rbb, bbf, kn);
-    mfma_tile(acc, la[cur], lb[cur]);
-    store_a(ra, la[cur ^ 1]);
-    if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[cur ^ 1]);
-    else store_a(rbb, lb[cur ^ 1]);
-    __syncthreads();
-  }
+  gemm_k_loop(acc, la, lb, ring, H / BK);
+  // Even columns hold gate rows, odd columns the matching up rows, in
+  // neighbouring lanes.  The lanes of a pair swap half of their results, so
+  // that the even lane finishes the elements of block row 0 and the odd lane
+  // those of block row 1: every lane does useful epilogue work.
   const int lane = threadIdx.x & 63;
   const bool even = (lane & 1) == 0;
+  const int ih = even ? 0 : 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float mine = acc.c[i][j][e];
-        const float other = dpp_f<0xB1>(mine);       // partner lane ^ 1
-        const int r = m0 + acc_row(i, e);
-        const int col = acc_col(j);
-        const int ii = i0 + (col >> 1);
-        if (even && r < cnt && ii < inter) {
-          const float gv = round_bf16(mine * gs_g);
-          const float uv = round_bf16(other * gs_u);
-          const float av = round_bf16(silu_f32(gv));
-          const size_t row = shared ? (size_t)T * K + r : (size_t)base + r;
-          ws.h[row * imax + ii] = f32_to_bf16_bits(av * uv);
-        }
+    for (int e = 0; e < 16; ++e) {
+      const float a0 = acc.c[0][j][e], a1 = acc.c[1][j][e];
+      const float recv = dpp_f<0xB1>(even ? a1 : a0);   // partner lane ^ 1
+      const float gacc = even ? a0 : recv;
+      const float uacc = even ? recv : a1;
+      const int r = m0 + acc_row(ih, e);
+      const int ii = i0 + (acc_col(j) >> 1);
+      if (r < cnt && ii < inter) {
+        const float gv = round_bf16(gacc * gs_g);
+        const float uv = round_bf16(uacc * gs_u);
+        const float av = round_bf16(silu_f32(gv));
+        const size_t row = shared ? (size_t)T * K + r : (size_t)base + r;
+        ws.h[row * imax + ii] = f32_to_bf16_bits(av * uv);
       }
+    }
 }
 
 // ------------------------------------------------------------------ down --
@@ -551,57 +584,35 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(LayerArgs a, PrefillW
   const int imax = a.I > a.SI ? a.I : a.SI;
   const int t = threadIdx.x;
 
-  Rows arow;
+  TileRing<WF> ring;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = m0 + p * 32 + (t >> 3);
     const int rr = r < cnt ? r : cnt - 1;
-    arow.p[p] = ws.h + (base + rr) * imax;
+    ring.arow.p[p] = ws.h + (base + rr) * imax;
   }
   const int bn = n0 + (t >> 1);
   const int bnc = bn < H ? bn : H - 1;
-  const uint8_t* bcodes = nullptr;
-  const uint8_t* bscales = nullptr;
-  Rows bbf;
+  ring.bcodes = nullptr;
+  ring.bscales = nullptr;
   float gd = 1.f;
   if constexpr (WF == FMT_NVFP4) {
     const uint8_t* c0 = shared ? a.sh_d_codes : a.d_codes + (size_t)g * H * (inter / 2);
     const uint8_t* s0 = shared ? a.sh_d_scales : a.d_scales + (size_t)g * H * (inter / 16);
-    bcodes = c0 + (size_t)bnc * (inter / 2);
-    bscales = s0 + (size_t)bnc * (inter / 16);
+    ring.bcodes = c0 + (size_t)bnc * (inter / 2);
+    ring.bscales = s0 + (size_t)bnc * (inter / 16);
     gd = shared ? a.sh_gscale[2] : a.gscale[3 * g + 2];
   } else {
     const uint16_t* w0 = shared ? a.sh_d_bf16 : a.d_bf16 + (size_t)g * H * inter;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int r = n0 + p * 32 + (t >> 3);
-      bbf.p[p] = w0 + (size_t)(r < H ? r : H - 1) * inter;
+      ring.bbf.p[p] = w0 + (size_t)(r < H ? r : H - 1) * inter;
     }
   }
   Acc acc;
   acc_zero(acc);
-  ARegs ra, rbb;
-  BRegsNv rbn;
-  load_a(ra, arow, 0);
-  if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, 0);
-  else load_b_bf(rbb, bbf, 0);
-  store_a(ra, la[0]);
-  if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[0]);
-  else store_a(rbb, lb[0]);
-  __syncthreads();
-  const int nk = inter / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
-    load_a(ra, arow, kn);
-    if constexpr (WF == FMT_NVFP4) load_b_nv(rbn, bcodes, bscales, kn);
-    else load_b_bf(rbb, bbf, kn);
-    mfma_tile(acc, la[cur], lb[cur]);
-    store_a(ra, la[cur ^ 1]);
-    if constexpr (WF == FMT_NVFP4) store_b_nv(rbn, lb[cur ^ 1]);
-    else store_a(rbb, lb[cur ^ 1]);
-    __syncthreads();
-  }
+  gemm_k_loop(acc, la, lb, ring, inter / BK);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
