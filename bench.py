@@ -204,7 +204,7 @@ def bench_step(args, dev, batch=1, n_moe=47, n_dense=2, reps=20):
         g.replay()
         x.copy_(x0)
         secs = timed(g) / reps
-        idx = step.topk_idx[:, :batch * shape.top_k].view(n_moe, batch * shape.top_k).cpu()
+        idx = torch.stack([step.routing(l, batch)[0].reshape(-1) for l in range(n_moe)]).cpu()
         distinct = [len(set(idx[l].tolist())) for l in range(n_moe)]
         mult = 2.0 / (0.5 + 1.0 / 16) if wbf16 else 1.0      # bf16 bytes per weight vs nvfp4
         nb = sum(mult * (d * (eb["gate_up"] + eb["down"]) + eb["sh_gate_up"] + eb["sh_down"])

@@ -253,6 +253,35 @@ FLINT_API int32_t flint_moe_decode_stage(int32_t stage, const flint_moe_shape* s
                                void* out, int32_t* topk_idx, float* topk_w, const void* gamma,
                                void* ws, int64_t ws_bytes, void* stream);
 
+/* A stack of MoE sublayers for one token in one launch (the decode step's
+ * MoE part: [AR] "Flint 是什么" -- 47 MoE layers; [D0] "Model architecture"
+ * and "Optimizations" -- pre-norm residual sublayers, the low-latency path
+ * with each kernel's weight loads overlapping the previous step).  With x_0
+ * = x, for l = 0 .. n_layers-1:
+ *   x_{l+1} = BF16(x_l + flint_moe_decode(layer l, x_l)) with PRE_RMSNORM
+ *             and RESIDUAL (gamma_l; rms_eps from the shape)
+ * and out = x_{n_layers}.  Each layer's result equals one flint_moe_decode
+ * call bit for bit; only the launches between layers are gone (the
+ * residual is handed from layer to layer in the workspace).
+ *   shape      as flint_moe_decode; flags: FLINT_RENORM only (PRE_RMSNORM
+ *              and RESIDUAL are implied); the batch-1 single-launch envelope
+ *              (NVFP4, hidden 2048 or 4096, I and SI <= 2048), else
+ *              FLINT_ERR_UNSUPPORTED
+ *   layers     (device) flint_moe_weights [n_layers], NVFP4 fields used
+ *   n_layers   1 .. FLINT_MAX_STACK_LAYERS
+ *   gammas     (device) BF16 [n_layers][H]
+ *   x, out     (device) BF16 [H]; out may equal x
+ *   topk_idx   (device) int32 [n_layers][K], topk_w float [n_layers][K]:
+ *              every layer's selection (required)
+ *   layer_out  (device) BF16 [n_layers][H] or NULL: x_{l+1} of every layer
+ *   ws         as flint_moe_decode (the same workspace size)
+ * One launch; a batch-1 flint_moe_decode may share the workspace. */
+#define FLINT_MAX_STACK_LAYERS 4096
+FLINT_API int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const flint_moe_weights* layers,
+                                         int32_t n_layers, const void* gammas, const void* x, void* out,
+                                         int32_t* topk_idx, float* topk_w, void* layer_out, void* ws,
+                                         int64_t ws_bytes, void* stream);
+
 /* Which kernels flint_moe_decode runs for this shape (flags included) and
  * batch: FLINT_PATH_SPLIT, FLINT_PATH_SINGLE_ONE or FLINT_PATH_SINGLE_BATCH.
  * Reads only the shape; enqueues nothing.  Returns -status for an invalid

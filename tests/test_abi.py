@@ -154,3 +154,31 @@ def test_decode_path_rules():
     with pytest.raises(fm.FlintError) as e:
         fm.flint_moe_decode_path(fm.FlintMoeShape(2048, 256, 512, 512, 0, 0, 1e-6), 1)
     assert e.value.status == fm.FLINT_ERR_INVALID_ARG
+
+
+def test_decode_stack_validation_codes():
+    """flint_moe_decode_stack rejects bad arguments before enqueuing anything
+    (fake device addresses: nothing is dereferenced on the host)."""
+    L = fm.lib()
+    v = ctypes.c_void_p
+    s = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
+    big = 1 << 40
+
+    def st(shape=s, layers=v(64), n=3, gam=v(128), x=v(256), out=v(256), idx=v(512), w=v(768),
+           lo=None, ws=None, ws_bytes=big):
+        return L.flint_moe_decode_stack(ctypes.byref(shape), layers, n, gam, x, out, idx, w, lo, ws,
+                                        ws_bytes, None)
+
+    assert st(n=0) == fm.FLINT_ERR_INVALID_ARG
+    assert st(n=5000) == fm.FLINT_ERR_UNSUPPORTED                          # > 4096 layers
+    assert st(layers=None) == fm.FLINT_ERR_INVALID_ARG
+    assert st(gam=v(130)) == fm.FLINT_ERR_ALIGNMENT
+    assert st(idx=None) == fm.FLINT_ERR_INVALID_ARG
+    assert st(w=v(770)) == fm.FLINT_ERR_ALIGNMENT
+    assert st(lo=v(8)) == fm.FLINT_ERR_ALIGNMENT
+    assert st() == fm.FLINT_ERR_WORKSPACE                                  # ws missing
+    assert st(ws=v(4096), ws_bytes=100) == fm.FLINT_ERR_WORKSPACE
+    for flags in (fm.FLINT_PRE_RMSNORM, fm.FLINT_RESIDUAL, fm.FLINT_W_BF16, fm.FLINT_SPLIT):
+        assert st(shape=fm.FlintMoeShape(2048, 256, 512, 512, 6, flags, 1e-6)) == fm.FLINT_ERR_UNSUPPORTED
+    # outside the one-token single-launch envelope (hidden 512)
+    assert st(shape=fm.FlintMoeShape(512, 32, 128, 128, 4, 0, 1e-6), ws=v(4096)) == fm.FLINT_ERR_UNSUPPORTED

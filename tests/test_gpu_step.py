@@ -42,9 +42,9 @@ def _build(n_moe, n_dense, seed, wbf16=False):
     return srcs, layers, gmo, dsrc, dl, gde
 
 
-def _check_step(n_moe, n_dense, batch, seed, wbf16=False, flags=0):
+def _check_step(n_moe, n_dense, batch, seed, wbf16=False, flags=0, stack=None):
     srcs, layers, gmo, dsrc, dl, gde = _build(n_moe, n_dense, seed, wbf16)
-    step = fm.DecodeStep(layers, gmo, dl, gde, SH.top_k, flags=flags, wbf16=wbf16)
+    step = fm.DecodeStep(layers, gmo, dl, gde, SH.top_k, flags=flags, wbf16=wbf16, stack=stack)
     x = gen.activations(gen.seed_for(seed, "x"), batch, SH.hidden, "cuda")
     rec = []
     step(x, record=rec)
@@ -56,8 +56,8 @@ def _check_step(n_moe, n_dense, batch, seed, wbf16=False, flags=0):
         ex = oracle_experts_lazy(srcs[l])
         g = gen.numpy_f64(gmo[l])
         _, r = moe.moe_sublayer(xin, g, ex, SH.top_k, renorm)
-        idx = step.topk_idx[l, :batch * SH.top_k].view(batch, SH.top_k).cpu().numpy()
-        wts = step.topk_w[l, :batch * SH.top_k].view(batch, SH.top_k).cpu().numpy()
+        idx_t, w_t = step.routing(l, batch)
+        idx, wts = idx_t.cpu().numpy(), w_t.cpu().numpy()
         forced = check_routing(idx, wts, r, renorm)
         want, _ = moe.moe_sublayer(xin, g, ex, SH.top_k, renorm, forced_idx=forced)
         compare_residual(gen.numpy_f64(rec[l + 1]), want, xin, f"moe layer {l}")
@@ -73,6 +73,11 @@ def _check_step(n_moe, n_dense, batch, seed, wbf16=False, flags=0):
 
 def test_full_decode_step_batch1():
     _check_step(47, 2, 1, seed=1)
+
+
+def test_decode_step_batch1_one_call_per_layer():
+    """The batch-1 step without the layer stack (one decode call per layer)."""
+    _check_step(4, 1, 1, seed=6, stack=False)
 
 
 def test_decode_step_batch8_renorm():

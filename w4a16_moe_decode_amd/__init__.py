@@ -54,8 +54,8 @@ MAX_DECODE_BATCH = 8
 EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
-    "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_prefill",
-    "flint_dense_gemv",
+    "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
+    "flint_moe_prefill", "flint_dense_gemv",
 )
 
 
@@ -109,6 +109,9 @@ def lib() -> ctypes.CDLL:
         L.flint_moe_decode_stage.restype = i32
         L.flint_moe_decode_stage.argtypes = [i32] + dec
         L.flint_moe_decode_path.restype = i32
+        L.flint_moe_decode_stack.restype = i32
+        L.flint_moe_decode_stack.argtypes = [ctypes.POINTER(FlintMoeShape), vp, i32, vp, vp, vp, vp, vp, vp,
+                                             vp, i64, vp]
         L.flint_moe_decode_path.argtypes = [ctypes.POINTER(FlintMoeShape), i32]
         L.flint_moe_prefill.restype = i32
         L.flint_moe_prefill.argtypes = dec
@@ -196,6 +199,24 @@ def flint_moe_decode_path(shape: FlintMoeShape, batch: int) -> int:
     if v < 0:
         raise FlintError("flint_moe_decode_path", -v)
     return v
+
+
+def flint_moe_decode_stack(shape, layers_dev, n_layers, gammas, x, out, topk_idx, topk_w, layer_out, ws,
+                           ws_bytes, stream=None):
+    """``layers_dev``: a device uint8 tensor holding ``n_layers``
+    FlintMoeWeights structs (see ``weights_table``)."""
+    _check("flint_moe_decode_stack",
+           lib().flint_moe_decode_stack(ctypes.byref(shape), _p(layers_dev), int(n_layers), _p(gammas), _p(x),
+                                        _p(out), _p(topk_idx), _p(topk_w), _p(layer_out), _p(ws),
+                                        int(ws_bytes), _stream(stream)))
+
+
+def weights_table(layers, device) -> torch.Tensor:
+    """The FlintMoeWeights structs of ``layers`` (PackedMoeLayer) as a device
+    byte tensor, the layout flint_moe_decode_stack reads."""
+    arr = (FlintMoeWeights * len(layers))(*[L.weights() for L in layers])
+    host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return host.to(device)
 
 
 def flint_moe_prefill(shape, weights, x, n_tokens, out, topk_idx, topk_w, gamma, ws, ws_bytes,
@@ -419,17 +440,21 @@ def pack_dense_mlp(gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor, gsc
 
 class DecodeStep:
     """One decode step over a stack of pre-norm residual sublayers: the MoE
-    sublayers (flint_moe_decode with PRE_RMSNORM | RESIDUAL, updating the
-    residual in place), then the dense SwiGLU sublayers (flint_dense_gemv:
-    gate/up with the fused RMSNorm, then down with the residual epilogue).
+    sublayers, then the dense SwiGLU sublayers (flint_dense_gemv: gate/up
+    with the fused RMSNorm, then down with the residual epilogue).  At batch
+    1 the MoE sublayers run as one flint_moe_decode_stack launch when the
+    shape allows it (``stack``, default: whenever it does); otherwise one
+    flint_moe_decode call each (PRE_RMSNORM | RESIDUAL, residual in place).
     Every call enqueues kernels only, so a step can be captured in a graph."""
 
     def __init__(self, moe_layers, moe_gammas, dense_layers, dense_gammas, top_k: int,
-                 flags: int = 0, wbf16: bool = False, rms_eps: float = 1e-6, max_batch: int = 8):
+                 flags: int = 0, wbf16: bool = False, rms_eps: float = 1e-6, max_batch: int = 8,
+                 stack: Optional[bool] = None):
         self.moe_layers, self.moe_gammas = moe_layers, moe_gammas
         self.dense_layers, self.dense_gammas = dense_layers, dense_gammas
         self.wbf16 = wbf16
         self.eps = rms_eps
+        self.top_k = top_k
         f = flags | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | (FLINT_W_BF16 if wbf16 else 0)
         self.shapes = [L.shape(top_k, f, rms_eps) for L in moe_layers]
         self.cweights = [L.weights() for L in moe_layers]
@@ -439,20 +464,53 @@ class DecodeStep:
         self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev)
         self.h = [torch.empty((max_batch, d.inter), dtype=torch.bfloat16, device=dev)
                   for d in dense_layers]
-        K = top_k
-        self.topk_idx = torch.zeros((len(moe_layers), max_batch * K), dtype=torch.int32, device=dev)
-        self.topk_w = torch.zeros((len(moe_layers), max_batch * K), dtype=torch.float32, device=dev)
+        K, n = top_k, len(moe_layers)
+        self.topk_idx = torch.zeros((n, max_batch * K), dtype=torch.int32, device=dev)
+        self.topk_w = torch.zeros((n, max_batch * K), dtype=torch.float32, device=dev)
+        self.stack_shape = None
+        if moe_layers and not wbf16:
+            sshape = moe_layers[0].shape(top_k, flags & FLINT_RENORM, rms_eps)
+            ok = flint_moe_decode_path(moe_layers[0].shape(top_k, flags & FLINT_RENORM, rms_eps), 1) \
+                == FLINT_PATH_SINGLE_ONE
+            if (ok if stack is None else stack) and ok:
+                self.stack_shape = sshape
+                self.table = weights_table(moe_layers, dev)
+                self.gstack = torch.stack([g.reshape(-1) for g in moe_gammas]).contiguous()
+                self.stack_idx = torch.zeros((n, K), dtype=torch.int32, device=dev)
+                self.stack_w = torch.zeros((n, K), dtype=torch.float32, device=dev)
+                self.layer_out = torch.empty((n, moe_layers[0].hidden), dtype=torch.bfloat16, device=dev)
+        self.last_stack = False
+
+    def routing(self, layer: int, batch: int):
+        """(indices, weights) [batch][K] that MoE sublayer ``layer`` selected
+        in the last call."""
+        K = self.top_k
+        if self.last_stack:
+            return self.stack_idx[layer].view(1, K), self.stack_w[layer].view(1, K)
+        return (self.topk_idx[layer, :batch * K].view(batch, K), self.topk_w[layer, :batch * K].view(batch, K))
 
     def __call__(self, x: torch.Tensor, record=None, stream=None):
         """Runs the step on x [B][H] (BF16, updated in place).  If ``record``
         is a list, a copy of the residual entering each sublayer is appended
         (for per-layer checks; not for graph capture)."""
         B = x.shape[0]
-        for i, (L, g) in enumerate(zip(self.moe_layers, self.moe_gammas)):
+        self.last_stack = self.stack_shape is not None and B == 1
+        if self.last_stack:
+            n = len(self.moe_layers)
             if record is not None:
                 record.append(x.clone())
-            flint_moe_decode(self.shapes[i], self.cweights[i], x, B, x, self.topk_idx[i], self.topk_w[i],
-                             g, self.ws, self.ws_bytes, stream)
+            flint_moe_decode_stack(self.stack_shape, self.table, n, self.gstack, x, x, self.stack_idx,
+                                   self.stack_w, self.layer_out if record is not None else None, self.ws,
+                                   self.ws_bytes, stream)
+            if record is not None:
+                for l in range(n - 1):
+                    record.append(self.layer_out[l].view(1, -1).clone())
+        else:
+            for i, (L, g) in enumerate(zip(self.moe_layers, self.moe_gammas)):
+                if record is not None:
+                    record.append(x.clone())
+                flint_moe_decode(self.shapes[i], self.cweights[i], x, B, x, self.topk_idx[i], self.topk_w[i],
+                                 g, self.ws, self.ws_bytes, stream)
         fl = FLINT_W_BF16 if self.wbf16 else 0
         for j, (d, g) in enumerate(zip(self.dense_layers, self.dense_gammas)):
             if record is not None:

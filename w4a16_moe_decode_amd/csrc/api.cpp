@@ -140,6 +140,7 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
   w.slot_mask = reinterpret_cast<uint32_t*>(take((int64_t)S * 4));
   w.slot_w = reinterpret_cast<float*>(take((int64_t)S * B * 4));
   w.h_words = reinterpret_cast<uint64_t*>(take((int64_t)64 * (FLINT_MAX_TOP_K + 1) * (imax / 2) * 8));
+  w.x_words = reinterpret_cast<uint64_t*>(take((int64_t)8 * (s.hidden / 2) * 8));
   w.h = reinterpret_cast<uint16_t*>(take((int64_t)S * B * imax * 2));
   w.bytes = off;
   return w;
@@ -275,6 +276,44 @@ int32_t flint_moe_decode(const flint_moe_shape* shape, const flint_moe_weights* 
                          void* stream) {
   return decode_common(-1, shape, weights, x, batch, out, topk_idx, topk_w, gamma, ws, ws_bytes,
                        stream);
+}
+
+int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const flint_moe_weights* layers,
+                               int32_t n_layers, const void* gammas, const void* x, void* out,
+                               int32_t* topk_idx, float* topk_w, void* layer_out, void* ws,
+                               int64_t ws_bytes, void* stream) {
+  const int st = check_shape(shape);
+  if (st != FLINT_OK) return st;
+  if (shape->flags & ~FLINT_RENORM) return FLINT_ERR_UNSUPPORTED;
+  if (n_layers <= 0) return FLINT_ERR_INVALID_ARG;
+  if (n_layers > FLINT_MAX_STACK_LAYERS) return FLINT_ERR_UNSUPPORTED;
+  FLINT_NEED(layers);
+  FLINT_NEED(gammas);
+  FLINT_NEED(x);
+  FLINT_NEED(out);
+  if (!topk_idx || !topk_w) return FLINT_ERR_INVALID_ARG;
+  if (!aligned4(topk_idx) || !aligned4(topk_w)) return FLINT_ERR_ALIGNMENT;
+  if (layer_out && !aligned16(layer_out)) return FLINT_ERR_ALIGNMENT;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return FLINT_ERR_ALIGNMENT;
+  if (ws_bytes < decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH)) return FLINT_ERR_WORKSPACE;
+  DecodeWs w = carve_decode_ws(ws, *shape, FLINT_MAX_DECODE_BATCH);
+  StackArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  LayerArgs& a = sa.base;
+  a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
+  a.K = shape->top_k; a.B = 1; a.eps = shape->rms_eps;
+  a.flags = shape->flags | FLINT_PRE_RMSNORM | FLINT_RESIDUAL;
+  if (!fused_stack_supported(a)) return FLINT_ERR_UNSUPPORTED;
+  sa.layers = layers;
+  sa.gammas = static_cast<const uint16_t*>(gammas);
+  sa.x_in = static_cast<const uint16_t*>(x);
+  sa.x_out = static_cast<uint16_t*>(out);
+  sa.topk_idx = topk_idx;
+  sa.topk_w = topk_w;
+  sa.layer_out = static_cast<uint16_t*>(layer_out);
+  sa.L = n_layers;
+  return to_status(launch_fused_stack(sa, w, static_cast<hipStream_t>(stream)));
 }
 
 int32_t flint_moe_decode_stage(int32_t stage, const flint_moe_shape* shape,

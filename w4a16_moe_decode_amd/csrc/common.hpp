@@ -45,10 +45,26 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double d) {
 }
 
 // RMSNorm's first rounding, BF16(x / rms), with rms = sqrt(mean(x^2) + eps)
-// in float64: x / rms is then rounded once, from float64, like the
-// definition; the second step (times gamma) is exact in float32.
-__device__ __forceinline__ float rms_scale_bf16(float x, double rms) {
-  return bf16_bits_to_f32(f64_to_bf16_bits((double)x / rms));
+// in float64: x / rms is rounded once, from float64, like the definition;
+// the second step (times gamma) is exact in float32.  1/rms is taken once
+// per token and x * (1/rms) is within a few float64 ulps of the quotient, so
+// the two can only round to different BF16 values when the product lies
+// within a few ulps of a BF16 rounding midpoint: there the quotient itself
+// is computed.
+struct Rms { double rms, rinv; };
+__device__ __forceinline__ Rms make_rms(double rms) { return Rms{rms, 1.0 / rms}; }
+__device__ __forceinline__ float rms_scale_bf16(float x, const Rms& r) {
+  double q = (double)x * r.rinv;
+  const uint64_t low = (uint64_t)__double_as_longlong(q) & 0x1fffffffffffull;   // bits below BF16
+  const uint64_t half = 0x100000000000ull;
+  const uint64_t dist = low > half ? low - half : half - low;
+  const bool near = dist <= 64;
+  if (__ballot(near) != 0ull) {                   // a wave-wide branch: rarely taken
+    double qd = (double)x / r.rms;
+    asm volatile("" : "+v"(qd));                  // keeps the division inside the branch
+    q = near ? qd : q;
+  }
+  return bf16_bits_to_f32(f64_to_bf16_bits(q));
 }
 
 // SiLU(z) = z / (1 + e^-z) in fp32 (expf: the HIP device function).
@@ -263,6 +279,7 @@ struct DecodeWs {
   uint32_t* slot_mask;   // [S] bit t set = token t routed to routed slot r
   float* slot_w;         // [S][8] combine weight of token t at routed slot r
   uint64_t* h_words;     // [K+1][Imax/2] (epoch << 32) | two BF16 of h, single-launch path
+  uint64_t* x_words;     // [8][H/2] (epoch << 32) | two BF16 of the residual, layer stack
   uint16_t* h;           // [S][8][Imax] BF16 SiLU(g)*u per slot and token; slot 0
                          // is the shared expert when there is one, routed
                          // slot r is slot r + (shared ? 1 : 0)
@@ -301,6 +318,20 @@ bool fused_decode_supported(const LayerArgs& a);
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 bool fused_decode_bn_supported(const LayerArgs& a);
 hipError_t launch_fused_decode_bn(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
+// A stack of MoE layers for one token in one launch (flint_moe_decode_stack).
+struct StackArgs {
+  LayerArgs base;                      // shape, flags, eps; pointers set per layer
+  const flint_moe_weights* layers;     // device array [L]
+  const uint16_t* gammas;              // [L][H]
+  const uint16_t* x_in;                // [H]
+  uint16_t* x_out;                     // [H]
+  int32_t* topk_idx;                   // [L][K]
+  float* topk_w;                       // [L][K]
+  uint16_t* layer_out;                 // [L][H] or null
+  int L;
+};
+bool fused_stack_supported(const LayerArgs& a);
+hipError_t launch_fused_stack(const StackArgs& sa, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm_on_the_fly,
                           hipStream_t st);
 hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int dense_epilogue,

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
         }
       }
       ss = wave_sum_f64(ss);
-      const double rms = sqrt(ss / (double)H + (double)a.eps);
+      const Rms rms = make_rms(sqrt(ss / (double)H + (double)a.eps));
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
         uint32_t q[4] = {xt[i].x, xt[i].y, xt[i].z, xt[i].w};
@@ -248,7 +248,7 @@ __device__ __forceinline__ DChunk<WF> decode_chunk(uint4 c, uint32_t sc) {
 // x chunk with RMSNorm applied on the fly: BF16(BF16(x / rms) * gamma)
 template <int WF>
 __device__ __forceinline__ XChunk<WF> load_x_norm(const uint16_t* row, const uint16_t* gamma, int j,
-                                                  double rms) {
+                                                  const Rms& rms) {
   XChunk<WF> x = load_x<WF>(row, j);
   const XChunk<WF> g = load_x<WF>(gamma, j);
 #pragma unroll
@@ -313,9 +313,9 @@ __global__ __launch_bounds__(64 * NW) void gate_up_kernel(LayerArgs a, DecodeWs 
   }
   const uint16_t* xsrc = NORM ? a.x : ((a.flags & FLINT_PRE_RMSNORM) && !dense ? ws.xn : a.x);
 
-  double rinv[BT];      // RMS of each token (only with NORM)
+  Rms rinv[BT];         // RMS of each token (only with NORM)
 #pragma unroll
-  for (int t = 0; t < BT; ++t) rinv[t] = 1.0;
+  for (int t = 0; t < BT; ++t) rinv[t] = Rms{1.0, 1.0};
   if constexpr (NORM) {
     const int niter = (H + 511) / 512;
 #pragma unroll
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(64 * NW) void gate_up_kernel(LayerArgs a, DecodeWs 
           }
         }
         ss = wave_sum_f64(ss);
-        rinv[t] = sqrt(ss / (double)H + (double)a.eps);
+        rinv[t] = make_rms(sqrt(ss / (double)H + (double)a.eps));
       }
     }
   }

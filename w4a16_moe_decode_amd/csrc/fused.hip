@@ -32,7 +32,7 @@ namespace flint {
 namespace {
 
 // x chunk j (32 columns) of the layer input, RMS-normalised when asked
-__device__ __forceinline__ XChunk<FMT_NVFP4> input_chunk(const LayerArgs& a, int j, bool norm, double rms) {
+__device__ __forceinline__ XChunk<FMT_NVFP4> input_chunk(const LayerArgs& a, int j, bool norm, const Rms& rms) {
   XChunk<FMT_NVFP4> x = load_x<FMT_NVFP4>(a.x, j);
   if (norm) {
     const XChunk<FMT_NVFP4> g = load_x<FMT_NVFP4>(a.gamma, j);
@@ -47,7 +47,7 @@ __device__ __forceinline__ XChunk<FMT_NVFP4> input_chunk(const LayerArgs& a, int
 }
 
 // the 8 input columns c0..c0+7 (a 16-byte segment), RMS-normalised when asked
-__device__ __forceinline__ uint4 input_8(const LayerArgs& a, int c0, bool norm, double rms) {
+__device__ __forceinline__ uint4 input_8(const LayerArgs& a, int c0, bool norm, const Rms& rms) {
   uint4 v = *reinterpret_cast<const uint4*>(a.x + c0);
   if (norm) {
     const uint4 g = *reinterpret_cast<const uint4*>(a.gamma + c0);
@@ -85,10 +85,13 @@ __device__ __forceinline__ uint32_t gu_finish(const GUItem<NCH>& it, const GURow
   return pack_bf16x2(h[0], h[1]);
 }
 
+// One MoE layer for one token, run by every workgroup of the persistent grid.
 // Down rows of one workgroup: GPW = 64/GD rows per wave-wide load, DW
-// row-sets per workgroup (DW * GPW rows), chunk steps of GD lanes.
+// row-sets per workgroup (DW * GPW rows), chunk steps of GD lanes.  Layer
+// `layer` of a launch tags its hand-off words with the stored epoch + 1 +
+// layer; the epoch it used is returned.  a.x and a.out may point to LDS.
 template <int NCH, int GD, int DW, int MAXS>
-__global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, DecodeWs ws) {
+__device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const DecodeWs& ws, uint32_t layer) {
   constexpr int GPW = 64 / GD;
   constexpr int DROWS = DW * GPW;                 // output rows per workgroup
   constexpr int IMAXW = 2048 / 2;                 // h words per slot held in LDS (I <= 2048)
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
   const uint64_t* hw = hw_all + (size_t)rep * hrep;
 
   // ---- RMS of the token (every wave, from L2) -------------------------------
-  double rms = 1.0;
+  Rms rms{1.0, 1.0};
   if (norm) {
     double ss = 0.0;
     for (int c = 8 * lane; c < H; c += 512) {
@@ -127,14 +130,14 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
         ss = fma(hi, hi, ss);
       }
     }
-    rms = sqrt(wave_sum_f64(ss) / (double)H + (double)a.eps);
+    rms = make_rms(sqrt(wave_sum_f64(ss) / (double)H + (double)a.eps));
   }
   XChunk<FMT_NVFP4> xc[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) xc[c] = input_chunk(a, lane + 64 * c, norm, rms);
   // the launch epoch: a vector load, so that waiting for it holds up neither
   // the kernel arguments nor the loads above
-  const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u + layer;
 
   // ---- phase 1: router quarter rows + shared expert gate/up ------------------
   // expert e is owned by workgroup e % G; its 4 waves take a quarter each
@@ -374,11 +377,100 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
     }
   }
 
+  return epoch;
+}
+
+template <int NCH, int GD, int DW, int MAXS>
+__global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, DecodeWs ws) {
+  const uint32_t epoch = fused_layer_b1<NCH, GD, DW, MAXS>(a, ws, 0);
   // ---- advance the epoch for the next launch -----------------------------------
   // Every workgroup published a router logit or an arrival word tagged with
   // the epoch it read at its start, and workgroup 0 has seen all of them
   // before its top-k: no workgroup of this launch can still be about to read
   // the old value.  No ticket round trip is needed.
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ws.epoch = epoch;
+}
+
+// A stack of L MoE layers for one token: layer l takes the residual x_l
+// and leaves x_{l+1} = BF16(x_l + BF16(MoE_l(BF16(BF16(x_l / rms) * gamma_l))))
+// (pre-norm residual sublayers, the decode step of "Day-0 Support for Flint
+// on vLLM", "Model architecture").  The layers run back to back in one
+// launch: each workgroup keeps the residual in LDS, computes its output rows
+// of layer l, publishes them as epoch-tagged words (two BF16 per word,
+// kReplicas copies) and polls every row before layer l + 1 starts.  No word
+// can be overwritten while another workgroup still needs it: a workgroup
+// moves on to layer l + 1's hand-offs only after it has seen layer l's
+// logits (or arrival words) of every workgroup, each published after that
+// workgroup finished reading layer l's inputs.
+template <int NCH, int GD, int DW, int MAXS>
+__global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa, DecodeWs ws) {
+  constexpr int DROWS = DW * (64 / GD);
+  __shared__ __align__(16) uint16_t s_x[4096];      // the residual entering the layer
+  __shared__ __align__(16) uint16_t s_xo[4096];     // this workgroup's rows of its output
+  const int H = sa.base.H, K = sa.base.K;
+  const int n0 = blockIdx.x * DROWS;
+  const int rep = blockIdx.x % kReplicas;
+  const size_t xrep = (size_t)H / 2;
+  for (int q = threadIdx.x; q < H / 8; q += 256)
+    reinterpret_cast<uint4*>(s_x)[q] = reinterpret_cast<const uint4*>(sa.x_in)[q];
+  __syncthreads();
+  uint32_t epoch = 0;
+  for (int l = 0; l < sa.L; ++l) {
+    LayerArgs a = sa.base;
+    const flint_moe_weights& w = sa.layers[l];
+    a.router = static_cast<const uint16_t*>(w.router);
+    a.gu_codes = static_cast<const uint8_t*>(w.gu_codes);
+    a.gu_scales = static_cast<const uint8_t*>(w.gu_scales);
+    a.d_codes = static_cast<const uint8_t*>(w.d_codes);
+    a.d_scales = static_cast<const uint8_t*>(w.d_scales);
+    a.gscale = w.gscale;
+    a.sh_gu_codes = static_cast<const uint8_t*>(w.sh_gu_codes);
+    a.sh_gu_scales = static_cast<const uint8_t*>(w.sh_gu_scales);
+    a.sh_d_codes = static_cast<const uint8_t*>(w.sh_d_codes);
+    a.sh_d_scales = static_cast<const uint8_t*>(w.sh_d_scales);
+    a.sh_gscale = w.sh_gscale;
+    a.gamma = sa.gammas + (size_t)l * H;
+    a.x = s_x;
+    a.out = s_xo;
+    a.topk_idx = sa.topk_idx + (size_t)l * K;
+    a.topk_w = sa.topk_w + (size_t)l * K;
+    epoch = fused_layer_b1<NCH, GD, DW, MAXS>(a, ws, (uint32_t)l);
+    __syncthreads();                               // this workgroup's rows of x_{l+1} are in s_xo
+    if (sa.layer_out)
+      for (int r = threadIdx.x; r < DROWS; r += 256)
+        if (n0 + r < H) sa.layer_out[(size_t)l * H + n0 + r] = s_xo[n0 + r];
+    if (l + 1 == sa.L) {
+      for (int r = threadIdx.x; r < DROWS; r += 256)
+        if (n0 + r < H) sa.x_out[n0 + r] = s_xo[n0 + r];
+      break;
+    }
+    // publish this workgroup's rows (pairs n, n+1), one replica per lane
+    for (int q = threadIdx.x; q < (DROWS / 2) * kReplicas; q += 256) {
+      const int wq = q / kReplicas, r = q % kReplicas, n = n0 + 2 * wq;
+      if (n < H)
+        put_word(ws.x_words + (size_t)r * xrep + n / 2, epoch,
+                 (uint32_t)s_xo[n] | ((uint32_t)s_xo[n + 1] << 16));
+    }
+    // and take every row of x_{l+1}
+    const uint64_t* xw = ws.x_words + (size_t)rep * xrep;
+    for (int q0 = threadIdx.x; q0 < H / 2; q0 += 4 * 256) {
+      uint64_t wd[4];
+      const uint64_t* ptr[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + 256 * u;
+        ok[u] = q < H / 2;
+        ptr[u] = xw + (ok[u] ? q : 0);
+      }
+      poll_words<4>(wd, ptr, ok, epoch, ws.error);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ok[u]) reinterpret_cast<uint32_t*>(s_x)[q0 + 256 * u] = (uint32_t)wd[u];
+    }
+    __syncthreads();
+  }
+  // the last layer's epoch, seen by every workgroup as above
   if (blockIdx.x == 0 && threadIdx.x == 0) *ws.epoch = epoch;
 }
 
@@ -411,6 +503,31 @@ bool fused_config(const LayerArgs& a, FusedConfig& c) {
 }
 
 }  // namespace
+
+bool fused_stack_supported(const LayerArgs& a) {
+  FusedConfig c;
+  if (!fused_config(a, c)) return false;
+  return (c.dw * (64 / c.gd)) % 2 == 0;          // rows are published in pairs
+}
+
+hipError_t launch_fused_stack(const StackArgs& sa, const DecodeWs& ws, hipStream_t st) {
+  FusedConfig c;
+  if (!fused_config(sa.base, c) || (c.dw * (64 / c.gd)) % 2) return hipErrorInvalidConfiguration;
+  constexpr int MAXS = FLINT_MAX_TOP_K + 1;
+#define FLINT_STACK(NCH_, GD_, DW_)                                                              \
+  hipLaunchKernelGGL((fused_stack_b1_kernel<NCH_, GD_, DW_, MAXS>), dim3(c.G), dim3(256), 0, st, sa, ws)
+#define FLINT_STACK_GD(NCH_)                                                         \
+  switch (c.gd) {                                                                    \
+    case 8: if (c.dw <= 1) FLINT_STACK(NCH_, 8, 1); else FLINT_STACK(NCH_, 8, 2); break;    \
+    case 16: if (c.dw <= 1) FLINT_STACK(NCH_, 16, 1); else FLINT_STACK(NCH_, 16, 2); break; \
+    case 32: if (c.dw <= 1) FLINT_STACK(NCH_, 32, 1); else FLINT_STACK(NCH_, 32, 2); break; \
+    default: FLINT_STACK(NCH_, 64, 2); break;                                        \
+  }
+  if (c.nch == 1) { FLINT_STACK_GD(1) } else { FLINT_STACK_GD(2) }
+#undef FLINT_STACK_GD
+#undef FLINT_STACK
+  return hipGetLastError();
+}
 
 bool fused_decode_supported(const LayerArgs& a) {
   FusedConfig c;

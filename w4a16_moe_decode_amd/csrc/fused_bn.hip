@@ -237,7 +237,7 @@ void fused_decode_bn_kernel(LayerArgs a, DecodeWs ws) {
       const int t = q / (H / 8), c = 8 * (q - t * (H / 8));
       uint4* px = reinterpret_cast<uint4*>(s_x + t * Hw + c / 2);
       const uint4 v = *px;
-      const double rms = s_rms[t];
+      const Rms rms = make_rms(s_rms[t]);
       const uint4 g = gv[i];
       uint32_t xq[4] = {v.x, v.y, v.z, v.w};
       const uint32_t gq[4] = {g.x, g.y, g.z, g.w};

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(LayerArgs a, PrefillW
     }
   }
   ss = wave_sum_f64(ss);
-  const double rms = sqrt(ss / (double)H + (double)a.eps);
+  const Rms rms = make_rms(sqrt(ss / (double)H + (double)a.eps));
   for (int c = 8 * lane; c < H; c += 512) {
     const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
     const uint4 g = *reinterpret_cast<const uint4*>(a.gamma + c);
