@@ -44,27 +44,58 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double d) {
   return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)b)) >> 16);
 }
 
-// RMSNorm's first rounding, BF16(x / rms), with rms = sqrt(mean(x^2) + eps)
-// in float64: x / rms is rounded once, from float64, like the definition;
-// the second step (times gamma) is exact in float32.  1/rms is taken once
-// per token and x * (1/rms) is within a few float64 ulps of the quotient, so
-// the two can only round to different BF16 values when the product lies
-// within a few ulps of a BF16 rounding midpoint: there the quotient itself
-// is computed.
-struct Rms { double rms, rinv; };
-__device__ __forceinline__ Rms make_rms(double rms) { return Rms{rms, 1.0 / rms}; }
-__device__ __forceinline__ float rms_scale_bf16(float x, const Rms& r) {
-  double q = (double)x * r.rinv;
-  const uint64_t low = (uint64_t)__double_as_longlong(q) & 0x1fffffffffffull;   // bits below BF16
-  const uint64_t half = 0x100000000000ull;
-  const uint64_t dist = low > half ? low - half : half - low;
-  const bool near = dist <= 64;
-  if (__ballot(near) != 0ull) {                   // a wave-wide branch: rarely taken
-    double qd = (double)x / r.rms;
-    asm volatile("" : "+v"(qd));                  // keeps the division inside the branch
-    q = near ? qd : q;
+// RMSNorm of packed BF16 pairs: BF16(BF16(x / rms) * gamma), with
+// rms = sqrt(mean(x^2) + eps) in float64 and x / rms rounded once, from
+// float64, like the definition; the second step (times gamma) is exact in
+// float32 before its rounding.  The quotient is first taken as
+// x * float(1/rms) in float32, which is within 1.5 float32 ulps of x / rms;
+// both therefore round to the same BF16 value unless that product lies
+// within a few ulps of a BF16 rounding midpoint (its 16 bits below the BF16
+// mantissa near 0x8000).  Only such values -- a few in ten thousand -- are
+// recomputed as a float64 division.  When 1/rms is outside float32's
+// comfortable range every value takes the division.
+struct Rms { double rms; float rinv; bool fast; };
+__device__ __forceinline__ Rms make_rms(double rms) {
+  const float ri = (float)(1.0 / rms);
+  return Rms{rms, ri, ri >= 0x1p-100f && ri <= 0x1p100f};
+}
+__device__ __forceinline__ bool near_bf16_midpoint(float f) {
+  return ((__float_as_uint(f) - 0x7ffcu) & 0xffffu) <= 8u;
+}
+__device__ __forceinline__ uint32_t bf16_quotient_bits(float x, double rms) {
+  double q = (double)x / rms;
+  asm volatile("" : "+v"(q));                     // keeps the division on the rare path
+  return f64_to_bf16_bits(q);
+}
+template <int N>
+__device__ __forceinline__ void rms_norm_words(uint32_t (&v)[N], const uint32_t (&g)[N], const Rms& r) {
+  uint32_t y[N];
+  bool nlo[N], nhi[N];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float lo = bf16_lo(v[i]) * r.rinv, hi = bf16_hi(v[i]) * r.rinv;
+    nlo[i] = near_bf16_midpoint(lo) || !r.fast;
+    nhi[i] = near_bf16_midpoint(hi) || !r.fast;
+    any = any || nlo[i] || nhi[i];
+    y[i] = pack_bf16x2_rne(lo, hi);
   }
-  return bf16_bits_to_f32(f64_to_bf16_bits(q));
+  if (__ballot(any) != 0ull) {                    // wave-wide branch, rarely taken
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (nlo[i]) y[i] = (y[i] & 0xffff0000u) | bf16_quotient_bits(bf16_lo(v[i]), r.rms);
+      if (nhi[i]) y[i] = (y[i] & 0x0000ffffu) | (bf16_quotient_bits(bf16_hi(v[i]), r.rms) << 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = pack_bf16x2_rne(bf16_lo(y[i]) * bf16_lo(g[i]), bf16_hi(y[i]) * bf16_hi(g[i]));
+}
+// the same for one uint4 (8 values)
+__device__ __forceinline__ uint4 rms_norm_8(uint4 x, uint4 g, const Rms& r) {
+  uint32_t v[4] = {x.x, x.y, x.z, x.w};
+  const uint32_t gv[4] = {g.x, g.y, g.z, g.w};
+  rms_norm_words<4>(v, gv, r);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // SiLU(z) = z / (1 + e^-z) in fp32 (expf: the HIP device function).

@@ -98,15 +98,7 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
       const Rms rms = make_rms(sqrt(ss / (double)H + (double)a.eps));
 #pragma unroll
       for (int i = 0; i < NIT; ++i) {
-        uint32_t q[4] = {xt[i].x, xt[i].y, xt[i].z, xt[i].w};
-        const uint32_t g4[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float lo = round_bf16(rms_scale_bf16(bf16_lo(q[m]), rms) * bf16_lo(g4[m]));
-          const float hi = round_bf16(rms_scale_bf16(bf16_hi(q[m]), rms) * bf16_hi(g4[m]));
-          q[m] = pack_bf16x2(lo, hi);
-        }
-        xt[i] = make_uint4(q[0], q[1], q[2], q[3]);
+        xt[i] = rms_norm_8(xt[i], gv[i], rms);
         const int col = 8 * (lane + 64 * i);
         if (e == 0 && t < B && col < H) *reinterpret_cast<uint4*>(ws.xn + (size_t)t * H + col) = xt[i];
       }
@@ -251,12 +243,7 @@ __device__ __forceinline__ XChunk<WF> load_x_norm(const uint16_t* row, const uin
                                                   const Rms& rms) {
   XChunk<WF> x = load_x<WF>(row, j);
   const XChunk<WF> g = load_x<WF>(gamma, j);
-#pragma unroll
-  for (int m = 0; m < Fmt<WF>::VALS / 2; ++m) {
-    const float lo = round_bf16(rms_scale_bf16(bf16_lo(x.v[m]), rms) * bf16_lo(g.v[m]));
-    const float hi = round_bf16(rms_scale_bf16(bf16_hi(x.v[m]), rms) * bf16_hi(g.v[m]));
-    x.v[m] = pack_bf16x2(lo, hi);
-  }
+  rms_norm_words<Fmt<WF>::VALS / 2>(x.v, g.v, rms);
   return x;
 }
 
@@ -315,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void gate_up_kernel(LayerArgs a, DecodeWs 
 
   Rms rinv[BT];         // RMS of each token (only with NORM)
 #pragma unroll
-  for (int t = 0; t < BT; ++t) rinv[t] = Rms{1.0, 1.0};
+  for (int t = 0; t < BT; ++t) rinv[t] = make_rms(1.0);
   if constexpr (NORM) {
     const int niter = (H + 511) / 512;
 #pragma unroll
@@ -576,6 +563,572 @@ __global__ __launch_bounds__(64 * NW) void down_kernel(LayerArgs a, DecodeWs ws,
   }
 }
 
+// routed + shared slots a decode of this batch can fill (decode_max_slots)
+__device__ __forceinline__ int decode_max_slots_dev(const LayerArgs& a) {
+  const int u = a.B * a.K;
+  return (u < a.E ? u : a.E) + (a.SI > 0 ? 1 : 0);
+}
+
+// q / d and q % d for 0 <= q < 2^22 and d >= 1 (inv = 1.0f / d): a float
+// estimate corrected by one step either way, instead of an integer division.
+__device__ __forceinline__ int div_small(int q, int d, float inv, int& rem) {
+  int p = (int)((float)q * inv);
+  int r = q - p * d;
+  if (r >= d) { ++p; r -= d; }
+  if (r < 0) { --p; r += d; }
+  rem = r;
+  return p;
+}
+
+// ----------------------------------------------------- gate/up, batch 2..8 --
+// The rows of gate_up_kernel for a batch of tokens, 64 lanes per row.  The
+// workgroup issues its weight loads, then stages the activations of the
+// tokens routed to its slot in LDS (one copy per workgroup; every load of
+// the workgroup is in flight at once, so the whole prologue costs one HBM
+// round trip).  Each lane then decodes its NCH weight chunks once and walks
+// the staged tokens,
+// finishing one token (reduction, SiLU * up, store) before the next.  LDS
+// layout: staged token i, 16-byte quad m of chunk j at
+// s_x[(i * QPC + m) * cpr + j], so a wave reads consecutive words.
+template <int WF, int P, int NW, int NCH, int KQ>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KQ > 1 ? 2 : 4, KQ > 1 ? 2 : 4)))
+void gate_up_batch_kernel(LayerArgs a, DecodeWs ws, uint16_t* hout,
+                                                                int h_slot_stride, int h_tok_stride) {
+  constexpr int BT = kMaxB, NT = 64 * NW;
+  constexpr int VALS = Fmt<WF>::VALS, QPC = VALS / 8;
+  extern __shared__ uint4 s_x[];
+  const int slot = blockIdx.y;
+  const bool has_sh = a.SI > 0;
+  const bool shared = has_sh && slot == 0;
+  const int inter = shared ? a.SI : a.I;
+  if ((int)blockIdx.x * NW * P >= inter) return;    // the whole workgroup
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * NW + wave) * P;
+  const int H = a.H, cpr = H / VALS, q8 = H / 8;
+
+  MatRef<WF> mg, mu;
+  float gs_g = 1.f, gs_u = 1.f;
+  mg.cols = mu.cols = H;
+  uint32_t mask;
+  if (shared) {
+    mask = (1u << a.B) - 1u;
+    if constexpr (WF == FMT_NVFP4) {
+      mg.codes = a.sh_gu_codes;  mu.codes = a.sh_gu_codes + (size_t)inter * H / 2;
+      mg.scales = a.sh_gu_scales; mu.scales = a.sh_gu_scales + (size_t)inter * H / 16;
+      gs_g = a.sh_gscale[0]; gs_u = a.sh_gscale[1];
+    } else {
+      mg.wbf = a.sh_gu_bf16; mu.wbf = a.sh_gu_bf16 + (size_t)inter * H;
+    }
+  } else {
+    const int r = slot - (has_sh ? 1 : 0);
+    if (r >= *ws.nslot) return;
+    const int e = ws.slot_expert[r];
+    mask = ws.slot_mask[r];
+    if constexpr (WF == FMT_NVFP4) {
+      const size_t mc = (size_t)inter * H / 2, ms = (size_t)inter * H / 16;
+      mg.codes = a.gu_codes + (size_t)(2 * e) * mc;  mu.codes = mg.codes + mc;
+      mg.scales = a.gu_scales + (size_t)(2 * e) * ms; mu.scales = mg.scales + ms;
+      gs_g = a.gscale[3 * e + 0]; gs_u = a.gscale[3 * e + 1];
+    } else {
+      const size_t mb = (size_t)inter * H;
+      mg.wbf = a.gu_bf16 + (size_t)(2 * e) * mb; mu.wbf = mg.wbf + mb;
+    }
+  }
+  const uint16_t* xsrc = (a.flags & FLINT_PRE_RMSNORM) ? ws.xn : a.x;
+  const int n = __popc(mask);
+  uint32_t tokp = 0;                               // token of staged position i, 4 bits each
+  {
+    uint32_t m = mask;
+#pragma unroll
+    for (int i = 0; i < BT; ++i)
+      if (m) { tokp |= (uint32_t)(__ffs(m) - 1) << (4 * i); m &= m - 1u; }
+  }
+
+  // weights: chunks j = lane + 64 c of P gate rows and P up rows, every load
+  // unconditional (rows and chunks out of range read row 0, chunk 0)
+  uint4 rg[NCH][P], ru[NCH][P];
+  uint32_t sg[NCH][P], su[NCH][P];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int j = lane + 64 * c;
+    const int jc = j < cpr ? j : 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int r = row0 + p;
+      const int rc = r < inter ? r : 0;
+      rg[c][p] = load_chunk_raw<WF>(mg, rc, jc, sg[c][p]);
+      ru[c][p] = load_chunk_raw<WF>(mu, rc, jc, su[c][p]);
+    }
+  }
+  // activations: quad q (chunk j, quad m) of every staged token, q8 <= KQ * NT
+  uint4 xv[KQ][BT];
+  int qv[KQ];
+  const float inv_cpr = 1.0f / (float)cpr;
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) {
+    const int q = threadIdx.x + NT * kq;
+    qv[kq] = q;
+    int j;
+    const int m = div_small(q, cpr, inv_cpr, j);
+    // every load is issued; positions out of range all read the first quad,
+    // so their lanes share one address
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const int t = (tokp >> (4 * i)) & 15;
+      const bool ok = q < q8 && i < n;
+      const uint16_t* src = ok ? xsrc + (size_t)t * H + j * VALS + 8 * m : xsrc;
+      xv[kq][i] = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+
+  // every store is made too (a conditional one would draw its load into the
+  // branch, behind a full wait): positions out of range go to this thread's
+  // slot past the staged tokens
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+    for (int i = 0; i < BT; ++i)
+      s_x[qv[kq] < q8 && i < n ? i * q8 + qv[kq] : a.B * q8 + (int)threadIdx.x] = xv[kq][i];
+  __syncthreads();
+
+  DChunk<WF> dg[NCH][P], du[NCH][P];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      dg[c][p] = decode_chunk<WF>(rg[c][p], sg[c][p]);
+      du[c][p] = decode_chunk<WF>(ru[c][p], su[c][p]);
+    }
+  for (int i = 0; i < n; ++i) {
+    float acc[P][2];
+#pragma unroll
+    for (int p = 0; p < P; ++p) acc[p][0] = acc[p][1] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int j = lane + 64 * c;
+      if (j < cpr) {
+        XChunk<WF> xc;
+#pragma unroll
+        for (int m = 0; m < QPC; ++m) {
+          const uint4 v = s_x[(i * QPC + m) * cpr + j];
+          xc.v[4 * m + 0] = v.x; xc.v[4 * m + 1] = v.y; xc.v[4 * m + 2] = v.z; xc.v[4 * m + 3] = v.w;
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          acc[p][0] += chunk_dot(dg[c][p], xc);
+          acc[p][1] += chunk_dot(du[c][p], xc);
+        }
+      }
+    }
+    const int t = (tokp >> (4 * i)) & 15;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float g = group_sum<64>(acc[p][0]);
+      const float u = group_sum<64>(acc[p][1]);
+      const int r = row0 + p;
+      if (lane == 0 && r < inter) {
+        const float gv = round_bf16(g * gs_g);
+        const float uv = round_bf16(u * gs_u);
+        const float av = round_bf16(silu_f32(gv));
+        hout[(size_t)slot * h_slot_stride + (size_t)t * h_tok_stride + r] = f32_to_bf16_bits(av * uv);
+      }
+    }
+  }
+}
+
+// ------------------------------------------- gate/up, batch 2..8, NVFP4 ----
+// The NVFP4 rows of gate_up_kernel for a batch, 16 lanes per row: lane li of
+// a row group owns the CPL consecutive chunks li * CPL .. li * CPL + CPL - 1
+// (64 * CPL bytes of codes, 2 * CPL of scales), so a row's cross-lane sum is
+// four steps, paid once per CPL chunks.  A wave holds 4 rows, a workgroup
+// NW * 4.  The slot table entry is read first (scalar loads, one round
+// trip); the weight loads follow, then the activations of the slot's tokens
+// are staged in LDS (every load of the workgroup in flight at once; the
+// staging waits for the weights, as loads complete in order).  The expert
+// and the matrix bases are wave-uniform; each lane adds a 32-bit offset of
+// its row and chunks, taken once.  LDS layout: staged token i, quad m of the
+// lane's chunk c at s_x[i * q8 + (c * 4 + m) * 16 + li], so the 16 lanes of
+// a row group read consecutive words.
+template <int NW, int CPL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(CPL > 4 ? 2 : 4, CPL > 4 ? 2 : 4)))
+void gate_up_nv_batch_kernel(LayerArgs a, DecodeWs ws, uint16_t* hout, int h_slot_stride, int h_tok_stride) {
+  constexpr int BT = kMaxB, NT = 64 * NW;
+  constexpr int G = 16, QPC = 4;
+  extern __shared__ uint4 s_x[];
+  const int slot = blockIdx.y;
+  const bool has_sh = a.SI > 0;
+  const bool shared = has_sh && slot == 0;
+  const int inter = shared ? a.SI : a.I;
+  if ((int)blockIdx.x * NW * 4 >= inter) return;    // the whole workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int grp = lane / G, li = lane % G;
+  const int r = (blockIdx.x * NW + wave) * 4 + grp;  // this lane's row
+  const int H = a.H, q8 = H / 8;
+
+  // the slot table entry (read before the slot count, which the table always
+  // exceeds, so that the three loads make one round trip)
+  const int rr = slot - (has_sh ? 1 : 0);
+  const int e = shared ? 0 : ws.slot_expert[rr];
+  const uint32_t mask = shared ? (1u << a.B) - 1u : ws.slot_mask[rr];
+  if (!shared && rr >= *ws.nslot) return;
+  const size_t mc = (size_t)inter * H / 2, ms = (size_t)inter * H / 16;
+  const uint8_t* gc = shared ? a.sh_gu_codes : a.gu_codes + (size_t)(2 * e) * mc;
+  const uint8_t* gsb = shared ? a.sh_gu_scales : a.gu_scales + (size_t)(2 * e) * ms;
+  const uint8_t* uc = gc + mc;
+  const uint8_t* usb = gsb + ms;
+  const float gs_g = shared ? a.sh_gscale[0] : a.gscale[3 * e + 0];
+  const float gs_u = shared ? a.sh_gscale[1] : a.gscale[3 * e + 1];
+
+  // weights: this lane's CPL chunks of its gate and up rows (rows past the
+  // matrix read row 0 and are not stored)
+  const uint32_t rc = r < inter ? (uint32_t)r : 0u;
+  const uint32_t oc = rc * ((uint32_t)H / 2) + (uint32_t)li * 16u * CPL;
+  const uint32_t os = rc * ((uint32_t)H / 16) + (uint32_t)li * 2u * CPL;
+  uint4 wg[CPL], wu[CPL];
+  uint32_t sg2[CPL / 2], su2[CPL / 2];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    wg[c] = reinterpret_cast<const uint4*>(gc + oc)[c];
+    wu[c] = reinterpret_cast<const uint4*>(uc + oc)[c];
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; c += 2) {
+    sg2[c / 2] = reinterpret_cast<const uint32_t*>(gsb + os)[c / 2];
+    su2[c / 2] = reinterpret_cast<const uint32_t*>(usb + os)[c / 2];
+  }
+
+  const uint16_t* xsrc = (a.flags & FLINT_PRE_RMSNORM) ? ws.xn : a.x;
+  const int n = __popc(mask);
+  uint32_t tokp = 0;                               // token of staged position i, 4 bits each
+  {
+    uint32_t m = mask;
+#pragma unroll
+    for (int i = 0; i < BT; ++i)
+      if (m) { tokp |= (uint32_t)(__ffs(m) - 1) << (4 * i); m &= m - 1u; }
+  }
+  // activations: LDS position q of staged token i holds columns
+  // 32 * (CPL * (q % 16) + (q / 16) / 4) + 8 * ((q / 16) % 4); q8 <= NT.
+  // Every load and store is made (a conditional one would draw its load into
+  // the branch behind a full wait): positions out of range read the first
+  // quad and write this thread's slot past the staged tokens.
+  {
+    const int q = threadIdx.x;
+    const int qli = q % G, qcm = q / G;
+    const int col = 32 * (CPL * qli + qcm / QPC) + 8 * (qcm % QPC);
+    uint4 xv[BT];
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const int t = (tokp >> (4 * i)) & 15;
+      const bool ok = q < q8 && i < n;
+      xv[i] = *reinterpret_cast<const uint4*>(ok ? xsrc + (size_t)t * H + col : xsrc);
+    }
+#pragma unroll
+    for (int i = 0; i < BT; ++i) s_x[q < q8 && i < n ? i * q8 + q : a.B * q8 + q] = xv[i];
+  }
+  __syncthreads();
+
+  float ag[BT], au[BT];
+#pragma unroll
+  for (int i = 0; i < BT; ++i) ag[i] = au[i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const uint32_t sgc = c % 2 ? sg2[c / 2] >> 16 : sg2[c / 2] & 0xffffu;
+    const uint32_t suc = c % 2 ? su2[c / 2] >> 16 : su2[c / 2] & 0xffffu;
+    const DChunk<FMT_NVFP4> dg = decode_nvfp4(wg[c], sgc);
+    const DChunk<FMT_NVFP4> du = decode_nvfp4(wu[c], suc);
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      if (i >= n) break;
+      XChunk<FMT_NVFP4> xc;
+#pragma unroll
+      for (int m = 0; m < QPC; ++m) {
+        const uint4 v = s_x[i * q8 + (c * QPC + m) * G + li];
+        xc.v[4 * m + 0] = v.x; xc.v[4 * m + 1] = v.y; xc.v[4 * m + 2] = v.z; xc.v[4 * m + 3] = v.w;
+      }
+      ag[i] += chunk_dot(dg, xc);
+      au[i] += chunk_dot(du, xc);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < BT; ++i) {
+    if (i >= n) break;
+    const float g = group_sum<G>(ag[i]);
+    const float u = group_sum<G>(au[i]);
+    if (li == 0 && r < inter) {
+      const int t = (tokp >> (4 * i)) & 15;
+      const float gv = round_bf16(g * gs_g);
+      const float uv = round_bf16(u * gs_u);
+      const float av = round_bf16(silu_f32(gv));
+      hout[(size_t)slot * h_slot_stride + (size_t)t * h_tok_stride + r] = f32_to_bf16_bits(av * uv);
+    }
+  }
+}
+
+// ------------------------------------------------ down+combine, batch 2..8 --
+// down_kernel for a batch.  Every (slot, token) pair of the layer has its h
+// row staged in LDS once per workgroup: wave 0 reads the slot table (one
+// round trip: every entry a lane may need is loaded at once) and builds the
+// pair list with a prefix sum of the slots' token counts; all threads then
+// copy the h rows into LDS.  Only after that does any wave issue weight
+// loads: vector loads complete in order, so h issued behind the weights
+// would wait for all of them, while weights issued last let each item be
+// computed as soon as its own rows arrive.  LDS layout as in
+// gate_up_batch_kernel: pair p, quad m of chunk j at
+// s_h[(p * QPC + m) * cmax + j].
+template <int WF, int G, int RW, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void down_batch_kernel(LayerArgs a, DecodeWs ws, const uint16_t* hin,
+                                                             int h_slot_stride, int h_tok_stride) {
+  constexpr int BT = kMaxB, NT = 64 * NW;
+  constexpr int GPW = 64 / G, RPW = RW * GPW;
+  constexpr int VALS = Fmt<WF>::VALS, QPC = VALS / 8;
+  constexpr int NHL = 8;                           // h loads per thread issued together
+  extern __shared__ uint4 s_h[];
+  __shared__ float s_red[NW][RPW][BT];
+  __shared__ int s_exp[kMaxSlots];
+  __shared__ uint32_t s_msk[kMaxSlots];
+  __shared__ int s_pb[kMaxSlots];
+  __shared__ float s_wt[kMaxSlots][BT];
+  __shared__ uint16_t s_pair[kMaxSlots * BT];      // pair -> slot << 3 | token
+  __shared__ int s_np;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane / G, li = lane % G;
+  const int H = a.H;
+  const int n0 = blockIdx.x * RPW;
+  const int sh = a.SI > 0 ? 1 : 0;
+  const int I = a.I, SI = a.SI;
+  const int imax = I > SI ? I : SI;
+  const int cmax = imax / VALS, qmax = imax / 8;
+  const int nch = (cmax + G - 1) / G;
+  const bool resid = (a.flags & FLINT_RESIDUAL) != 0;
+  const int nmax = decode_max_slots_dev(a) - sh;   // routed slots the table can hold
+
+  // slot table and pair list (wave 0, two slots per lane, S <= 128)
+  if (wave == 0) {
+    const int S = *ws.nslot + sh;
+    uint32_t mraw[2];
+    int eraw[2];
+    float wraw[2][BT];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {             // every load at once, clamped to the table
+      const int r = 2 * lane + h2 - sh;
+      const int rc = r < 0 ? 0 : (r < nmax ? r : nmax - 1);
+      eraw[h2] = ws.slot_expert[rc];
+      mraw[h2] = ws.slot_mask[rc];
+#pragma unroll
+      for (int t = 0; t < BT; ++t) wraw[h2][t] = ws.slot_w[rc * kMaxB + t];
+    }
+    uint32_t msk[2];
+    int cnt[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int s = 2 * lane + h2;
+      const bool is_sh = sh && s == 0;
+      const uint32_t m = s < S ? (is_sh ? (1u << a.B) - 1u : mraw[h2]) : 0u;
+      if (s < S) {
+        s_exp[s] = is_sh ? -1 : eraw[h2];
+        s_msk[s] = m;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) s_wt[s][t] = is_sh ? 1.f : wraw[h2][t];
+      }
+      msk[h2] = m;
+      cnt[h2] = __popc(m);
+    }
+    int incl = cnt[0] + cnt[1];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    int base = incl - cnt[0] - cnt[1];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int s = 2 * lane + h2;
+      if (s < S) s_pb[s] = base;
+      uint32_t m = msk[h2];
+      for (int k = 0; m; ++k, m &= m - 1u) s_pair[base + k] = (uint16_t)((s << 3) | (__ffs(m) - 1));
+      base += cnt[h2];
+    }
+    if (lane == 63) s_np = incl;
+  }
+  // the residual of the rows this thread will write, fetched early (always:
+  // threads without a row read x[0])
+  uint16_t xres_bits;
+  {
+    const int q = threadIdx.x;
+    const int rloc = q / BT, t = q - rloc * BT, n = n0 + rloc;
+    const bool ok = q < RPW * BT && t < a.B && n < H;
+    xres_bits = a.x[ok ? (size_t)t * H + n : 0];
+  }
+  __syncthreads();
+  const int S = *ws.nslot + sh;
+
+  // h rows into LDS.  Thread t copies quad (m, j) = t % qmax of pairs
+  // t / qmax + ppp * k (ppp = NT / qmax pairs per pass, qmax <= NT); every
+  // load and store is made, those past the list reading the first quad and
+  // writing this thread's slot past the largest list.
+  {
+    const int np = s_np;
+    const int ppp = NT / qmax;
+    int rem, j;
+    const int p0 = div_small(threadIdx.x, qmax, 1.0f / (float)qmax, rem);
+    const int m = div_small(rem, cmax, 1.0f / (float)cmax, j);
+    const bool tv = p0 < ppp;
+    const int hdummy = (a.B * (a.K < a.E ? a.K : a.E) + (sh ? a.B : 0)) * qmax + (int)threadIdx.x;
+    const size_t off = (size_t)j * VALS + 8 * m;
+    for (int pb0 = 0; pb0 < np; pb0 += ppp * NHL) {
+      uint4 hv[NHL];
+#pragma unroll
+      for (int k = 0; k < NHL; ++k) {
+        const int p = p0 + pb0 + ppp * k;
+        const bool ok = tv && p < np;
+        const int pr = s_pair[ok ? p : 0];
+        const uint16_t* src = hin + (size_t)(pr >> 3) * h_slot_stride + (size_t)(pr & 7) * h_tok_stride + off;
+        hv[k] = *reinterpret_cast<const uint4*>(ok ? src : hin);
+      }
+#pragma unroll
+      for (int k = 0; k < NHL; ++k) {
+        const int p = p0 + pb0 + ppp * k;
+        s_h[tv && p < np ? p * qmax + rem : hdummy] = hv[k];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Weights of U items (slot, chunk step) per wave.  The item, its expert and
+  // the matrix bases are wave-uniform (scalar); each lane adds fixed 32-bit
+  // offsets of its rows and chunk, taken once.  Every load is made: an item
+  // out of range reads slot 0's first chunk, a chunk past a narrower slot
+  // reads the row's first chunk, and neither is used.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int total = S * nch;
+  uint32_t oc[2][RW], osc[2][RW];                 // [routed, shared] code / scale offsets
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int inter = k == 0 ? I : SI;
+    const uint32_t rowc = WF == FMT_NVFP4 ? (uint32_t)inter / 2 : (uint32_t)inter * 2;
+#pragma unroll
+    for (int rw = 0; rw < RW; ++rw) {
+      const int n = n0 + rw * GPW + grp;
+      const uint32_t nc = n < H ? (uint32_t)n : 0u;
+      oc[k][rw] = nc * rowc + 16u * (uint32_t)li;
+      osc[k][rw] = nc * ((uint32_t)inter / 16) + 2u * (uint32_t)li;
+    }
+  }
+  uint4 raw[U][RW];
+  uint32_t sc[U][RW];
+  int ie[U];
+  float igd[U];
+  auto load_items = [&](int it0) {
+    int sl[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * NW;
+      sl[u] = it < total ? (nch == 1 ? it : it / nch) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) ie[u] = __builtin_amdgcn_readfirstlane(s_exp[sl[u]]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * NW;
+      const int c = it < total ? it - sl[u] * nch : 0;
+      const int e = ie[u];
+      const bool shd = e < 0;
+      const int inter = shd ? SI : I;
+      igd[u] = 1.f;
+      if constexpr (WF == FMT_NVFP4) igd[u] = shd ? a.sh_gscale[2] : a.gscale[3 * e + 2];
+      const bool jok = li + G * c < inter / VALS;
+      const uint8_t* cb;
+      const uint8_t* sb = nullptr;
+      if constexpr (WF == FMT_NVFP4) {
+        cb = shd ? a.sh_d_codes : a.d_codes + (size_t)e * H * (inter / 2);
+        sb = shd ? a.sh_d_scales : a.d_scales + (size_t)e * H * (inter / 16);
+      } else {
+        cb = reinterpret_cast<const uint8_t*>(shd ? a.sh_d_bf16 : a.d_bf16 + (size_t)e * H * inter);
+      }
+      cb += (size_t)16 * G * c;
+      if constexpr (WF == FMT_NVFP4) sb += (size_t)2 * G * c;
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) {
+        const uint32_t o = jok ? (shd ? oc[1][rw] : oc[0][rw]) : 0u;
+        raw[u][rw] = *reinterpret_cast<const uint4*>(cb + o);
+        if constexpr (WF == FMT_NVFP4) {
+          const uint32_t os = jok ? (shd ? osc[1][rw] : osc[0][rw]) : 0u;
+          sc[u][rw] = *reinterpret_cast<const uint16_t*>(sb + os);
+        } else {
+          sc[u][rw] = 0;
+        }
+      }
+    }
+  };
+  load_items(wv);
+
+  float acc[RW][BT];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int t = 0; t < BT; ++t) acc[rw][t] = 0.f;
+  for (int it0 = wv;; ) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * NW;
+      if (it >= total) break;
+      const int s = nch == 1 ? it : it / nch, c = it - s * nch;
+      const int e = ie[u];
+      const int inter = e < 0 ? SI : I;
+      const int j = li + G * c;
+      if (j >= inter / VALS) continue;
+      const uint32_t mask = s_msk[s];
+      const int pb = s_pb[s];
+      const float gd = igd[u];
+      DChunk<WF> d[RW];
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) d[rw] = decode_chunk<WF>(raw[u][rw], sc[u][rw]);
+#pragma unroll
+      for (int t = 0; t < BT; ++t) {
+        if ((mask >> t) & 1u) {
+          const int p = pb + __popc(mask & ((1u << t) - 1u));
+          XChunk<WF> hx;
+#pragma unroll
+          for (int m = 0; m < QPC; ++m) {
+            const uint4 v = s_h[(p * QPC + m) * cmax + j];
+            hx.v[4 * m + 0] = v.x; hx.v[4 * m + 1] = v.y; hx.v[4 * m + 2] = v.z; hx.v[4 * m + 3] = v.w;
+          }
+          const float f = s_wt[s][t] * gd;
+#pragma unroll
+          for (int rw = 0; rw < RW; ++rw) acc[rw][t] = fmaf(f, chunk_dot(d[rw], hx), acc[rw][t]);
+        }
+      }
+    }
+    it0 += NW * U;
+    if (it0 >= total) break;
+    load_items(it0);                               // layers with more items than U per wave
+  }
+
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw)
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      const float v = group_sum<G>(acc[rw][t]);
+      if (li == 0) s_red[wave][rw * GPW + grp][t] = v;
+    }
+  __syncthreads();
+
+  const int q = threadIdx.x;
+  if (q < RPW * BT) {
+    const int rloc = q / BT, t = q - rloc * BT;
+    const int n = n0 + rloc;
+    if (t < a.B && n < H) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += s_red[w][rloc][t];
+      float o = round_bf16(v);
+      if (resid) o = bf16_bits_to_f32(xres_bits) + o;
+      a.out[(size_t)t * H + n] = f32_to_bf16_bits(o);
+    }
+  }
+}
+
 // ------------------------------------------------------------ dispatch ----
 
 inline int pow2ceil(int v) {
@@ -643,6 +1196,90 @@ hipError_t down_dispatch_g(const LayerArgs& a, const DecodeWs& ws, bool dense, i
   }
 }
 
+// Batch kernels: the LDS they stage (activations of up to 8 tokens; h rows
+// of every (slot, token) pair) must fit these bounds, else the per-wave
+// kernels above run.
+constexpr int kBatchXBytes = 64 * 1024;
+constexpr int kBatchHBytes = 96 * 1024;
+
+// Raises a kernel's dynamic LDS limit to the largest size it may be given;
+// each launch template below calls it once, from a function-local static.
+template <typename K>
+bool allow_dynamic_lds(K kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             bytes) == hipSuccess;
+}
+
+// chunk steps of the batch gate/up kernel (64 lanes per row); 0 = not covered
+template <int WF>
+int gate_up_batch_nch(const LayerArgs& a) {
+  const int cpr = a.H / Fmt<WF>::VALS;
+  if (a.B < 2 || cpr < 64 || a.H / 8 > 2 * 256 || a.B * a.H * 2 > kBatchXBytes) return 0;
+  const int nch = (cpr + 63) / 64;
+  return (WF == FMT_NVFP4 ? (nch <= 2) : (nch == 4)) ? nch : 0;
+}
+
+int down_batch_lds(const LayerArgs& a) {
+  const int imax = a.I > a.SI ? a.I : a.SI;
+  const int pairs = a.B * (a.K < a.E ? a.K : a.E) + (a.SI > 0 ? a.B : 0);
+  return pairs * imax * 2;
+}
+
+template <int WF, int NCH, int KQ>
+hipError_t gate_up_batch_launch(const LayerArgs& a, const DecodeWs& ws, uint16_t* hout, int hs, int ht,
+                                int rows, hipStream_t st) {
+  constexpr int NW = 4, P = 2;
+  const int tiles = (rows + NW * P - 1) / (NW * P);
+  const int slots = decode_max_slots({a.H, a.E, a.I, a.SI, a.K, 0, 0.f}, a.B);
+  auto k = gate_up_batch_kernel<WF, P, NW, NCH, KQ>;
+  static const bool lds_ok = allow_dynamic_lds(k, kBatchXBytes + 64 * NW * 16);
+  (void)lds_ok;
+  hipLaunchKernelGGL(k, dim3(tiles, slots), dim3(64 * NW), a.B * a.H * 2 + 64 * NW * 16, st, a, ws, hout, hs,
+                     ht);
+  return hipGetLastError();
+}
+
+template <int CPL>
+hipError_t gate_up_nv_batch_launch(const LayerArgs& a, const DecodeWs& ws, uint16_t* hout, int hs, int ht,
+                                   int rows, hipStream_t st) {
+  constexpr int NW = 8;
+  const int tiles = (rows + NW * 4 - 1) / (NW * 4);
+  const int slots = decode_max_slots({a.H, a.E, a.I, a.SI, a.K, 0, 0.f}, a.B);
+  auto k = gate_up_nv_batch_kernel<NW, CPL>;
+  static const bool lds_ok = allow_dynamic_lds(k, kBatchXBytes + 64 * NW * 16);
+  (void)lds_ok;
+  hipLaunchKernelGGL(k, dim3(tiles, slots), dim3(64 * NW), a.B * a.H * 2 + 64 * NW * 16, st, a, ws, hout, hs,
+                     ht);
+  return hipGetLastError();
+}
+
+template <int WF, int G>
+hipError_t down_batch_dispatch(const LayerArgs& a, const DecodeWs& ws, const uint16_t* hin, int hs, int ht,
+                               hipStream_t st) {
+  constexpr int NW = 8, U = 6;
+  constexpr int RW = (G == 64) ? 4 : 2;
+  constexpr int RPW = RW * (64 / G);
+  const int tiles = (a.H + RPW - 1) / RPW;
+  auto k = down_batch_kernel<WF, G, RW, NW, U>;
+  static const bool lds_ok = allow_dynamic_lds(k, kBatchHBytes + 64 * NW * 16);
+  (void)lds_ok;
+  hipLaunchKernelGGL(k, dim3(tiles), dim3(64 * NW), down_batch_lds(a) + 64 * NW * 16, st, a, ws, hin, hs, ht);
+  return hipGetLastError();
+}
+
+template <int WF>
+hipError_t down_batch_g(const LayerArgs& a, const DecodeWs& ws, const uint16_t* hin, int hs, int ht,
+                        hipStream_t st) {
+  int red = a.I;
+  if (a.SI > 0 && a.SI < red) red = a.SI;
+  switch (lanes_per_row(red / Fmt<WF>::VALS)) {
+    case 8: return down_batch_dispatch<WF, 8>(a, ws, hin, hs, ht, st);
+    case 16: return down_batch_dispatch<WF, 16>(a, ws, hin, hs, ht, st);
+    case 32: return down_batch_dispatch<WF, 32>(a, ws, hin, hs, ht, st);
+    default: return down_batch_dispatch<WF, 64>(a, ws, hin, hs, ht, st);
+  }
+}
+
 template <int BT, bool NORM>
 hipError_t route_dispatch_n(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
   const int nit = (a.H + 511) / 512;
@@ -686,6 +1323,14 @@ hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bo
   if (a.B == 1)
     return bf ? gate_up_dispatch_g<FMT_BF16, 1>(a, ws, dense, norm, hout, hs, ht, imax, st)
               : gate_up_dispatch_g<FMT_NVFP4, 1>(a, ws, dense, norm, hout, hs, ht, imax, st);
+  if (!dense && !norm) {
+    const int kq = a.H / 8 > 256 ? 2 : 1;
+    if (bf && gate_up_batch_nch<FMT_BF16>(a) == 4 && kq == 1)
+      return gate_up_batch_launch<FMT_BF16, 4, 1>(a, ws, hout, hs, ht, imax, st);
+    if (!bf && a.B > 1 && a.B * a.H * 2 <= kBatchXBytes && (a.H == 2048 || a.H == 4096))
+      return a.H == 2048 ? gate_up_nv_batch_launch<4>(a, ws, hout, hs, ht, imax, st)
+                         : gate_up_nv_batch_launch<8>(a, ws, hout, hs, ht, imax, st);
+  }
   return bf ? gate_up_dispatch_g<FMT_BF16, kMaxB>(a, ws, dense, norm, hout, hs, ht, imax, st)
             : gate_up_dispatch_g<FMT_NVFP4, kMaxB>(a, ws, dense, norm, hout, hs, ht, imax, st);
 }
@@ -701,6 +1346,8 @@ hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int d
   if (a.B == 1)
     return bf ? down_dispatch_g<FMT_BF16, 1>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st)
               : down_dispatch_g<FMT_NVFP4, 1>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st);
+  if (!dense && down_batch_lds(a) <= kBatchHBytes && (a.I > a.SI ? a.I : a.SI) / 8 <= 512)
+    return bf ? down_batch_g<FMT_BF16>(a, ws, hin, hs, ht, st) : down_batch_g<FMT_NVFP4>(a, ws, hin, hs, ht, st);
   return bf ? down_dispatch_g<FMT_BF16, kMaxB>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st)
             : down_dispatch_g<FMT_NVFP4, kMaxB>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st);
 }

@@ -31,37 +31,6 @@
 namespace flint {
 namespace {
 
-// x chunk j (32 columns) of the layer input, RMS-normalised when asked
-__device__ __forceinline__ XChunk<FMT_NVFP4> input_chunk(const LayerArgs& a, int j, bool norm, const Rms& rms) {
-  XChunk<FMT_NVFP4> x = load_x<FMT_NVFP4>(a.x, j);
-  if (norm) {
-    const XChunk<FMT_NVFP4> g = load_x<FMT_NVFP4>(a.gamma, j);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float lo = round_bf16(rms_scale_bf16(bf16_lo(x.v[m]), rms) * bf16_lo(g.v[m]));
-      const float hi = round_bf16(rms_scale_bf16(bf16_hi(x.v[m]), rms) * bf16_hi(g.v[m]));
-      x.v[m] = pack_bf16x2(lo, hi);
-    }
-  }
-  return x;
-}
-
-// the 8 input columns c0..c0+7 (a 16-byte segment), RMS-normalised when asked
-__device__ __forceinline__ uint4 input_8(const LayerArgs& a, int c0, bool norm, const Rms& rms) {
-  uint4 v = *reinterpret_cast<const uint4*>(a.x + c0);
-  if (norm) {
-    const uint4 g = *reinterpret_cast<const uint4*>(a.gamma + c0);
-    uint32_t q[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      q[m] = pack_bf16x2(round_bf16(rms_scale_bf16(bf16_lo(q[m]), rms) * bf16_lo(gq[m])),
-                         round_bf16(rms_scale_bf16(bf16_hi(q[m]), rms) * bf16_hi(gq[m])));
-    v = make_uint4(q[0], q[1], q[2], q[3]);
-  }
-  return v;
-}
-
 template <int NCH>
 __device__ __forceinline__ uint32_t gu_finish(const GUItem<NCH>& it, const GURows& R,
                                               const XChunk<FMT_NVFP4>* xc) {
@@ -116,32 +85,57 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   const uint64_t* lw = lw_all + (size_t)rep * lstride;   // this workgroup's copies
   const uint64_t* hw = hw_all + (size_t)rep * hrep;
 
-  // ---- RMS of the token (every wave, from L2) -------------------------------
-  Rms rms{1.0, 1.0};
-  if (norm) {
-    double ss = 0.0;
-    for (int c = 8 * lane; c < H; c += 512) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a.x + c);
-      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const double lo = bf16_lo(q[m]), hi = bf16_hi(q[m]);
-        ss = fma(lo, lo, ss);
-        ss = fma(hi, hi, ss);
-      }
-    }
-    rms = make_rms(sqrt(wave_sum_f64(ss) / (double)H + (double)a.eps));
-  }
+  // ---- the token --------------------------------------------------------------
+  // Lane l holds chunks j = l + 64c (32 columns each) of x: every wave holds
+  // the whole token.  Wave w owns the w-th quarter (8 columns) of each chunk:
+  // it normalises that quarter and dots it with the same columns of its
+  // router rows, so the router never waits on the other waves.  With
+  // RMSNorm the four waves then swap their normalised quarters through LDS.
+  // All loads are issued up front and unconditionally (loads complete in
+  // order: a load issued on one path only would make the compiler wait for
+  // it on the other path too): x, gamma, the first router row, epoch.
+  __shared__ uint4 s_xn[4][64 * NCH];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int e0 = (int)blockIdx.x < E ? (int)blockIdx.x : 0;
+  const uint16_t* gsrc = norm ? a.gamma : a.x;
   XChunk<FMT_NVFP4> xc[NCH];
+  uint4 xq[NCH], gq[NCH], rq[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) xc[c] = input_chunk(a, lane + 64 * c, norm, rms);
+  for (int c = 0; c < NCH; ++c) {                  // this wave's quarter of each chunk
+    const int col = 32 * (lane + 64 * c) + 8 * wv;
+    xq[c] = *reinterpret_cast<const uint4*>(a.x + col);
+    gq[c] = *reinterpret_cast<const uint4*>(gsrc + col);
+    rq[c] = *reinterpret_cast<const uint4*>(a.router + (size_t)e0 * H + col);
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) xc[c] = load_x<FMT_NVFP4>(a.x, lane + 64 * c);
   // the launch epoch: a vector load, so that waiting for it holds up neither
   // the kernel arguments nor the loads above
   const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u + layer;
+  __shared__ double s_ss[4];
+  if (norm) {                                      // this wave's part of sum(x^2)
+    double ss0 = 0.0, ss1 = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t q[4] = {xq[c].x, xq[c].y, xq[c].z, xq[c].w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const double lo = bf16_lo(q[m]), hi = bf16_hi(q[m]);
+        ss0 = fma(lo, lo, ss0);
+        ss1 = fma(hi, hi, ss1);
+      }
+    }
+    const double ssw = wave_sum_f64(ss0 + ss1);
+    if (lane == 0) s_ss[wv] = ssw;
+  }
+  // wait for all first loads here (the epoch is the last of them), before
+  // the loads below that only some waves issue
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) asm volatile("" ::"v"(gq[c].x), "v"(rq[c].x));   // one register per load is enough
+  asm volatile("" ::"v"(epoch));
 
   // ---- phase 1: router quarter rows + shared expert gate/up ------------------
   // expert e is owned by workgroup e % G; its 4 waves take a quarter each
-  const int qlen = H / 4;                          // columns per quarter
   const int nsh_items = has_sh ? SI / 2 : 0;
   // shared items are spread over all workgroups, one per sh_stride waves;
   // when there are fewer items than waves, wave 0 of each workgroup gets
@@ -155,15 +149,30 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   GURows Rsh;
   if (has_sh) Rsh = gu_rows(a, -1);
   if (my_sh) gu_load<NCH>(shit, Rsh, sh_first, H);
+
+  if (norm) {                                      // RMS, then this wave's normalised quarter
+    __syncthreads();
+    const double ss = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+    const Rms rms = make_rms(sqrt(ss / (double)H + (double)a.eps));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      xq[c] = rms_norm_8(xq[c], gq[c], rms);
+      s_xn[wv][lane + 64 * c] = xq[c];
+    }
+  }
   for (int e = blockIdx.x; e < E; e += G) {
+    if (e != (int)blockIdx.x) {                    // grids smaller than E only
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        rq[c] = *reinterpret_cast<const uint4*>(a.router + (size_t)e * H + 32 * (lane + 64 * c) + 8 * wv);
+    }
     float part = 0.f;
-    for (int c0 = wave * qlen + 8 * lane; c0 < (wave + 1) * qlen; c0 += 512) {
-      const uint4 w = *reinterpret_cast<const uint4*>(a.router + (size_t)e * H + c0);
-      const uint4 xq = input_8(a, c0, norm, rms);
-      part = dot2_bf16(w.x, xq.x, part);
-      part = dot2_bf16(w.y, xq.y, part);
-      part = dot2_bf16(w.z, xq.z, part);
-      part = dot2_bf16(w.w, xq.w, part);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      part = dot2_bf16(rq[c].x, xq[c].x, part);
+      part = dot2_bf16(rq[c].y, xq[c].y, part);
+      part = dot2_bf16(rq[c].z, xq[c].z, part);
+      part = dot2_bf16(rq[c].w, xq[c].w, part);
     }
     part = group_sum<64>(part);
     if (lane == 0) s_logit_part[wave] = part;
@@ -173,6 +182,16 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
       put_word_all(lw_all, lstride, e, epoch, __float_as_uint(l));
     }
     __syncthreads();
+  }
+  if (norm) {                                      // the normalised token, from the four waves
+    if ((int)blockIdx.x >= E) __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint4 v = s_xn[w][lane + 64 * c];
+        xc[c].v[4 * w + 0] = v.x; xc[c].v[4 * w + 1] = v.y; xc[c].v[4 * w + 2] = v.z; xc[c].v[4 * w + 3] = v.w;
+      }
   }
   announce_arrival(ws, E, epoch);
   if (my_sh) put_word_all(hw_all, hrep, sh_first, epoch, gu_finish<NCH>(shit, Rsh, xc));

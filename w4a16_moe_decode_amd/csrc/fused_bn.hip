@@ -238,14 +238,7 @@ void fused_decode_bn_kernel(LayerArgs a, DecodeWs ws) {
       uint4* px = reinterpret_cast<uint4*>(s_x + t * Hw + c / 2);
       const uint4 v = *px;
       const Rms rms = make_rms(s_rms[t]);
-      const uint4 g = gv[i];
-      uint32_t xq[4] = {v.x, v.y, v.z, v.w};
-      const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        xq[m] = pack_bf16x2(round_bf16(rms_scale_bf16(bf16_lo(xq[m]), rms) * bf16_lo(gq[m])),
-                            round_bf16(rms_scale_bf16(bf16_hi(xq[m]), rms) * bf16_hi(gq[m])));
-      *px = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+      *px = rms_norm_8(v, gv[i], rms);
     }
     __syncthreads();
   }

@@ -278,14 +278,7 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(LayerArgs a, PrefillW
   for (int c = 8 * lane; c < H; c += 512) {
     const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
     const uint4 g = *reinterpret_cast<const uint4*>(a.gamma + c);
-    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t gq[4] = {g.x, g.y, g.z, g.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      o[m] = pack_bf16x2(round_bf16(rms_scale_bf16(bf16_lo(q[m]), rms) * bf16_lo(gq[m])),
-                         round_bf16(rms_scale_bf16(bf16_hi(q[m]), rms) * bf16_hi(gq[m])));
-    *reinterpret_cast<uint4*>(ws.xn + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(ws.xn + (size_t)t * H + c) = rms_norm_8(v, g, rms);
   }
 }
 
