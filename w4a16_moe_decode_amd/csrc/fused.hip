@@ -59,8 +59,32 @@ __device__ __forceinline__ uint32_t gu_finish(const GUItem<NCH>& it, const GURow
 // row-sets per workgroup (DW * GPW rows), chunk steps of GD lanes.  Layer
 // `layer` of a launch tags its hand-off words with the stored epoch + 1 +
 // layer; the epoch it used is returned.  a.x and a.out may point to LDS.
-template <int NCH, int GD, int DW, int MAXS>
-__device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const DecodeWs& ws, uint32_t layer) {
+// A layer's first loads that do not depend on its input: this wave's
+// quarter of gamma and of its first router row, and the launch epoch.  A
+// stack of layers issues them for layer l + 1 while it waits for layer l's
+// output rows.
+template <int NCH>
+struct LayerPre {
+  uint4 gq[NCH], rq[NCH];
+  uint32_t epoch0;                                 // the stored epoch
+};
+
+template <int NCH>
+__device__ __forceinline__ void layer_prefetch(LayerPre<NCH>& p, const uint16_t* gamma, const uint16_t* router,
+                                               int H, int E) {
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e0 = (int)blockIdx.x < E ? (int)blockIdx.x : 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = 32 * (lane + 64 * c) + 8 * wv;
+    p.gq[c] = *reinterpret_cast<const uint4*>(gamma + col);
+    p.rq[c] = *reinterpret_cast<const uint4*>(router + (size_t)e0 * H + col);
+  }
+}
+
+template <int NCH, int GD, int DW, int MAXS, bool PRE>
+__device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const DecodeWs& ws, uint32_t layer,
+                                                   const LayerPre<NCH>& pre) {
   constexpr int GPW = 64 / GD;
   constexpr int DROWS = DW * GPW;                 // output rows per workgroup
   constexpr int IMAXW = 2048 / 2;                 // h words per slot held in LDS (I <= 2048)
@@ -104,14 +128,20 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   for (int c = 0; c < NCH; ++c) {                  // this wave's quarter of each chunk
     const int col = 32 * (lane + 64 * c) + 8 * wv;
     xq[c] = *reinterpret_cast<const uint4*>(a.x + col);
-    gq[c] = *reinterpret_cast<const uint4*>(gsrc + col);
-    rq[c] = *reinterpret_cast<const uint4*>(a.router + (size_t)e0 * H + col);
+    if constexpr (PRE) {
+      gq[c] = pre.gq[c];
+      rq[c] = pre.rq[c];
+    } else {
+      gq[c] = *reinterpret_cast<const uint4*>(gsrc + col);
+      rq[c] = *reinterpret_cast<const uint4*>(a.router + (size_t)e0 * H + col);
+    }
   }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) xc[c] = load_x<FMT_NVFP4>(a.x, lane + 64 * c);
   // the launch epoch: a vector load, so that waiting for it holds up neither
   // the kernel arguments nor the loads above
-  const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u + layer;
+  const uint32_t epoch =
+      (PRE ? pre.epoch0 : __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u + layer;
   __shared__ double s_ss[4];
   if (norm) {                                      // this wave's part of sum(x^2)
     double ss0 = 0.0, ss1 = 0.0;
@@ -401,7 +431,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
 
 template <int NCH, int GD, int DW, int MAXS>
 __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, DecodeWs ws) {
-  const uint32_t epoch = fused_layer_b1<NCH, GD, DW, MAXS>(a, ws, 0);
+  const LayerPre<NCH> none{};
+  const uint32_t epoch = fused_layer_b1<NCH, GD, DW, MAXS, false>(a, ws, 0, none);
   // ---- advance the epoch for the next launch -----------------------------------
   // Every workgroup published a router logit or an arrival word tagged with
   // the epoch it read at its start, and workgroup 0 has seen all of them
@@ -432,6 +463,11 @@ __global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa, Decod
   const size_t xrep = (size_t)H / 2;
   for (int q = threadIdx.x; q < H / 8; q += 256)
     reinterpret_cast<uint4*>(s_x)[q] = reinterpret_cast<const uint4*>(sa.x_in)[q];
+  // layer 0's input-independent first loads (layer l + 1's are issued at the
+  // end of layer l, before its output rows are exchanged)
+  LayerPre<NCH> pre;
+  pre.epoch0 = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  layer_prefetch<NCH>(pre, sa.gammas, static_cast<const uint16_t*>(sa.layers[0].router), H, sa.base.E);
   __syncthreads();
   uint32_t epoch = 0;
   for (int l = 0; l < sa.L; ++l) {
@@ -453,7 +489,10 @@ __global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa, Decod
     a.out = s_xo;
     a.topk_idx = sa.topk_idx + (size_t)l * K;
     a.topk_w = sa.topk_w + (size_t)l * K;
-    epoch = fused_layer_b1<NCH, GD, DW, MAXS>(a, ws, (uint32_t)l);
+    epoch = fused_layer_b1<NCH, GD, DW, MAXS, true>(a, ws, (uint32_t)l, pre);
+    if (l + 1 < sa.L)
+      layer_prefetch<NCH>(pre, sa.gammas + (size_t)(l + 1) * H,
+                          static_cast<const uint16_t*>(sa.layers[l + 1].router), H, sa.base.E);
     __syncthreads();                               // this workgroup's rows of x_{l+1} are in s_xo
     if (sa.layer_out)
       for (int r = threadIdx.x; r < DROWS; r += 256)
