@@ -340,14 +340,15 @@ __global__ __launch_bounds__(1024) void prefill_topk_kernel(LayerArgs a, Prefill
                          : 0ull;
     }
   }
+  // the TPW tokens of a wave take their K rounds together (four independent
+  // chains of wave reductions, so their latencies overlap)
+  float my_s[TPW], ssum[TPW];
+  int my_e[TPW];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int j = wave * TPW + u;
-    const int t = c * CHUNK + j;
-    if (t >= T) break;
-    float my_s = 0.f, ssum = 0.f;
-    int my_e = 0;
-    for (int k = 0; k < K; ++k) {
+  for (int u = 0; u < TPW; ++u) { my_s[u] = 0.f; ssum[u] = 0.f; my_e[u] = 0; }
+  for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
       uint64_t m = key[u][0];
 #pragma unroll
       for (int q = 1; q < 4; ++q) m = key[u][q] > m ? key[u][q] : m;
@@ -356,13 +357,18 @@ __global__ __launch_bounds__(1024) void prefill_topk_kernel(LayerArgs a, Prefill
       for (int q = 0; q < 4; ++q)
         if (key[u][q] == m) key[u][q] = 0ull;
       const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
-      ssum += sg;
-      if (lane == k) { my_s = sg; my_e = (int)~(uint32_t)m; }
+      ssum[u] += sg;
+      if (lane == k) { my_s[u] = sg; my_e[u] = (int)~(uint32_t)m; }
     }
-    if (lane < K) {
-      a.topk_idx[(size_t)t * K + lane] = my_e;
-      a.topk_w[(size_t)t * K + lane] = renorm ? my_s / ssum : my_s;
-      atomicOr(&s_mask[my_e], 1ull << j);
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int j = wave * TPW + u;
+    const int t = c * CHUNK + j;
+    if (t < T && lane < K) {
+      a.topk_idx[(size_t)t * K + lane] = my_e[u];
+      a.topk_w[(size_t)t * K + lane] = renorm ? my_s[u] / ssum[u] : my_s[u];
+      atomicOr(&s_mask[my_e[u]], 1ull << j);
     }
   }
   __syncthreads();
@@ -374,62 +380,78 @@ __global__ __launch_bounds__(1024) void prefill_topk_kernel(LayerArgs a, Prefill
 }
 
 // ------------------------------------------------------------------ scan --
-// One workgroup: per-expert counts and offsets, per-chunk bases (the counts
-// the top-k kernel left in cbase are replaced by exclusive prefixes), tile
-// list.  Loads are issued 16 chunks at a time.
-__global__ __launch_bounds__(256) void prefill_scan_kernel(LayerArgs a, PrefillWs ws, int T) {
+// One workgroup of 1024 threads: thread (part, e) sums the counts of expert e
+// over its quarter of the chunks (all loads of a pass in flight together),
+// the parts and then the experts are scanned through LDS and wave prefix
+// sums, and a second pass writes every chunk's base (the counts the top-k
+// kernel left in cbase become bases).  Then the tile list.
+__global__ __launch_bounds__(1024) void prefill_scan_kernel(LayerArgs a, PrefillWs ws, int T) {
+  constexpr int NB = 32;                           // chunk loads per thread per batch
+  __shared__ int s_cnt[4][FLINT_MAX_EXPERTS];
   __shared__ int s_part[4];
   const int E = a.E, C = (T + CHUNK - 1) / CHUNK;
-  const int e = threadIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool has_sh = a.SI > 0;
+  const int cpp = (C + 3) / 4, c_lo = part * cpp, c_hi = min(C, c_lo + cpp);
   int cnt = 0;
   if (e < E) {
-    for (int c0 = 0; c0 < C; c0 += 16) {
-      int v[16];
+    for (int c0 = c_lo; c0 < c_hi; c0 += NB) {
+      int v[NB];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = c0 + u < C ? ws.cbase[(size_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < NB; ++u) v[u] = ws.cbase[(size_t)(c0 + u < c_hi ? c0 + u : c_lo) * E + e];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int here = cnt;
-        cnt += v[u];
-        v[u] = here;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (c0 + u < C) ws.cbase[(size_t)(c0 + u) * E + e] = v[u];
+      for (int u = 0; u < NB; ++u) cnt += c0 + u < c_hi ? v[u] : 0;
     }
   }
-  // exclusive scan of counts over experts (256 threads = 4 waves)
-  int incl = cnt;
+  s_cnt[part][e] = cnt;
+  __syncthreads();
+  // expert totals and the exclusive scan over experts (first 256 threads)
+  int total_e = 0, before_part = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int v = s_cnt[q][e];
+    if (q < part) before_part += v;
+    total_e += v;
+  }
+  if (e >= E) total_e = 0;
+  int incl = total_e;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int v = __shfl_up(incl, off, 64);
     if (lane >= off) incl += v;
   }
-  if (lane == 63) s_part[wave] = incl;
+  if (part == 0 && lane == 63) s_part[wave] = incl;
   __syncthreads();
   int before = 0;
-  for (int w = 0; w < wave; ++w) before += s_part[w];
-  const int offset = before + incl - cnt;
+  for (int w = 0; w < (wave & 3); ++w) before += s_part[w];
+  const int offset = before + incl - total_e;     // expert e's first permuted position
+  const int total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   if (e < E) {
-    ws.counts[e] = cnt;
-    ws.offsets[e] = offset;
-    for (int c0 = 0; c0 < C; c0 += 16) {
-      int v[16];
+    if (part == 0) {
+      ws.counts[e] = total_e;
+      ws.offsets[e] = offset;
+    }
+    int run = offset + before_part;
+    for (int c0 = c_lo; c0 < c_hi; c0 += NB) {
+      int v[NB];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = c0 + u < C ? ws.cbase[(size_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < NB; ++u) v[u] = ws.cbase[(size_t)(c0 + u < c_hi ? c0 + u : c_lo) * E + e];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (c0 + u < C) ws.cbase[(size_t)(c0 + u) * E + e] = v[u] + offset;
+      for (int u = 0; u < NB; ++u) {
+        if (c0 + u < c_hi) {
+          ws.cbase[(size_t)(c0 + u) * E + e] = run;
+          run += v[u];
+        }
+      }
     }
   }
-  const int total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   if (threadIdx.x == 0) {
     ws.offsets[E] = total;
     ws.counts[E] = has_sh ? T : 0;
   }
   // tile list: routed groups in expert order, then the shared group
-  const int nt = e < E ? (cnt + BM - 1) / BM : 0;
+  const int nt = (part == 0 && e < E) ? (total_e + BM - 1) / BM : 0;
   int tincl = nt;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -437,15 +459,15 @@ __global__ __launch_bounds__(256) void prefill_scan_kernel(LayerArgs a, PrefillW
     if (lane >= off) tincl += v;
   }
   __syncthreads();
-  if (lane == 63) s_part[wave] = tincl;
+  if (part == 0 && lane == 63) s_part[wave] = tincl;
   __syncthreads();
   int tbefore = 0;
-  for (int w = 0; w < wave; ++w) tbefore += s_part[w];
+  for (int w = 0; w < (wave & 3); ++w) tbefore += s_part[w];
   const int tfirst = tbefore + tincl - nt;
   for (int i = 0; i < nt; ++i) ws.tiles[tfirst + i] = make_int2(e, i * BM);
   const int routed_tiles = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   const int sh_tiles = has_sh ? (T + BM - 1) / BM : 0;
-  for (int i = threadIdx.x; i < sh_tiles; i += 256) ws.tiles[routed_tiles + i] = make_int2(E, i * BM);
+  for (int i = threadIdx.x; i < sh_tiles; i += 1024) ws.tiles[routed_tiles + i] = make_int2(E, i * BM);
   if (threadIdx.x == 0) *ws.ntiles = routed_tiles + sh_tiles;
 }
 
@@ -683,7 +705,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
                      st, a, ws, T, xin);
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(1024), 0, st, a, ws, T);
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(256), 0, st, a, ws, T);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
   const dim3 ggu(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2));
   const dim3 gdn(ws.max_tiles, (a.H + BN - 1) / BN);
