@@ -205,6 +205,174 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
   }
 }
 
+// ------------------------------------------------------ route, batch 2..8 --
+// One workgroup per routed expert; wave w takes the w-th quarter of the row
+// (8 columns per lane), so every load of the kernel -- its router quarter,
+// every token's matching quarter, γ -- is one 16-byte load per lane, all
+// issued at once and unconditionally (tokens past the batch re-read token
+// 0).  With RMSNorm each wave adds its quarter's squares (float64) and the
+// four are combined through LDS.  A logit is the sum of the four quarter
+// sums in wave order, with the same per-lane order as the single-launch
+// batch kernel, so both produce the same logits bit for bit.  Workgroup 0
+// then polls every logit word (no ticket: the other workgroups' words carry
+// this call's epoch, read before they were written), selects the top-k of
+// every token, writes the expert set and advances the epoch.
+template <int NQ, bool NORM>
+__global__ __launch_bounds__(256) void route_batch_kernel(LayerArgs a, DecodeWs ws) {
+  constexpr int BT = kMaxB;
+  __shared__ float s_part[4][BT];
+  __shared__ double s_ss[4][BT];
+  __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
+  __shared__ float s_w[FLINT_MAX_EXPERTS][kMaxB];
+  __shared__ int s_wcnt[4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int H = a.H, B = a.B, E = a.E;
+  const int e = blockIdx.x;
+  const int qlen = H / 4, q0 = wave * qlen;
+  uint4 rv[NQ], gv[NQ], xv[BT][NQ];
+  bool okc[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int off = 8 * lane + 512 * i;
+    okc[i] = off < qlen;
+    const int col = q0 + (okc[i] ? off : 0);
+    rv[i] = *reinterpret_cast<const uint4*>(a.router + (size_t)e * H + col);
+    if constexpr (NORM) gv[i] = *reinterpret_cast<const uint4*>(a.gamma + col);
+#pragma unroll
+    for (int t = 0; t < BT; ++t) xv[t][i] = *reinterpret_cast<const uint4*>(a.x + (size_t)(t < B ? t : 0) * H + col);
+  }
+  // the launch epoch (a vector load behind the others)
+  const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      double ss0 = 0.0, ss1 = 0.0;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        if (!okc[i]) continue;
+        const uint32_t q[4] = {xv[t][i].x, xv[t][i].y, xv[t][i].z, xv[t][i].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const double lo = bf16_lo(q[m]), hi = bf16_hi(q[m]);
+          ss0 = fma(lo, lo, ss0);
+          ss1 = fma(hi, hi, ss1);
+        }
+      }
+      const double ssw = wave_sum_f64(ss0 + ss1);
+      if (lane == 0) s_ss[wave][t] = ssw;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+      const double ss = (s_ss[0][t] + s_ss[1][t]) + (s_ss[2][t] + s_ss[3][t]);
+      const Rms rms = make_rms(sqrt(ss / (double)H + (double)a.eps));
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        xv[t][i] = rms_norm_8(xv[t][i], gv[i], rms);
+        if (e == 0 && t < B && okc[i])
+          *reinterpret_cast<uint4*>(ws.xn + (size_t)t * H + q0 + 8 * lane + 512 * i) = xv[t][i];
+      }
+    }
+  }
+  float part[BT];
+#pragma unroll
+  for (int t = 0; t < BT; ++t) {
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      if (!okc[i]) continue;
+      p = dot2_bf16(rv[i].x, xv[t][i].x, p);
+      p = dot2_bf16(rv[i].y, xv[t][i].y, p);
+      p = dot2_bf16(rv[i].z, xv[t][i].z, p);
+      p = dot2_bf16(rv[i].w, xv[t][i].w, p);
+    }
+    part[t] = group_sum<64>(p);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < BT; ++t) s_part[wave][t] = part[t];
+  }
+  __syncthreads();
+  if (wave == 0 && lane < B) {
+    const float l = s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
+    __hip_atomic_store(ws.logit_words + (size_t)lane * E + e, ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(l),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (blockIdx.x != 0) return;
+
+  // ---- workgroup 0: top-k per token (tokens w and w + 4 on wave w)
+  for (int q = threadIdx.x; q < FLINT_MAX_EXPERTS; q += 256) {
+    s_mask[q] = 0u;
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) s_w[q][t] = 0.f;
+  }
+  __syncthreads();
+  const bool renorm = (a.flags & FLINT_RENORM) != 0;
+  {
+    uint64_t wd[8];
+    const uint64_t* ptr[8];
+    bool ok[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = wave + 4 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ex = lane + 64 * q;
+        ok[4 * h + q] = t < B && ex < E;
+        ptr[4 * h + q] = ws.logit_words + (size_t)(t < B ? t : 0) * E + (ex < E ? ex : 0);
+      }
+    }
+    poll_words<8>(wd, ptr, ok, epoch, ws.error);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = wave + 4 * h;
+      if (t >= B) break;                            // the same in every lane
+      uint64_t key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ex = lane + 64 * q;
+        key[q] = ok[4 * h + q] ? (((uint64_t)float_order_key(__uint_as_float((uint32_t)wd[4 * h + q])) << 32) |
+                                  (uint32_t)~(uint32_t)ex)
+                               : 0ull;
+      }
+      const uint64_t my_key = select_topk(key, a.K);
+      const int my_e = (int)~(uint32_t)my_key;
+      const float my_s = lane < a.K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
+      float ssum = 0.f;
+      for (int k = 0; k < a.K; ++k)                 // selection order
+        ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+      if (lane < a.K) {
+        const float w = renorm ? my_s / ssum : my_s;
+        a.topk_idx[t * a.K + lane] = my_e;
+        a.topk_w[t * a.K + lane] = w;
+        atomicOr(&s_mask[my_e], 1u << t);
+        s_w[my_e][t] = w;
+      }
+    }
+  }
+  __syncthreads();
+
+  // routed slots = the selected experts in ascending index order
+  const int ex = threadIdx.x;
+  const uint32_t m = ex < E ? s_mask[ex] : 0u;
+  const unsigned long long bal = __ballot(m != 0u);
+  if (lane == 0) s_wcnt[wave] = __popcll(bal);
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wcnt[w];
+  if (m != 0u) {
+    const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+    ws.slot_expert[pos] = ex;
+    ws.slot_mask[pos] = m;
+#pragma unroll
+    for (int t = 0; t < kMaxB; ++t) ws.slot_w[pos * kMaxB + t] = s_w[ex][t];
+  }
+  if (threadIdx.x == 0) {
+    *ws.nslot = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+    *ws.epoch = epoch;
+  }
+}
+
 // -------------------------------------------------------------- weights ----
 
 // Row pointers of one matrix of the selected expert.
@@ -1309,7 +1477,20 @@ int decode_max_slots(const flint_moe_shape& s, int batch) {
 }
 
 hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
-  return a.B == 1 ? route_dispatch<1>(a, ws, st) : route_dispatch<kMaxB>(a, ws, st);
+  if (a.B == 1) return route_dispatch<1>(a, ws, st);
+  const bool norm = (a.flags & FLINT_PRE_RMSNORM) != 0;
+  const int nq = (a.H / 4 + 511) / 512;            // 16-byte loads per lane per quarter row
+  if (a.E <= FLINT_MAX_EXPERTS && nq <= 2) {
+    if (nq == 1) {
+      if (norm) hipLaunchKernelGGL((route_batch_kernel<1, true>), dim3(a.E), dim3(256), 0, st, a, ws);
+      else hipLaunchKernelGGL((route_batch_kernel<1, false>), dim3(a.E), dim3(256), 0, st, a, ws);
+    } else {
+      if (norm) hipLaunchKernelGGL((route_batch_kernel<2, true>), dim3(a.E), dim3(256), 0, st, a, ws);
+      else hipLaunchKernelGGL((route_batch_kernel<2, false>), dim3(a.E), dim3(256), 0, st, a, ws);
+    }
+    return hipGetLastError();
+  }
+  return route_dispatch<kMaxB>(a, ws, st);
 }
 
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm,
