@@ -191,6 +191,30 @@ __device__ __forceinline__ XChunk<WF> load_x(const uint16_t* row, int j) {
   return x;
 }
 
+// Load of a T from device memory through a global-qualified pointer.  For
+// pointers the compiler cannot trace to a kernel argument (read from an
+// array of per-layer pointers, say) a plain dereference becomes a flat load,
+// which counts against the LDS counter too, so every later LDS read would
+// wait for it.
+template <class T>
+__device__ __forceinline__ T ldg(const void* p) {
+  typedef __attribute__((address_space(1))) const T GT;
+  return *(GT*)p;
+}
+// uint4's copy constructor takes a generic reference, so 16 bytes are loaded
+// as a native vector
+template <>
+__device__ __forceinline__ uint4 ldg<uint4>(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const v4u GV;
+  const v4u v = *(GV*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt 0 and leaves
+// expcnt and lgkmcnt unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------- wave reductions --
 
 template <int CTRL>

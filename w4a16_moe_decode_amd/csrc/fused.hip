@@ -77,8 +77,8 @@ __device__ __forceinline__ void layer_prefetch(LayerPre<NCH>& p, const uint16_t*
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int col = 32 * (lane + 64 * c) + 8 * wv;
-    p.gq[c] = *reinterpret_cast<const uint4*>(gamma + col);
-    p.rq[c] = *reinterpret_cast<const uint4*>(router + (size_t)e0 * H + col);
+    p.gq[c] = ldg<uint4>(gamma + col);
+    p.rq[c] = ldg<uint4>(router + (size_t)e0 * H + col);
   }
 }
 
@@ -92,6 +92,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   __shared__ int s_exp[MAXS];
   __shared__ float s_w[MAXS];
   __shared__ int s_nU;
+  __shared__ int s_sel_e[MAXS];
+  __shared__ float s_sel_w[MAXS];
   __shared__ uint32_t s_h[MAXS][IMAXW];           // h of every slot, packed BF16 pairs
   __shared__ float s_red[4][DROWS];
 
@@ -194,7 +196,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     if (e != (int)blockIdx.x) {                    // grids smaller than E only
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        rq[c] = *reinterpret_cast<const uint4*>(a.router + (size_t)e * H + 32 * (lane + 64 * c) + 8 * wv);
+        rq[c] = ldg<uint4>(a.router + (size_t)e * H + 32 * (lane + 64 * c) + 8 * wv);
     }
     float part = 0.f;
 #pragma unroll
@@ -279,10 +281,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     if (lane < K) {
       s_exp[sh + rank] = my_e;
       s_w[sh + rank] = w;
-      if (blockIdx.x == 0) {
-        a.topk_idx[lane] = my_e;
-        a.topk_w[lane] = w;
-      }
+      s_sel_e[lane] = my_e;                        // selection order, for the top-k outputs
+      s_sel_w[lane] = w;
     }
     if (lane == 0) {
       s_nU = K;
@@ -290,6 +290,14 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     }
   }
   __syncthreads();
+  // Nothing this wave loaded earlier is still in flight here (every earlier
+  // load was consumed, every store long acknowledged), but loads issued on
+  // one path only (the shared expert's rows and tensor scales) would leave
+  // the compiler believing so: it then waits for the memory counter to drop
+  // to a small number in the middle of the weight loads below, i.e. for the
+  // first item's rows to arrive before the second item's and the down rows
+  // are requested.  An explicit wait for zero clears that state for free.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   const int nU = s_nU, S = nU + sh;
 
   // ---- phase 3: routed gate/up items (round-robin over all waves) ------------
@@ -337,8 +345,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
       const bool okr = ok && n < H;
       const uint8_t* cp = okr ? codes + (size_t)n * (inter / 2) + 16 * j : a.d_codes;
       const uint8_t* sp = okr ? scales + (size_t)n * (inter / 16) + 2 * j : a.d_scales;
-      draw[u][rw] = *reinterpret_cast<const uint4*>(cp);
-      dsc[u][rw] = *reinterpret_cast<const uint16_t*>(sp);
+      draw[u][rw] = ldg<uint4>(cp);
+      dsc[u][rw] = ldg<uint16_t>(sp);
     }
   }
 
@@ -406,7 +414,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     XChunk<FMT_NVFP4> hx;
 #pragma unroll
     for (int m = 0; m < 16; ++m) hx.v[m] = s_h[s][16 * j + m];
-    const float f = s_w[s] * (e < 0 ? a.sh_gscale[2] : a.gscale[3 * e + 2]);
+    const float f = s_w[s] * ldg<float>(e < 0 ? a.sh_gscale + 2 : a.gscale + 3 * e + 2);
 #pragma unroll
     for (int rw = 0; rw < DW; ++rw) acc[rw] = fmaf(f, chunk_dot(decode_nvfp4(draw[u][rw], dsc[u][rw]), hx), acc[rw]);
   }
@@ -424,6 +432,10 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
       if (resid) o = xres + o;
       a.out[n] = f32_to_bf16_bits(o);
     }
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < K) {  // the top-k outputs, off the critical path
+    a.topk_idx[threadIdx.x] = s_sel_e[threadIdx.x];
+    a.topk_w[threadIdx.x] = s_sel_w[threadIdx.x];
   }
 
   return epoch;

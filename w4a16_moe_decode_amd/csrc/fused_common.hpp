@@ -74,13 +74,13 @@ __device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert /* -1 =
     const size_t mc = (size_t)a.SI * H / 2, ms = (size_t)a.SI * H / 16;
     r.gc = a.sh_gu_codes; r.uc = a.sh_gu_codes + mc;
     r.gs = a.sh_gu_scales; r.us = a.sh_gu_scales + ms;
-    r.g_scale = a.sh_gscale[0]; r.u_scale = a.sh_gscale[1];
+    r.g_scale = ldg<float>(a.sh_gscale); r.u_scale = ldg<float>(a.sh_gscale + 1);
   } else {
     r.inter = a.I;
     const size_t mc = (size_t)a.I * H / 2, ms = (size_t)a.I * H / 16;
     r.gc = a.gu_codes + (size_t)(2 * expert) * mc; r.uc = r.gc + mc;
     r.gs = a.gu_scales + (size_t)(2 * expert) * ms; r.us = r.gs + ms;
-    r.g_scale = a.gscale[3 * expert]; r.u_scale = a.gscale[3 * expert + 1];
+    r.g_scale = ldg<float>(a.gscale + 3 * expert); r.u_scale = ldg<float>(a.gscale + 3 * expert + 1);
   }
   return r;
 }
@@ -103,10 +103,10 @@ __device__ __forceinline__ void gu_load(GUItem<NCH>& it, const GURows& R, int p,
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int j = lane + 64 * c;
-      it.c[rr][0][c] = reinterpret_cast<const uint4*>(R.gc + (size_t)row * (H / 2))[j];
-      it.s[rr][0][c] = reinterpret_cast<const uint16_t*>(R.gs + (size_t)row * (H / 16))[j];
-      it.c[rr][1][c] = reinterpret_cast<const uint4*>(R.uc + (size_t)row * (H / 2))[j];
-      it.s[rr][1][c] = reinterpret_cast<const uint16_t*>(R.us + (size_t)row * (H / 16))[j];
+      it.c[rr][0][c] = ldg<uint4>(R.gc + (size_t)row * (H / 2) + 16 * j);
+      it.s[rr][0][c] = ldg<uint16_t>(R.gs + (size_t)row * (H / 16) + 2 * j);
+      it.c[rr][1][c] = ldg<uint4>(R.uc + (size_t)row * (H / 2) + 16 * j);
+      it.s[rr][1][c] = ldg<uint16_t>(R.us + (size_t)row * (H / 16) + 2 * j);
     }
   }
 }
