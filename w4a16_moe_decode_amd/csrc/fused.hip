@@ -15,7 +15,8 @@
 //   phase 2  every workgroup waits for all logits, selects the top-k itself
 //            and issues the loads of its own down rows of all selected
 //            experts (they do not depend on h)
-//   phase 3  routed gate/up rows (work dealt round-robin over all waves)
+//   phase 3  routed gate/up rows (an equal share of row pairs per
+//            workgroup, dealt round-robin over its waves)
 //   phase 4  every workgroup waits for the h values it needs, then computes
 //            its output rows: weighted combine of the selected experts and
 //            the shared expert, one BF16 rounding (+ residual)
@@ -92,6 +93,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   __shared__ int s_exp[MAXS];
   __shared__ float s_w[MAXS];
   __shared__ int s_nU;
+  __shared__ uint64_t s_key[MAXS];
   __shared__ int s_sel_e[MAXS];
   __shared__ float s_sel_w[MAXS];
   __shared__ uint32_t s_h[MAXS][IMAXW];           // h of every slot, packed BF16 pairs
@@ -256,19 +258,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
                        : 0ull;
       }
     }
-    // each lane sorts its four keys (descending); a round then takes the
-    // wave maximum of the lanes' heads and the winning lane pops its head
-#define FLINT_CSWAP(i, j) { const uint64_t hi_ = key[i] > key[j] ? key[i] : key[j]; \
-                            const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
-    FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
-#undef FLINT_CSWAP
-    // K rounds; lane k keeps the k-th selected key
-    uint64_t my_key = 0ull;
-    for (int k = 0; k < K; ++k) {
-      const uint64_t m = wave_max_key(key[0]);
-      if (key[0] == m) { key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull; }
-      if (lane == k) my_key = m;
-    }
+    topk_keys_to_lds(key, K, s_key);
+    const uint64_t my_key = lane < K ? s_key[lane] : 0ull;   // lane k: the k-th selected key
     const int my_e = (int)~(uint32_t)my_key;
     const float my_s = lane < K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
     float ssum = 0.f;
@@ -300,16 +291,24 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   const int nU = s_nU, S = nU + sh;
 
-  // ---- phase 3: routed gate/up items (round-robin over all waves) ------------
-  // The first round's loads (items gw and gw + NWV) are issued before the
-  // down-row prefetch: loads complete in order, so finishing these items then
-  // waits only on their own rows while the prefetch stays in flight.
+  // ---- phase 3: routed gate/up items -----------------------------------------
+  // Workgroup g takes items [g q, g q + q), q = ceil(items / workgroups), so
+  // every workgroup streams the same number of rows (dealing the items
+  // round-robin over all waves of the grid gave half of the workgroups twice
+  // the rows of the others, and the last of them set the time of the h
+  // exchange); its waves take them round-robin.  The first round's loads
+  // (rounds 0 and 1) are issued before the down-row prefetch: loads complete
+  // in order, so finishing these items then waits only on their own rows
+  // while the prefetch stays in flight.
   const int ipw = I / 2;                           // items per routed slot
   const int nitems = nU * ipw;
+  const int iq = (nitems + G - 1) / G;
+  const int ibase = blockIdx.x * iq;
+  const int iend = ibase + iq < nitems ? ibase + iq : nitems;
   GUItem<NCH> A, B;
-  const int itB = gw + NWV;
-  const bool hasA = gw < nitems, hasB = itB < nitems;
-  const int rA = hasA ? gw / ipw : 0, pA = hasA ? gw - rA * ipw : 0;
+  const int itA = ibase + wave, itB = itA + 4;
+  const bool hasA = itA < iend, hasB = itB < iend;
+  const int rA = hasA ? itA / ipw : 0, pA = hasA ? itA - rA * ipw : 0;
   const int rB = hasB ? itB / ipw : 0, pB = hasB ? itB - rB * ipw : 0;
   const GURows RA = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rA]));
   const GURows RB = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rB]));
@@ -352,14 +351,14 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
 
   if (hasA) put_word_all(hw_all, hrep, (size_t)(sh + rA) * hstride + pA, epoch, gu_finish<NCH>(A, RA, xc));
   if (hasB) put_word_all(hw_all, hrep, (size_t)(sh + rB) * hstride + pB, epoch, gu_finish<NCH>(B, RB, xc));
-  // further rounds, for layers with more routed items than twice the waves
-  for (int it0 = gw + 2 * NWV; it0 < nitems; it0 += 2 * NWV) {
+  // further rounds, for layers with more routed items than 8 per workgroup
+  for (int it0 = itA + 8; it0 < iend; it0 += 8) {
     GUItem<NCH> C, D;
-    const int itD = it0 + NWV;
+    const int itD = it0 + 4;
     const int rC = it0 / ipw, pC = it0 - rC * ipw;
     const GURows RC = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rC]));
     gu_load<NCH>(C, RC, pC, H);
-    const bool hasD = itD < nitems;
+    const bool hasD = itD < iend;
     const int rD = hasD ? itD / ipw : rC, pD = hasD ? itD - rD * ipw : pC;
     const GURows RD = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rD]));
     if (hasD) gu_load<NCH>(D, RD, pD, H);

@@ -21,20 +21,24 @@ __device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch,
 
 // Batched wait: all U words are loaded at once, then only the ones that do
 // not carry the epoch yet are loaded again.  Entries with ok[u] false are
-// skipped.
+// skipped; their pointers must still be valid: the first loads are made
+// unconditionally (a load made on one path only can leave the compiler
+// believing it may still be in flight, and waiting for the memory counter
+// to drain in the middle of the next batch of loads).
 template <int U>
 __device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* const (&p)[U],
                                            const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
 #pragma unroll
+  for (int u = 0; u < U; ++u) w[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
   for (int u = 0; u < U; ++u)
-    w[u] = ok[u] ? __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : ((uint64_t)epoch << 32);
+    if (!ok[u]) w[u] = (uint64_t)epoch << 32;
   for (uint32_t spin = 0; spin < kFusedSpin; ++spin) {
     bool ready = true;
 #pragma unroll
     for (int u = 0; u < U; ++u) ready = ready && (uint32_t)(w[u] >> 32) == epoch;
     if (ready) return;
-    __builtin_amdgcn_s_sleep(8);     // back off: every workgroup is polling
+    __builtin_amdgcn_s_sleep(1);     // a short back-off: a reload takes a round trip anyway
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if ((uint32_t)(w[u] >> 32) != epoch)
@@ -148,6 +152,47 @@ __device__ __forceinline__ uint64_t select_topk(uint64_t (&key)[4], int K) {
     if (lane == k) mine = m;
   }
   return mine;
+}
+
+// Maximum over the wave of a 32-bit value, in every lane: DPP steps within
+// rows of 16 lanes, then the four row maxima combined with the permlane
+// swaps, so that no value makes a round trip through a scalar register.
+__device__ __forceinline__ uint32_t wave_max_u32_all(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));                   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));                   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141>(v));                  // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));                  // row_mirror
+  { const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false); v = max(r[0], r[1]); }
+  { const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false); v = max(r[0], r[1]); }
+  return v;
+}
+
+// top-k of one token from its four keys per lane (order key of the logit
+// << 32 | inverted expert index; 0 for no entry): the k-th selected key
+// (descending logit, equal logits to the lower index) is written to
+// s_key[k].  Each lane sorts its keys, then every round takes the wave
+// maximum of the lanes' heads on the 32-bit logit key alone and the winning
+// lane stores and pops its head; only when several lanes hold the maximal
+// logit (equal logits) is the index half compared too.
+__device__ __forceinline__ void topk_keys_to_lds(uint64_t (&key)[4], int K, uint64_t* s_key) {
+#define FLINT_CSWAP(i, j) { const uint64_t hi_ = key[i] > key[j] ? key[i] : key[j]; \
+                            const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
+  FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
+#undef FLINT_CSWAP
+  for (int k = 0; k < K; ++k) {
+    const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+    const uint32_t mhi = wave_max_u32_all(hi);
+    const bool at = hi == mhi;
+    bool win = at;
+    if (__popcll(__ballot(at)) != 1) {            // equal logits: the lower index wins
+      const uint32_t mlo = wave_max_u32_all(at ? lo : 0u);
+      win = at && lo == mlo;
+    }
+    if (win) {
+      s_key[k] = key[0];
+      key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull;
+    }
+  }
 }
 
 inline int device_num_cu() {
