@@ -249,7 +249,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
         ptr[q] = lw + (ex < E ? ex : 0);
       }
       arrival_slots(ws, E, G, ptr + 4, ok + 4);   // workgroup 0 only
-      poll_words<8>(wd, ptr, ok, epoch, ws.error);
+      poll_words_pipelined<8, 10>(wd, ptr, ok, epoch, ws.error);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int ex = lane + 64 * q;
@@ -262,13 +262,18 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     const uint64_t my_key = lane < K ? s_key[lane] : 0ull;   // lane k: the k-th selected key
     const int my_e = (int)~(uint32_t)my_key;
     const float my_s = lane < K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
+    // both loops unrolled to the largest K (lane indices are constants, so
+    // the readlanes issue back to back)
     float ssum = 0.f;
-    for (int k = 0; k < K; ++k)                   // selection order, like the split path
-      ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+#pragma unroll
+    for (int k = 0; k < FLINT_MAX_TOP_K; ++k)     // selection order, like the split path
+      if (k < K) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
     const float w = (a.flags & FLINT_RENORM) ? my_s / ssum : my_s;
     // routed slots in ascending expert order: rank of each selected expert
     int rank = 0;
-    for (int k = 0; k < K; ++k) rank += __builtin_amdgcn_readlane(my_e, k) < my_e ? 1 : 0;
+#pragma unroll
+    for (int k = 0; k < FLINT_MAX_TOP_K; ++k)
+      if (k < K) rank += __builtin_amdgcn_readlane(my_e, k) < my_e ? 1 : 0;
     if (lane < K) {
       s_exp[sh + rank] = my_e;
       s_w[sh + rank] = w;

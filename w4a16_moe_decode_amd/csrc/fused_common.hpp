@@ -47,6 +47,47 @@ __device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* con
   *err = 1u;
 }
 
+// Pipelined wait for small sets of words: a new batch of loads of all U
+// words is issued every SLEEP x 64 cycles, and each batch is checked while
+// the next is in flight (loads complete in order, so checking one batch
+// waits only for it).  A word that lands just after a batch passed it is
+// then seen about one issue interval later instead of one round trip later.
+// Entries with ok[u] false are skipped; their pointers must still be valid.
+template <int U, int SLEEP>
+__device__ __forceinline__ void poll_words_pipelined(uint64_t (&w)[U], const uint64_t* const (&p)[U],
+                                                     const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
+  uint64_t a[U], b[U];
+  auto ready = [&](const uint64_t (&v)[U]) {
+    bool r = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) r = r && (!ok[u] || (uint32_t)(v[u] >> 32) == epoch);
+    return r;
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) a[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t spin = 0; spin < kFusedSpin; spin += 2) {
+    __builtin_amdgcn_s_sleep(SLEEP);
+#pragma unroll
+    for (int u = 0; u < U; ++u) b[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ready(a)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u] = ok[u] ? a[u] : (uint64_t)epoch << 32;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(SLEEP);
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ready(b)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u] = ok[u] ? b[u] : (uint64_t)epoch << 32;
+      return;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) w[u] = ok[u] ? a[u] : (uint64_t)epoch << 32;
+  *err = 1u;
+}
+
 __device__ __forceinline__ void put_word(uint64_t* p, uint32_t epoch, uint32_t payload) {
   __hip_atomic_store(p, ((uint64_t)epoch << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -179,7 +220,9 @@ __device__ __forceinline__ void topk_keys_to_lds(uint64_t (&key)[4], int K, uint
                             const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
   FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
 #undef FLINT_CSWAP
-  for (int k = 0; k < K; ++k) {
+#pragma unroll
+  for (int k = 0; k < FLINT_MAX_TOP_K; ++k) {
+    if (k >= K) break;                            // the same in every lane
     const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
     const uint32_t mhi = wave_max_u32_all(hi);
     const bool at = hi == mhi;
