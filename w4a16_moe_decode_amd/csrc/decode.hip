@@ -1037,14 +1037,15 @@ void gate_up_nv_batch_kernel(LayerArgs a, DecodeWs ws, uint16_t* hout, int h_slo
 // row staged in LDS once per workgroup: wave 0 reads the slot table (one
 // round trip: every entry a lane may need is loaded at once) and builds the
 // pair list with a prefix sum of the slots' token counts; all threads then
-// copy the h rows into LDS.  Only after that does any wave issue weight
-// loads: vector loads complete in order, so h issued behind the weights
-// would wait for all of them, while weights issued last let each item be
-// computed as soon as its own rows arrive.  LDS layout as in
+// issue the loads of the h rows, then the weight loads, and only then store
+// h to LDS: vector loads complete in order, so h issued first is waited for
+// alone, and the weights are already in flight meanwhile; weights issued
+// last let each item be computed as soon as its own rows arrive.  LDS
+// layout as in
 // gate_up_batch_kernel: pair p, quad m of chunk j at
 // s_h[(p * QPC + m) * cmax + j].
 template <int WF, int G, int RW, int NW, int U>
-__global__ __launch_bounds__(64 * NW) void down_batch_kernel(LayerArgs a, DecodeWs ws, const uint16_t* hin,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 2))) void down_batch_kernel(LayerArgs a, DecodeWs ws, const uint16_t* hin,
                                                              int h_slot_stride, int h_tok_stride) {
   constexpr int BT = kMaxB, NT = 64 * NW;
   constexpr int GPW = 64 / G, RPW = RW * GPW;
@@ -1131,37 +1132,32 @@ __global__ __launch_bounds__(64 * NW) void down_batch_kernel(LayerArgs a, Decode
   __syncthreads();
   const int S = *ws.nslot + sh;
 
-  // h rows into LDS.  Thread t copies quad (m, j) = t % qmax of pairs
-  // t / qmax + ppp * k (ppp = NT / qmax pairs per pass, qmax <= NT); every
-  // load and store is made, those past the list reading the first quad and
-  // writing this thread's slot past the largest list.
-  {
-    const int np = s_np;
-    const int ppp = NT / qmax;
-    int rem, j;
-    const int p0 = div_small(threadIdx.x, qmax, 1.0f / (float)qmax, rem);
-    const int m = div_small(rem, cmax, 1.0f / (float)cmax, j);
-    const bool tv = p0 < ppp;
-    const int hdummy = (a.B * (a.K < a.E ? a.K : a.E) + (sh ? a.B : 0)) * qmax + (int)threadIdx.x;
-    const size_t off = (size_t)j * VALS + 8 * m;
-    for (int pb0 = 0; pb0 < np; pb0 += ppp * NHL) {
-      uint4 hv[NHL];
-#pragma unroll
-      for (int k = 0; k < NHL; ++k) {
-        const int p = p0 + pb0 + ppp * k;
-        const bool ok = tv && p < np;
-        const int pr = s_pair[ok ? p : 0];
-        const uint16_t* src = hin + (size_t)(pr >> 3) * h_slot_stride + (size_t)(pr & 7) * h_tok_stride + off;
-        hv[k] = *reinterpret_cast<const uint4*>(ok ? src : hin);
-      }
-#pragma unroll
-      for (int k = 0; k < NHL; ++k) {
-        const int p = p0 + pb0 + ppp * k;
-        s_h[tv && p < np ? p * qmax + rem : hdummy] = hv[k];
-      }
-    }
+  // h rows into LDS, copied by the load units straight from memory
+  // (global_load_lds: no registers).  Thread t copies quad (m, j) = t % qmax
+  // of pairs t / qmax + ppp * k (ppp = NT / qmax pairs per pass,
+  // qmax <= NT) to s_h[t + ppp * k * qmax], so each wave's 64 quads land in
+  // consecutive LDS words.  The first pass is issued before the weight loads
+  // below: loads complete in order, so waiting for the copies does not wait
+  // for the weights, and the weights' latency runs under the copies' instead
+  // of after them.  (Layers with more than ppp * NHL pairs copy the rest
+  // after the weights.)
+  const int np = s_np;
+  const int ppp = NT / qmax;
+  int hrem, hj;
+  const int hp0 = div_small(threadIdx.x, qmax, 1.0f / (float)qmax, hrem);
+  const int hm = div_small(hrem, cmax, 1.0f / (float)cmax, hj);
+  const size_t hoff = (size_t)hj * VALS + 8 * hm;
+#define FLINT_H_COPY(PB0)                                                                              \
+  _Pragma("unroll") for (int k = 0; k < NHL; ++k) {                                                   \
+    const int p = hp0 + (PB0) + ppp * k;                                                                \
+    const bool ok = p < np;                                                                             \
+    const int pr = s_pair[ok ? p : 0];                                                                  \
+    const uint16_t* src = hin + (size_t)(pr >> 3) * h_slot_stride + (size_t)(pr & 7) * h_tok_stride + hoff; \
+    uint4* dst = s_h + ((PB0) + ppp * k) * qmax + (threadIdx.x & ~63);                                  \
+    if (ok) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);                                       \
   }
-  __syncthreads();
+  FLINT_H_COPY(0)
+  asm volatile("" ::: "memory");                   // the weight loads stay behind the copies
 
   // Weights of U items (slot, chunk step) per wave.  The item, its expert and
   // the matrix bases are wave-uniform (scalar); each lane adds fixed 32-bit
@@ -1231,47 +1227,68 @@ __global__ __launch_bounds__(64 * NW) void down_batch_kernel(LayerArgs a, Decode
   };
   load_items(wv);
 
+  // This wave's copies are complete once at most the weight loads issued
+  // after them are outstanding (every one of those loads is made); then the
+  // barrier makes every wave's copies visible.
+  constexpr int kWeightLoads = U * RW * (WF == FMT_NVFP4 ? 2 : 1);
+  static_assert(kWeightLoads < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (kWeightLoads & 15) | ((kWeightLoads & 48) << 10));
+  if (np > ppp * NHL) {
+    for (int pb0 = ppp * NHL; pb0 < np; pb0 += ppp * NHL) { FLINT_H_COPY(pb0) }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+#undef FLINT_H_COPY
+  __syncthreads();
+
   float acc[RW][BT];
 #pragma unroll
   for (int rw = 0; rw < RW; ++rw)
 #pragma unroll
     for (int t = 0; t < BT; ++t) acc[rw][t] = 0.f;
-  for (int it0 = wv;; ) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int it = it0 + u * NW;
-      if (it >= total) break;
-      const int s = nch == 1 ? it : it / nch, c = it - s * nch;
-      const int e = ie[u];
-      const int inter = e < 0 ? SI : I;
-      const int j = li + G * c;
-      if (j >= inter / VALS) continue;
-      const uint32_t mask = s_msk[s];
-      const int pb = s_pb[s];
-      const float gd = igd[u];
-      DChunk<WF> d[RW];
-#pragma unroll
-      for (int rw = 0; rw < RW; ++rw) d[rw] = decode_chunk<WF>(raw[u][rw], sc[u][rw]);
-#pragma unroll
-      for (int t = 0; t < BT; ++t) {
-        if ((mask >> t) & 1u) {
-          const int p = pb + __popc(mask & ((1u << t) - 1u));
-          XChunk<WF> hx;
-#pragma unroll
-          for (int m = 0; m < QPC; ++m) {
-            const uint4 v = s_h[(p * QPC + m) * cmax + j];
-            hx.v[4 * m + 0] = v.x; hx.v[4 * m + 1] = v.y; hx.v[4 * m + 2] = v.z; hx.v[4 * m + 3] = v.w;
-          }
-          const float f = s_wt[s][t] * gd;
-#pragma unroll
-          for (int rw = 0; rw < RW; ++rw) acc[rw][t] = fmaf(f, chunk_dot(d[rw], hx), acc[rw][t]);
-        }
-      }
-    }
-    it0 += NW * U;
-    if (it0 >= total) break;
-    load_items(it0);                               // layers with more items than U per wave
+  // The first round of items is straight-line code: inside a loop, the
+  // registers the last weight loads write were reused at the loop head,
+  // which made every item wait for all of them.
+#define FLINT_DOWN_ITEMS(IT0)                                                 \
+  {                                                                           \
+    const int it0 = (IT0);                                                    \
+  _Pragma("unroll")                                                      \
+    for (int u = 0; u < U; ++u) {                                             \
+      const int it = it0 + u * NW;                                            \
+      if (it >= total) break;                                                 \
+      const int s = nch == 1 ? it : it / nch, c = it - s * nch;               \
+      const int e = ie[u];                                                    \
+      const int inter = e < 0 ? SI : I;                                       \
+      const int j = li + G * c;                                               \
+      if (j >= inter / VALS) continue;                                        \
+      const uint32_t mask = s_msk[s];                                         \
+      const int pb = s_pb[s];                                                 \
+      const float gd = igd[u];                                                \
+      DChunk<WF> d[RW];                                                       \
+  _Pragma("unroll")                                                      \
+      for (int rw = 0; rw < RW; ++rw) d[rw] = decode_chunk<WF>(raw[u][rw], sc[u][rw]); \
+  _Pragma("unroll")                                                      \
+      for (int t = 0; t < BT; ++t) {                                          \
+        if ((mask >> t) & 1u) {                                               \
+          const int p = pb + __popc(mask & ((1u << t) - 1u));                 \
+          XChunk<WF> hx;                                                      \
+  _Pragma("unroll")                                                      \
+          for (int m = 0; m < QPC; ++m) {                                     \
+            const uint4 v = s_h[(p * QPC + m) * cmax + j];                    \
+            hx.v[4 * m + 0] = v.x; hx.v[4 * m + 1] = v.y; hx.v[4 * m + 2] = v.z; hx.v[4 * m + 3] = v.w; \
+          }                                                                   \
+          const float f = s_wt[s][t] * gd;                                    \
+  _Pragma("unroll")                                                      \
+          for (int rw = 0; rw < RW; ++rw) acc[rw][t] = fmaf(f, chunk_dot(d[rw], hx), acc[rw][t]); \
+        }                                                                     \
+      }                                                                       \
+    }                                                                         \
   }
+  FLINT_DOWN_ITEMS(wv)
+  for (int it1 = wv + NW * U; it1 < total; it1 += NW * U) {   // layers with more items than U per wave
+    load_items(it1);
+    FLINT_DOWN_ITEMS(it1)
+  }
+#undef FLINT_DOWN_ITEMS
 
 #pragma unroll
   for (int rw = 0; rw < RW; ++rw)
