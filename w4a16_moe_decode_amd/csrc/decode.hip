@@ -225,6 +225,7 @@ __global__ __launch_bounds__(256) void route_batch_kernel(LayerArgs a, DecodeWs 
   __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
   __shared__ float s_w[FLINT_MAX_EXPERTS][kMaxB];
   __shared__ int s_wcnt[4];
+  __shared__ uint64_t s_key[4][FLINT_MAX_TOP_K];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.H, B = a.B, E = a.E;
   const int e = blockIdx.x;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256) void route_batch_kernel(LayerArgs a, DecodeWs 
         ptr[4 * h + q] = ws.logit_words + (size_t)(t < B ? t : 0) * E + (ex < E ? ex : 0);
       }
     }
-    poll_words<8>(wd, ptr, ok, epoch, ws.error);
+    poll_words_pipelined<8, 10>(wd, ptr, ok, epoch, ws.error);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = wave + 4 * h;
@@ -335,12 +336,14 @@ __global__ __launch_bounds__(256) void route_batch_kernel(LayerArgs a, DecodeWs 
                                   (uint32_t)~(uint32_t)ex)
                                : 0ull;
       }
-      const uint64_t my_key = select_topk(key, a.K);
+      topk_keys_to_lds(key, a.K, s_key[wave]);
+      const uint64_t my_key = lane < a.K ? s_key[wave][lane] : 0ull;   // lane k: the k-th selected key
       const int my_e = (int)~(uint32_t)my_key;
       const float my_s = lane < a.K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
       float ssum = 0.f;
-      for (int k = 0; k < a.K; ++k)                 // selection order
-        ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+#pragma unroll
+      for (int k = 0; k < FLINT_MAX_TOP_K; ++k)     // selection order
+        if (k < a.K) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
       if (lane < a.K) {
         const float w = renorm ? my_s / ssum : my_s;
         a.topk_idx[t * a.K + lane] = my_e;
