@@ -1231,9 +1231,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 2)))
   load_items(wv);
 
   // This wave's copies are complete once at most the weight loads issued
-  // after them are outstanding (every one of those loads is made); then the
-  // barrier makes every wave's copies visible.
-  constexpr int kWeightLoads = U * RW * (WF == FMT_NVFP4 ? 2 : 1);
+  // after them are outstanding; then the barrier makes every wave's copies
+  // visible.  Only the 16-byte code loads are counted (every one is made,
+  // and no two can merge; scale loads may be merged into fewer), so the
+  // count never exceeds the loads actually issued after the copies.
+  constexpr int kWeightLoads = U * RW;
   static_assert(kWeightLoads < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (kWeightLoads & 15) | ((kWeightLoads & 48) << 10));
   if (np > ppp * NHL) {
