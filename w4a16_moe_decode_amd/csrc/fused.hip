@@ -249,7 +249,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
         ptr[q] = lw + (ex < E ? ex : 0);
       }
       arrival_slots(ws, E, G, ptr + 4, ok + 4);   // workgroup 0 only
-      poll_words_pipelined<8, 10>(wd, ptr, ok, epoch, ws.error);
+      poll_words_pipelined<8, 1>(wd, ptr, ok, epoch, ws.error);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int ex = lane + 64 * q;
