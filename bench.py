@@ -24,6 +24,8 @@ Reported (one JSON line):
                residual) at batch 1, NVFP4 and BF16 weights
   prefill      8,192 tokens through one layer: TFLOP/s against the BF16
                MFMA peak, for i.i.d. and for skewed (correlated) tokens
+  lm_head      an NVFP4 LM-head GEMV (2048 -> 150,144, 173 MB) through
+               flint_dense_gemv at batch 1 and 8: TB/s against 8 TB/s
 The timed loops replay HIP graphs of the layer calls, so host launch cost is
 not on the clock.
 """
@@ -221,6 +223,51 @@ def bench_step(args, dev, batch=1, n_moe=47, n_dense=2, reps=20):
     return out
 
 
+LM_HEAD_VOCAB = 150144
+
+
+def bench_lm_head(dev, seed, n_copies=3, reps=30):
+    """An NVFP4 LM-head GEMV (hidden 2048 -> 150,144 vocabulary rows, 173 MB
+    of packed weights) through flint_dense_gemv at batch 1 and 8, rotating
+    n_copies independently seeded matrices (519 MB, past the 256 MB cache)."""
+    rows, cols = LM_HEAD_VOCAB, 2048
+    mats = []
+    for c in range(n_copies):
+        src = gen.nvfp4_source(gen.seed_for(seed, "lm-head", c), 1, rows, cols, dev)
+        mats.append(fm.repack_matrices(src))
+        del src
+    gs = torch.tensor([1 / 64, 0, 0, 0], dtype=torch.float32, device=dev)
+    nbytes = rows * cols // 2 + rows * cols // 16
+    out = {"rows": rows, "cols": cols, "weight_bytes": nbytes, "copies": n_copies}
+    for batch in (1, 8):
+        x = gen.activations(gen.seed_for(seed, "lm-x", batch), batch, cols, dev)
+        y = torch.empty((batch, rows), dtype=torch.bfloat16, device=dev)
+
+        def body(n):
+            for i in range(n):
+                c, s = mats[i % n_copies]
+                fm.flint_dense_gemv(c, s, gs, None, rows, cols, 0, x, batch, y, fm.FLINT_EPI_NONE)
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            body(n_copies)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body(reps)
+        g.replay()
+        secs = timed(g) / reps
+        b = nbytes + 2 * batch * (rows + cols)
+        out[f"batch{batch}"] = {"us": round(secs * 1e6, 2), "tb_s": round(b / secs / 1e12, 3),
+                                "frac_hbm_peak": round(b / secs / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] lm head batch {batch}: {secs * 1e6:.1f} us, {b / secs / 1e12:.3f} TB/s",
+              file=sys.stderr, flush=True)
+        del g
+    del mats
+    return out
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -344,6 +391,7 @@ def main():
     ap.add_argument("--no-batch8", action="store_true")
     ap.add_argument("--no-step", action="store_true", help="skip the 49-layer decode step")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8,192-token prefill")
+    ap.add_argument("--no-lm-head", action="store_true", help="skip the NVFP4 LM-head GEMV")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy (fp32 negate) of this many MiB three "
                          "times, so that a counter run can scale FETCH_SIZE / WRITE_SIZE by it")
@@ -434,6 +482,8 @@ def main():
                           "gate_up_frac": round(gu8 / HBM_PEAK_GBS, 4)}
     if not args.no_prefill:
         line["prefill"] = bench_prefill(layers[0], shape, args.seed)
+    if not args.no_lm_head:
+        line["lm_head"] = bench_lm_head(dev, args.seed)
     if not args.no_step:
         del layers
         torch.cuda.empty_cache()

@@ -103,3 +103,49 @@ def test_residual_in_place():
     wd = formats.decode_source_matrix(d_src[0].numpy(), "interleaved", 1 / 64)
     want = obf.round_bf16(gen.numpy_f64(aux) + obf.round_bf16(gen.numpy_f64(x.cpu()) @ wd.T))
     compare_outputs(gen.numpy_f64(y), want, "y")
+
+
+@pytest.mark.parametrize("rows,cols,batch", [(1000, 2048, 1), (1000, 2048, 5), (333, 4096, 8), (64, 4096, 1)])
+@pytest.mark.parametrize("epi", [fm.FLINT_EPI_NONE, fm.FLINT_EPI_RESIDUAL])
+def test_tall_projection_shapes(rows, cols, batch, epi):
+    """The tall-matrix NVFP4 projection (2048 or 4096 columns): ragged row
+    counts, every batch size class, both epilogues, non-power-of-two scale."""
+    ts = gen.tensor_scales(gen.seed_for(30, rows, cols), 1, "varied")
+    d_src = gen.nvfp4_source(gen.seed_for(31, rows, cols), 1, rows, cols, scale_mode="full")
+    t0 = float(ts.reshape(-1)[2])
+    x = gen.activations(gen.seed_for(32, cols, batch), batch, cols)
+    aux = gen.activations(gen.seed_for(33, rows, batch), batch, rows)
+    y = torch.empty((batch, rows), dtype=torch.bfloat16, device="cuda")
+    gs = torch.tensor([t0, 0, 0, 0], dtype=torch.float32).cuda()
+    codes, scales = fm.repack_matrices(d_src.cuda())
+    auxd = aux.cuda() if epi == fm.FLINT_EPI_RESIDUAL else None
+    fm.flint_dense_gemv(codes, scales, gs, None, rows, cols, 0, x.cuda(), batch, y, epi, aux=auxd)
+    torch.cuda.synchronize()
+    wd = formats.decode_source_matrix(d_src[0].numpy(), "interleaved", t0)
+    want = obf.round_bf16(gen.numpy_f64(x) @ wd.T)
+    if epi == fm.FLINT_EPI_RESIDUAL:
+        want = obf.round_bf16(gen.numpy_f64(aux) + want)
+    compare_outputs(gen.numpy_f64(y), want, "y")
+
+
+LM_HEAD_ROWS = 150144      # vocabulary rows of an NVFP4 LM head over hidden 2048
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_lm_head_projection_sampled(batch):
+    """The LM-head shape (2048 -> 150,144, 173 MB of NVFP4 weights) in the
+    launch configuration the benchmark times, checked against the oracle on
+    a sample of rows (every 151st row plus the ragged tail), which the
+    oracle decodes from the source bytes."""
+    rows, cols = LM_HEAD_ROWS, 2048
+    d_src = gen.nvfp4_source(gen.seed_for(40, batch), 1, rows, cols)
+    x = gen.activations(gen.seed_for(41, batch), batch, cols)
+    y = torch.empty((batch, rows), dtype=torch.bfloat16, device="cuda")
+    gs = torch.tensor([1 / 64, 0, 0, 0], dtype=torch.float32).cuda()
+    codes, scales = fm.repack_matrices(d_src.cuda())
+    fm.flint_dense_gemv(codes, scales, gs, None, rows, cols, 0, x.cuda(), batch, y, fm.FLINT_EPI_NONE)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([np.arange(0, rows, 151), np.arange(rows - 70, rows)]))
+    wd = formats.decode_source_matrix(d_src[0, torch.from_numpy(sample)].numpy(), "interleaved", 1 / 64)
+    want = obf.round_bf16(gen.numpy_f64(x) @ wd.T)
+    compare_outputs(gen.numpy_f64(y.cpu())[:, sample], want, "y")

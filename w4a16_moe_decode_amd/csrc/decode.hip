@@ -1515,6 +1515,133 @@ hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) 
   return route_dispatch<kMaxB>(a, ws, st);
 }
 
+// ------------------------------------- dense NVFP4 projection, tall matrix --
+// y[t][r] = BF16(g * sum_c W[r][c] x[t][c]), or BF16(aux[t][r] + that), for a
+// packed NVFP4 matrix W [rows][cols] with many rows and 1..8 tokens: the
+// plain and residual projections of flint_dense_gemv (the small-batch dense
+// GEMV on the same packed weights of "Day-0 Support for Flint on vLLM",
+// "Optimizations"; the same call serves an NVFP4 LM head).  16 lanes per
+// row, lane li owning the CPL consecutive chunks li * CPL .. li * CPL +
+// CPL - 1, so a row's cross-lane sum is four DPP steps; a wave holds RPL
+// sets of 4 rows, a workgroup NW * 4 * RPL rows.  Every weight load of the
+// workgroup is issued first, then the tokens are staged in LDS in the layout
+// of gate_up_nv_batch_kernel (position q of token i holds columns
+// 32 * (CPL * (q % 16) + (q / 16) / 4) + 8 * ((q / 16) % 4), so the 16 lanes
+// of a row group read consecutive words), and each decoded chunk is applied
+// to every token.  Every load and LDS store is made (rows past the matrix
+// read row 0 and are not stored; token positions past the batch read token
+// 0 and are stored past the staged tokens).
+template <int NW, int CPL, int RPL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                     const float* __restrict__ gscale, const uint16_t* __restrict__ x, int B, int rows, int cols,
+                     uint16_t* y, const uint16_t* aux, int resid) {
+  constexpr int G = 16, QPC = 4, BT = kMaxB;
+  extern __shared__ uint4 s_x[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int grp = lane / G, li = lane % G;
+  const int rbase = (blockIdx.x * NW + wave) * 4 * RPL + grp;     // row of set p: rbase + 4 p
+  const int q8 = cols / 8;
+
+  uint4 wc[RPL][CPL];
+  uint32_t sc2[RPL][CPL / 2];
+#pragma unroll
+  for (int p = 0; p < RPL; ++p) {
+    const int r = rbase + 4 * p;
+    const uint32_t rc = r < rows ? (uint32_t)r : 0u;
+    const uint32_t oc = rc * ((uint32_t)cols / 2) + (uint32_t)li * 16u * CPL;
+    const uint32_t os = rc * ((uint32_t)cols / 16) + (uint32_t)li * 2u * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wc[p][c] = reinterpret_cast<const uint4*>(codes + oc)[c];
+#pragma unroll
+    for (int c = 0; c < CPL; c += 2) sc2[p][c / 2] = reinterpret_cast<const uint32_t*>(scales + os)[c / 2];
+  }
+  const float g = gscale[0];
+  // residual values of this lane's rows, fetched early (always: without a
+  // residual, or past the batch or the matrix, they read y's first element)
+  uint16_t xr[RPL][BT];
+  const uint16_t* ab = resid ? aux : y;
+#pragma unroll
+  for (int p = 0; p < RPL; ++p)
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const int r = rbase + 4 * p;
+      const bool ok = resid && i < B && r < rows;
+      xr[p][i] = ab[ok ? (size_t)i * rows + r : 0];
+    }
+  {
+    const int q = threadIdx.x;
+    const int col = 32 * (CPL * (q % G) + (q / G) / QPC) + 8 * ((q / G) % QPC);
+    uint4 xv[BT];
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      const bool ok = q < q8 && i < B;
+      xv[i] = *reinterpret_cast<const uint4*>(ok ? x + (size_t)i * cols + col : x);
+    }
+#pragma unroll
+    for (int i = 0; i < BT; ++i) s_x[q < q8 && i < B ? i * q8 + q : B * q8 + q] = xv[i];
+  }
+  __syncthreads();
+
+  float acc[RPL][BT];
+#pragma unroll
+  for (int p = 0; p < RPL; ++p)
+#pragma unroll
+    for (int i = 0; i < BT; ++i) acc[p][i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    DChunk<FMT_NVFP4> d[RPL];
+#pragma unroll
+    for (int p = 0; p < RPL; ++p)
+      d[p] = decode_nvfp4(wc[p][c], c % 2 ? sc2[p][c / 2] >> 16 : sc2[p][c / 2] & 0xffffu);
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      if (i >= B) break;
+      XChunk<FMT_NVFP4> xc;
+#pragma unroll
+      for (int m = 0; m < QPC; ++m) {
+        const uint4 v = s_x[i * q8 + (c * QPC + m) * G + li];
+        xc.v[4 * m + 0] = v.x; xc.v[4 * m + 1] = v.y; xc.v[4 * m + 2] = v.z; xc.v[4 * m + 3] = v.w;
+      }
+#pragma unroll
+      for (int p = 0; p < RPL; ++p) acc[p][i] += chunk_dot(d[p], xc);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < RPL; ++p) {
+    const int r = rbase + 4 * p;
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      if (i >= B) break;
+      const float v = group_sum<G>(acc[p][i]);
+      if (li == 0 && r < rows) {
+        float o = round_bf16(v * g);
+        if (resid) o = bf16_bits_to_f32(xr[p][i]) + o;
+        y[(size_t)i * rows + r] = f32_to_bf16_bits(o);
+      }
+    }
+  }
+}
+
+// the tall-matrix projection for NVFP4 weights with 2048 or 4096 columns;
+// false when the shape is outside what it covers
+bool dense_nv_supported(int cols, int batch) {
+  return (cols == 2048 || cols == 4096) && batch >= 1 && batch <= kMaxB;
+}
+
+template <int NW, int CPL, int RPL>
+hipError_t dense_nv_launch(const uint8_t* codes, const uint8_t* scales, const float* gscale, const uint16_t* x,
+                           int B, int rows, int cols, uint16_t* y, const uint16_t* aux, int resid, hipStream_t st) {
+  auto k = dense_nv_kernel<NW, CPL, RPL>;
+  const int lds = (B * cols / 8 + 64 * NW) * 16;
+  static const bool lds_ok = allow_dynamic_lds(k, (kMaxB * 4096 / 8 + 64 * NW) * 16);
+  (void)lds_ok;
+  const int per = NW * 4 * RPL;
+  hipLaunchKernelGGL(k, dim3((rows + per - 1) / per), dim3(64 * NW), lds, st, codes, scales, gscale, x, B, rows,
+                     cols, y, aux, resid);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm,
                           hipStream_t st) {
   // decode: h[slot][t][Imax]; dense: y[t][rows] with rows = SI
@@ -1546,6 +1673,13 @@ hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int d
   const int ht = dense ? a.SI : imax;
   const int dcols = dense ? a.SI : 0;
   const bool bf = (a.flags & FLINT_W_BF16) != 0;
+  if (dense && !bf && dense_nv_supported(a.SI, a.B)) {      // W [H][SI] . x[B][SI]
+    const int resid = dense_epilogue == FLINT_EPI_RESIDUAL ? 1 : 0;
+    return a.SI == 2048 ? dense_nv_launch<8, 4, 2>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.SI,
+                                                    a.out, aux, resid, st)
+                        : dense_nv_launch<8, 8, 1>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.SI,
+                                                    a.out, aux, resid, st);
+  }
   if (a.B == 1)
     return bf ? down_dispatch_g<FMT_BF16, 1>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st)
               : down_dispatch_g<FMT_NVFP4, 1>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st);
