@@ -1523,20 +1523,23 @@ hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) 
 // "Optimizations"; the same call serves an NVFP4 LM head).  16 lanes per
 // row, lane li owning the CPL consecutive chunks li * CPL .. li * CPL +
 // CPL - 1, so a row's cross-lane sum is four DPP steps; a wave holds RPL
-// sets of 4 rows, a workgroup NW * 4 * RPL rows.  Every weight load of the
+// sets of 4 rows, a workgroup NW * 4 * RPL rows (NW = 1 for one token).  Every weight load of the
 // workgroup is issued first, then the tokens are staged in LDS in the layout
 // of gate_up_nv_batch_kernel (position q of token i holds columns
 // 32 * (CPL * (q % 16) + (q / 16) / 4) + 8 * ((q / 16) % 4), so the 16 lanes
 // of a row group read consecutive words), and each decoded chunk is applied
 // to every token.  Every load and LDS store is made (rows past the matrix
 // read row 0 and are not stored; token positions past the batch read token
-// 0 and are stored past the staged tokens).
-template <int NW, int CPL, int RPL>
+// 0 and are stored past the staged tokens).  BT is the token capacity (1 for
+// the one-token variant, so that its staging registers stay few).
+template <int NW, int CPL, int RPL, int BT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                      const float* __restrict__ gscale, const uint16_t* __restrict__ x, int B, int rows, int cols,
                      uint16_t* y, const uint16_t* aux, int resid) {
-  constexpr int G = 16, QPC = 4, BT = kMaxB;
+  constexpr int G = 16, QPC = 4, NT = 64 * NW;
+  constexpr int KQ = CPL / NW;                     // staged positions per thread: cols / 8 = KQ * NT
+  static_assert(CPL % NW == 0, "staging layout");
   extern __shared__ uint4 s_x[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int grp = lane / G, li = lane % G;
@@ -1570,16 +1573,20 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
       xr[p][i] = ab[ok ? (size_t)i * rows + r : 0];
     }
   {
-    const int q = threadIdx.x;
-    const int col = 32 * (CPL * (q % G) + (q / G) / QPC) + 8 * ((q / G) % QPC);
-    uint4 xv[BT];
+    uint4 xv[KQ][BT];
 #pragma unroll
-    for (int i = 0; i < BT; ++i) {
-      const bool ok = q < q8 && i < B;
-      xv[i] = *reinterpret_cast<const uint4*>(ok ? x + (size_t)i * cols + col : x);
+    for (int kq = 0; kq < KQ; ++kq) {
+      const int q = threadIdx.x + NT * kq;
+      const int col = 32 * (CPL * (q % G) + (q / G) / QPC) + 8 * ((q / G) % QPC);
+#pragma unroll
+      for (int i = 0; i < BT; ++i) xv[kq][i] = *reinterpret_cast<const uint4*>(x + (size_t)(i < B ? i : 0) * cols + col);
     }
 #pragma unroll
-    for (int i = 0; i < BT; ++i) s_x[q < q8 && i < B ? i * q8 + q : B * q8 + q] = xv[i];
+    for (int kq = 0; kq < KQ; ++kq) {
+      const int q = threadIdx.x + NT * kq;
+#pragma unroll
+      for (int i = 0; i < BT; ++i) s_x[(i < B ? i : B) * q8 + q] = xv[kq][i];
+    }
   }
   __syncthreads();
 
@@ -1629,12 +1636,12 @@ bool dense_nv_supported(int cols, int batch) {
   return (cols == 2048 || cols == 4096) && batch >= 1 && batch <= kMaxB;
 }
 
-template <int NW, int CPL, int RPL>
+template <int NW, int CPL, int RPL, int BT>
 hipError_t dense_nv_launch(const uint8_t* codes, const uint8_t* scales, const float* gscale, const uint16_t* x,
                            int B, int rows, int cols, uint16_t* y, const uint16_t* aux, int resid, hipStream_t st) {
-  auto k = dense_nv_kernel<NW, CPL, RPL>;
-  const int lds = (B * cols / 8 + 64 * NW) * 16;
-  static const bool lds_ok = allow_dynamic_lds(k, (kMaxB * 4096 / 8 + 64 * NW) * 16);
+  auto k = dense_nv_kernel<NW, CPL, RPL, BT>;
+  const int lds = (B + 1) * (cols / 8) * 16;       // the staged tokens and one slot for positions past them
+  static const bool lds_ok = allow_dynamic_lds(k, (BT + 1) * (CPL * 64) * 16);
   (void)lds_ok;
   const int per = NW * 4 * RPL;
   hipLaunchKernelGGL(k, dim3((rows + per - 1) / per), dim3(64 * NW), lds, st, codes, scales, gscale, x, B, rows,
@@ -1674,11 +1681,17 @@ hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int d
   const int dcols = dense ? a.SI : 0;
   const bool bf = (a.flags & FLINT_W_BF16) != 0;
   if (dense && !bf && dense_nv_supported(a.SI, a.B)) {      // W [H][SI] . x[B][SI]
+    // one-wave workgroups for one token (more of them resident per CU: a
+    // 2048-column LM head ran at 67 % of HBM peak against 57 % with 8
+    // waves); four waves for a batch, whose 8 staged tokens each workgroup
+    // would otherwise read again
     const int resid = dense_epilogue == FLINT_EPI_RESIDUAL ? 1 : 0;
-    return a.SI == 2048 ? dense_nv_launch<8, 4, 2>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.SI,
-                                                    a.out, aux, resid, st)
-                        : dense_nv_launch<8, 8, 1>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.SI,
-                                                    a.out, aux, resid, st);
+#define FLINT_DENSE_NV(NW_, CPL_, RPL_, BT_)                                                                   \
+  dense_nv_launch<NW_, CPL_, RPL_, BT_>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.SI, a.out,   \
+                                        aux, resid, st)
+    if (a.SI == 2048) return a.B == 1 ? FLINT_DENSE_NV(1, 4, 2, 1) : FLINT_DENSE_NV(4, 4, 2, kMaxB);
+    return a.B == 1 ? FLINT_DENSE_NV(1, 8, 1, 1) : FLINT_DENSE_NV(4, 8, 1, kMaxB);
+#undef FLINT_DENSE_NV
   }
   if (a.B == 1)
     return bf ? down_dispatch_g<FMT_BF16, 1>(a, ws, dense, dense_epilogue, hin, hs, ht, dcols, aux, st)
