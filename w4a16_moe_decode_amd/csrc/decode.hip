@@ -912,10 +912,13 @@ void gate_up_batch_kernel(LayerArgs a, DecodeWs ws, uint16_t* hout,
 // a row group owns the CPL consecutive chunks li * CPL .. li * CPL + CPL - 1
 // (64 * CPL bytes of codes, 2 * CPL of scales), so a row's cross-lane sum is
 // four steps, paid once per CPL chunks.  A wave holds 4 rows, a workgroup
-// NW * 4.  The slot table entry is read first (scalar loads, one round
-// trip); the weight loads follow, then the activations of the slot's tokens
-// are staged in LDS (every load of the workgroup in flight at once; the
-// staging waits for the weights, as loads complete in order).  The expert
+// NW * 4 (small workgroups: the grid of ~45 slots x 32 row tiles then
+// streams through the CUs instead of running as one full round and a
+// latency-bound second round).  The slot table entry is read first (scalar
+// loads, one round trip); the weight loads follow, then the activations of
+// the slot's tokens are copied into LDS (every load of the workgroup in
+// flight at once; the copies complete after the weights, as loads complete
+// in order).  The expert
 // and the matrix bases are wave-uniform; each lane adds a 32-bit offset of
 // its row and chunks, taken once.  LDS layout: staged token i, quad m of the
 // lane's chunk c at s_x[i * q8 + (c * 4 + m) * 16 + li], so the 16 lanes of
@@ -978,24 +981,29 @@ void gate_up_nv_batch_kernel(LayerArgs a, DecodeWs ws, uint16_t* hout, int h_slo
       if (m) { tokp |= (uint32_t)(__ffs(m) - 1) << (4 * i); m &= m - 1u; }
   }
   // activations: LDS position q of staged token i holds columns
-  // 32 * (CPL * (q % 16) + (q / 16) / 4) + 8 * ((q / 16) % 4); q8 <= NT.
-  // Every load and store is made (a conditional one would draw its load into
-  // the branch behind a full wait): positions out of range read the first
-  // quad and write this thread's slot past the staged tokens.
+  // 32 * (CPL * (q % 16) + (q / 16) / 4) + 8 * ((q / 16) % 4), q < q8 = H / 8.
+  // They are copied by the load units straight into LDS (global_load_lds:
+  // lane l of a wave writes the l-th 16 bytes after the wave's base, and
+  // positions q = threadIdx.x + NT * kq are consecutive within a wave), so
+  // no registers hold them and a workgroup of any width stages all q8
+  // positions; positions of tokens past the slot's are not copied.
   {
-    const int q = threadIdx.x;
-    const int qli = q % G, qcm = q / G;
-    const int col = 32 * (CPL * qli + qcm / QPC) + 8 * (qcm % QPC);
-    uint4 xv[BT];
+    constexpr int KQ = CPL * 64 / NT;              // positions per thread (H = 512 * CPL)
+    static_assert(KQ >= 1 && KQ * NT == CPL * 64, "staging layout");
 #pragma unroll
-    for (int i = 0; i < BT; ++i) {
-      const int t = (tokp >> (4 * i)) & 15;
-      const bool ok = q < q8 && i < n;
-      xv[i] = *reinterpret_cast<const uint4*>(ok ? xsrc + (size_t)t * H + col : xsrc);
+    for (int kq = 0; kq < KQ; ++kq) {
+      const int q = threadIdx.x + NT * kq;
+      const int qli = q % G, qcm = q / G;
+      const int col = 32 * (CPL * qli + qcm / QPC) + 8 * (qcm % QPC);
+#pragma unroll
+      for (int i = 0; i < BT; ++i) {
+        const int t = (tokp >> (4 * i)) & 15;
+        uint4* dst = s_x + i * q8 + NT * kq + (threadIdx.x & ~63);
+        if (i < n) __builtin_amdgcn_global_load_lds(xsrc + (size_t)t * H + col, dst, 16, 0, 0);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < BT; ++i) s_x[q < q8 && i < n ? i * q8 + q : a.B * q8 + q] = xv[i];
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);         // this wave's copies (and weights) are in
   __syncthreads();
 
   float ag[BT], au[BT];
@@ -1432,7 +1440,7 @@ hipError_t gate_up_batch_launch(const LayerArgs& a, const DecodeWs& ws, uint16_t
 template <int CPL>
 hipError_t gate_up_nv_batch_launch(const LayerArgs& a, const DecodeWs& ws, uint16_t* hout, int hs, int ht,
                                    int rows, hipStream_t st) {
-  constexpr int NW = 8;
+  constexpr int NW = 4;                           // 16 rows per workgroup (8 waves: +2.6 us at batch 8)
   const int tiles = (rows + NW * 4 - 1) / (NW * 4);
   const int slots = decode_max_slots({a.H, a.E, a.I, a.SI, a.K, 0, 0.f}, a.B);
   auto k = gate_up_nv_batch_kernel<NW, CPL>;
