@@ -32,7 +32,8 @@ def _bf16_of(src, ts):
                         dtype=torch.float32).to(torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("rows,cols,batch", [(5632, 2048, 1), (5632, 2048, 8), (192, 320, 3), (64, 64, 2)])
+@pytest.mark.parametrize("rows,cols,batch", [(5632, 2048, 1), (5632, 2048, 8), (960, 2048, 3), (320, 4096, 1),
+                                             (320, 4096, 2), (192, 320, 3), (64, 64, 2)])
 @pytest.mark.parametrize("norm", [False, True])
 @pytest.mark.parametrize("wbf16", [False, True])
 def test_swiglu_pair(rows, cols, batch, norm, wbf16):

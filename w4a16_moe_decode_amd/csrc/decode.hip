@@ -1539,27 +1539,37 @@ hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) 
 // to every token.  Every load and LDS store is made (rows past the matrix
 // read row 0 and are not stored; token positions past the batch read token
 // 0 and are stored past the staged tokens).  BT is the token capacity (1 for
-// the one-token variant, so that its staging registers stay few).
-template <int NW, int CPL, int RPL, int BT>
+// the one-token variant, so that its staging registers stay few).  With SW
+// the matrix is the SwiGLU pair [2][rows][cols]: lane group g of a wave takes
+// the gate row (row set 0) and the up row (set 1) of the same index, and
+// writes h = BF16(BF16(SiLU(BF16(g))) * BF16(u)); with NORM every workgroup
+// first RMS-normalises the tokens it stages (float64 mean of squares,
+// BF16(BF16(x / rms) * gamma), as the other kernels do).
+template <int NW, int CPL, int RPL, int BT, bool SW, bool NORM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                      const float* __restrict__ gscale, const uint16_t* __restrict__ x, int B, int rows, int cols,
-                     uint16_t* y, const uint16_t* aux, int resid) {
+                     uint16_t* y, const uint16_t* aux, int resid, const uint16_t* __restrict__ gamma, float eps) {
   constexpr int G = 16, QPC = 4, NT = 64 * NW;
   constexpr int KQ = CPL / NW;                     // staged positions per thread: cols / 8 = KQ * NT
   static_assert(CPL % NW == 0, "staging layout");
+  static_assert(!SW || RPL == 2, "the SwiGLU pair takes row set 0 from gate, 1 from up");
   extern __shared__ uint4 s_x[];
+  __shared__ double s_ss[NW][BT];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int grp = lane / G, li = lane % G;
-  const int rbase = (blockIdx.x * NW + wave) * 4 * RPL + grp;     // row of set p: rbase + 4 p
+  // output row of row set p (SW: row r of the gate (p = 0) and up (p = 1)
+  // matrices, stacked as [2][rows][cols])
+  const int r0 = SW ? (blockIdx.x * NW + wave) * 4 + grp : (blockIdx.x * NW + wave) * 4 * RPL + grp;
+  auto out_row = [&](int p) { return SW ? r0 : r0 + 4 * p; };
   const int q8 = cols / 8;
 
   uint4 wc[RPL][CPL];
   uint32_t sc2[RPL][CPL / 2];
 #pragma unroll
   for (int p = 0; p < RPL; ++p) {
-    const int r = rbase + 4 * p;
-    const uint32_t rc = r < rows ? (uint32_t)r : 0u;
+    const int r = out_row(p);
+    const uint32_t rc = (r < rows ? (uint32_t)r : 0u) + (SW && p == 1 ? (uint32_t)rows : 0u);
     const uint32_t oc = rc * ((uint32_t)cols / 2) + (uint32_t)li * 16u * CPL;
     const uint32_t os = rc * ((uint32_t)cols / 16) + (uint32_t)li * 2u * CPL;
 #pragma unroll
@@ -1567,7 +1577,7 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
 #pragma unroll
     for (int c = 0; c < CPL; c += 2) sc2[p][c / 2] = reinterpret_cast<const uint32_t*>(scales + os)[c / 2];
   }
-  const float g = gscale[0];
+  const float g0 = gscale[0], g1 = SW ? gscale[1] : 0.f;
   // residual values of this lane's rows, fetched early (always: without a
   // residual, or past the batch or the matrix, they read y's first element)
   uint16_t xr[RPL][BT];
@@ -1576,18 +1586,43 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
   for (int p = 0; p < RPL; ++p)
 #pragma unroll
     for (int i = 0; i < BT; ++i) {
-      const int r = rbase + 4 * p;
+      const int r = out_row(p);
       const bool ok = resid && i < B && r < rows;
       xr[p][i] = ab[ok ? (size_t)i * rows + r : 0];
     }
+  // tokens (and gamma) into LDS; with NORM each thread first adds the
+  // squares of its positions, and the tokens are normalised in LDS after the
+  // barrier (gamma staged at s_x[(B + 1) * q8 + q]), so no staged value
+  // stays in a register across it
   {
-    uint4 xv[KQ][BT];
+    uint4 xv[KQ][BT], gv[KQ];
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
       const int q = threadIdx.x + NT * kq;
       const int col = 32 * (CPL * (q % G) + (q / G) / QPC) + 8 * ((q / G) % QPC);
 #pragma unroll
       for (int i = 0; i < BT; ++i) xv[kq][i] = *reinterpret_cast<const uint4*>(x + (size_t)(i < B ? i : 0) * cols + col);
+      if constexpr (NORM) gv[kq] = *reinterpret_cast<const uint4*>(gamma + col);
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int i = 0; i < BT; ++i) {
+        double ss0 = 0.0, ss1 = 0.0;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+          const uint32_t w4[4] = {xv[kq][i].x, xv[kq][i].y, xv[kq][i].z, xv[kq][i].w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const double lo = bf16_lo(w4[m]), hi = bf16_hi(w4[m]);
+            ss0 = fma(lo, lo, ss0);
+            ss1 = fma(hi, hi, ss1);
+          }
+        }
+        const double ssw = wave_sum_f64(ss0 + ss1);
+        if (lane == 0) s_ss[wave][i] = ssw;
+      }
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) s_x[(B + 1) * q8 + threadIdx.x + NT * kq] = gv[kq];
     }
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
@@ -1597,6 +1632,24 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
     }
   }
   __syncthreads();
+  if constexpr (NORM) {
+    // RMSNorm of every token, as in the other decode kernels: the mean of
+    // squares and the square root in float64, BF16(BF16(x / rms) * gamma)
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      if (i >= B) break;
+      double ss = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ss += s_ss[w][i];
+      const Rms rms = make_rms(sqrt(ss / (double)cols + (double)eps));
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        const int q = threadIdx.x + NT * kq;
+        s_x[i * q8 + q] = rms_norm_8(s_x[i * q8 + q], s_x[(B + 1) * q8 + q], rms);
+      }
+    }
+    __syncthreads();
+  }
 
   float acc[RPL][BT];
 #pragma unroll
@@ -1622,39 +1675,75 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
       for (int p = 0; p < RPL; ++p) acc[p][i] += chunk_dot(d[p], xc);
     }
   }
-#pragma unroll
-  for (int p = 0; p < RPL; ++p) {
-    const int r = rbase + 4 * p;
+  if constexpr (SW) {
+    // h = BF16(BF16(SiLU(BF16(g)))  * BF16(u)), the SwiGLU rounding points
 #pragma unroll
     for (int i = 0; i < BT; ++i) {
       if (i >= B) break;
-      const float v = group_sum<G>(acc[p][i]);
-      if (li == 0 && r < rows) {
-        float o = round_bf16(v * g);
-        if (resid) o = bf16_bits_to_f32(xr[p][i]) + o;
-        y[(size_t)i * rows + r] = f32_to_bf16_bits(o);
+      const float gsum = group_sum<G>(acc[0][i]);
+      const float usum = group_sum<G>(acc[1][i]);
+      if (li == 0 && r0 < rows) {
+        const float gv = round_bf16(gsum * g0);
+        const float uv = round_bf16(usum * g1);
+        const float av = round_bf16(silu_f32(gv));
+        y[(size_t)i * rows + r0] = f32_to_bf16_bits(av * uv);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < RPL; ++p) {
+      const int r = out_row(p);
+#pragma unroll
+      for (int i = 0; i < BT; ++i) {
+        if (i >= B) break;
+        const float v = group_sum<G>(acc[p][i]);
+        if (li == 0 && r < rows) {
+          float o = round_bf16(v * g0);
+          if (resid) o = bf16_bits_to_f32(xr[p][i]) + o;
+          y[(size_t)i * rows + r] = f32_to_bf16_bits(o);
+        }
       }
     }
   }
 }
 
-// the tall-matrix projection for NVFP4 weights with 2048 or 4096 columns;
-// false when the shape is outside what it covers
+// the tall-matrix kernel covers NVFP4 weights with 2048 or 4096 columns
 bool dense_nv_supported(int cols, int batch) {
   return (cols == 2048 || cols == 4096) && batch >= 1 && batch <= kMaxB;
 }
 
-template <int NW, int CPL, int RPL, int BT>
+template <int NW, int CPL, int RPL, int BT, bool SW, bool NORM>
 hipError_t dense_nv_launch(const uint8_t* codes, const uint8_t* scales, const float* gscale, const uint16_t* x,
-                           int B, int rows, int cols, uint16_t* y, const uint16_t* aux, int resid, hipStream_t st) {
-  auto k = dense_nv_kernel<NW, CPL, RPL, BT>;
-  const int lds = (B + 1) * (cols / 8) * 16;       // the staged tokens and one slot for positions past them
-  static const bool lds_ok = allow_dynamic_lds(k, (BT + 1) * (CPL * 64) * 16);
+                           int B, int rows, int cols, uint16_t* y, const uint16_t* aux, int resid,
+                           const uint16_t* gamma, float eps, hipStream_t st) {
+  auto k = dense_nv_kernel<NW, CPL, RPL, BT, SW, NORM>;
+  // the staged tokens, one slot for positions past them, gamma
+  const int lds = (B + 2) * (cols / 8) * 16;
+  static const bool lds_ok = allow_dynamic_lds(k, (BT + 2) * (CPL * 64) * 16);
   (void)lds_ok;
-  const int per = NW * 4 * RPL;
+  const int per = SW ? NW * 4 : NW * 4 * RPL;
   hipLaunchKernelGGL(k, dim3((rows + per - 1) / per), dim3(64 * NW), lds, st, codes, scales, gscale, x, B, rows,
-                     cols, y, aux, resid);
+                     cols, y, aux, resid, gamma, eps);
   return hipGetLastError();
+}
+
+// SwiGLU pair [2][rows][cols] -> h [B][rows], with the RMSNorm of x fused
+// when asked; one-wave workgroups for one token, four waves for a batch
+hipError_t dense_nv_swiglu(const LayerArgs& a, bool norm, hipStream_t st) {
+#define FLINT_DNV_SW(NW_, CPL_, BT_, N_)                                                                     \
+  dense_nv_launch<NW_, CPL_, 2, BT_, true, N_>(a.sh_gu_codes, a.sh_gu_scales, a.sh_gscale, a.x, a.B, a.SI, a.H, \
+                                               a.out, nullptr, 0, a.gamma, a.eps, st)
+  if (a.H == 2048) {
+    if (norm) return a.B == 1 ? FLINT_DNV_SW(1, 4, 1, true) : FLINT_DNV_SW(4, 4, kMaxB, true);
+    return a.B == 1 ? FLINT_DNV_SW(1, 4, 1, false) : FLINT_DNV_SW(4, 4, kMaxB, false);
+  }
+  return norm ? FLINT_DNV_SW(1, 8, 1, true) : FLINT_DNV_SW(1, 8, 1, false);   // 4096 columns, one token
+#undef FLINT_DNV_SW
+}
+// shapes of the SwiGLU pair this path takes (4096 columns for a batch would
+// not fit the registers of four waves per SIMD)
+bool dense_nv_swiglu_supported(int cols, int batch) {
+  return dense_nv_supported(cols, batch) && (cols == 2048 || batch == 1);
 }
 
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm,
@@ -1665,6 +1754,7 @@ hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bo
   const int hs = dense ? 0 : kMaxB * imax;
   const int ht = dense ? a.SI : imax;
   const bool bf = (a.flags & FLINT_W_BF16) != 0;
+  if (dense && !bf && dense_nv_swiglu_supported(a.H, a.B)) return dense_nv_swiglu(a, norm, st);
   if (a.B == 1)
     return bf ? gate_up_dispatch_g<FMT_BF16, 1>(a, ws, dense, norm, hout, hs, ht, imax, st)
               : gate_up_dispatch_g<FMT_NVFP4, 1>(a, ws, dense, norm, hout, hs, ht, imax, st);
@@ -1695,8 +1785,8 @@ hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int d
     // would otherwise read again
     const int resid = dense_epilogue == FLINT_EPI_RESIDUAL ? 1 : 0;
 #define FLINT_DENSE_NV(NW_, CPL_, RPL_, BT_)                                                                   \
-  dense_nv_launch<NW_, CPL_, RPL_, BT_>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.SI, a.out,   \
-                                        aux, resid, st)
+  dense_nv_launch<NW_, CPL_, RPL_, BT_, false, false>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H,  \
+                                                      a.SI, a.out, aux, resid, nullptr, 0.f, st)
     if (a.SI == 2048) return a.B == 1 ? FLINT_DENSE_NV(1, 4, 2, 1) : FLINT_DENSE_NV(4, 4, 2, kMaxB);
     return a.B == 1 ? FLINT_DENSE_NV(1, 8, 1, 1) : FLINT_DENSE_NV(4, 8, 1, kMaxB);
 #undef FLINT_DENSE_NV
