@@ -1523,6 +1523,8 @@ hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) 
   return route_dispatch<kMaxB>(a, ws, st);
 }
 
+namespace {
+
 // ------------------------------------- dense NVFP4 projection, tall matrix --
 // y[t][r] = BF16(g * sum_c W[r][c] x[t][c]), or BF16(aux[t][r] + that), for a
 // packed NVFP4 matrix W [rows][cols] with many rows and 1..8 tokens: the
@@ -1745,6 +1747,8 @@ hipError_t dense_nv_swiglu(const LayerArgs& a, bool norm, hipStream_t st) {
 bool dense_nv_swiglu_supported(int cols, int batch) {
   return dense_nv_supported(cols, batch) && (cols == 2048 || batch == 1);
 }
+
+}  // namespace
 
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm,
                           hipStream_t st) {
