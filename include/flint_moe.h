@@ -73,15 +73,10 @@ extern "C" {
                                     (by default a batch-1 NVFP4 call with
                                     hidden 2048 or 4096 runs as one launch; see
                                     flint_moe_decode_path) */
-#define FLINT_SINGLE_BATCH 0x20u /* decode, batch 2..8: run as one launch when
-                                    the shape allows (slower than the three
-                                    kernels on MI355X at present: one wave per
-                                    SIMD leaves its VALU latency exposed) */
 
 /* decode paths reported by flint_moe_decode_path */
 #define FLINT_PATH_SPLIT        0  /* three kernels: route, gate/up, down    */
 #define FLINT_PATH_SINGLE_ONE   1  /* one launch, batch 1                    */
-#define FLINT_PATH_SINGLE_BATCH 2  /* one launch, batch 2..8                 */
 
 /* source NVFP4 super-block byte orders accepted by the repack */
 #define FLINT_SRC_INTERLEAVED   0  /* 4 x [scale byte, 8 code bytes]          */
@@ -94,6 +89,28 @@ extern "C" {
 #define FLINT_EPI_RESIDUAL 2   /* y = BF16(aux + BF16(g * W x))                  */
 
 #define FLINT_MAX_DECODE_BATCH 8
+
+/* Workspace header (byte offsets into the caller's workspace; each field is
+ * one uint32):
+ *   FLINT_WS_ERROR_OFFSET       the hand-off error word: 0 normally; set to 1
+ *                               by a single-launch or route kernel whose
+ *                               bounded wait for another workgroup's word
+ *                               gave up.  That can only happen when the grid
+ *                               of a single-launch call is not resident all
+ *                               at once (another kernel holding compute units
+ *                               meanwhile).  The kernel still exits, but the
+ *                               results of that call are undefined and so are
+ *                               those of later calls on the workspace until
+ *                               it is zero-filled again.  Read it with
+ *                               flint_moe_workspace_error.
+ *   FLINT_WS_WAIT_LIMIT_OFFSET  bound of each such wait, in reloads of the
+ *                               awaited words; 0 (the zero-filled default)
+ *                               means 2^20.  A caller may store a smaller
+ *                               value to bound how long a call can wait. */
+#define FLINT_WS_ERROR_OFFSET      512
+#define FLINT_WS_WAIT_LIMIT_OFFSET 768
+#define FLINT_WS_HEADER_BYTES      1024
+
 #define FLINT_MAX_TOP_K        8
 #define FLINT_MAX_EXPERTS      256
 
@@ -164,12 +181,19 @@ FLINT_API const char* flint_status_string(int32_t status);
 FLINT_API int32_t flint_nvfp4_packed_bytes(int64_t n_mats, int64_t rows, int64_t cols,
                                  int64_t* code_bytes, int64_t* scale_bytes);
 
-/* Workspace bytes flint_moe_decode (max_tokens <= 8) or flint_moe_prefill
- * (any max_tokens >= 1) needs for this shape; negative = a FLINT_ERR_* code
- * negated.  The workspace must be zero-filled once after allocation (it
- * carries a launch counter from call to call); calls that share one
- * workspace must be ordered on one stream. */
+/* Workspace bytes that flint_moe_decode (max_tokens <= 8) and
+ * flint_moe_prefill (up to max_tokens tokens) need for this shape; negative
+ * = a FLINT_ERR_* code negated.  The decode part (header, launch counters,
+ * hand-off words) comes first and the prefill part after it, so decode and
+ * prefill calls may share one workspace.  The workspace must be zero-filled
+ * once after allocation (it carries a launch counter from call to call);
+ * calls that share one workspace must be ordered on one stream. */
 FLINT_API int64_t flint_moe_workspace_bytes(const flint_moe_shape* shape, int32_t max_tokens);
+
+/* Enqueues a copy of the workspace's hand-off error word (see
+ * FLINT_WS_ERROR_OFFSET) into dst (device or pinned host memory, 4 bytes) on
+ * `stream`, after the calls already enqueued there. */
+FLINT_API int32_t flint_moe_workspace_error(const void* ws, int64_t ws_bytes, uint32_t* dst, void* stream);
 
 /* ------------------------------------------------------------------ repack -- */
 
@@ -229,14 +253,17 @@ FLINT_API int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int
  *   gamma     (device) BF16 [H], required with FLINT_PRE_RMSNORM
  *   ws        (device) workspace of at least flint_moe_workspace_bytes(shape, batch)
  * With NVFP4 weights and hidden 2048 or 4096 (I, SI <= 2048) a batch-1 call
- * is one launch of a persistent grid (one workgroup per compute unit) whose
- * phases hand data over through epoch-tagged words in the workspace; so is a
- * batch 2..8 call with FLINT_SINGLE_BATCH when also batch * (K + 1) *
- * max(I, SI) <= 32768.  Every other call, and any call with FLINT_SPLIT,
- * enqueues three kernels: route (RMSNorm, router GEMV, top-k, expert set),
- * gate/up (+SiLU*up), down (weighted combine, shared expert, residual).
- * flint_moe_decode_path tells which.  All paths give the same result up to
- * fp32 summation order. */
+ * is one launch of a persistent grid (at most one workgroup per compute
+ * unit) whose phases hand data over through epoch-tagged words in the
+ * workspace.  That grid relies on all of its workgroups running at once:
+ * the call checks at launch that the device can hold the whole grid (and
+ * runs the three kernels instead when it cannot), and the caller must not
+ * run other kernels on the device concurrently (on other streams or in
+ * other processes) while it runs; a caller that does should set
+ * FLINT_SPLIT.  Every other call enqueues three kernels: route (RMSNorm,
+ * router GEMV, top-k, expert set), gate/up (+SiLU*up), down (weighted
+ * combine, shared expert, residual).  flint_moe_decode_path tells which.
+ * All paths give the same result up to fp32 summation order. */
 FLINT_API int32_t flint_moe_decode(const flint_moe_shape* shape, const flint_moe_weights* weights,
                          const void* x, int32_t batch, void* out, int32_t* topk_idx,
                          float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
@@ -283,7 +310,7 @@ FLINT_API int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const fli
                                          int64_t ws_bytes, void* stream);
 
 /* Which kernels flint_moe_decode runs for this shape (flags included) and
- * batch: FLINT_PATH_SPLIT, FLINT_PATH_SINGLE_ONE or FLINT_PATH_SINGLE_BATCH.
+ * batch: FLINT_PATH_SPLIT or FLINT_PATH_SINGLE_ONE.
  * Reads only the shape; enqueues nothing.  Returns -status for an invalid
  * shape (-FLINT_ERR_INVALID_ARG, -FLINT_ERR_UNSUPPORTED) or a batch outside
  * 1..8 (-FLINT_ERR_UNSUPPORTED). */

@@ -34,8 +34,3 @@ def round_bf16(x) -> np.ndarray:
     out[finite] = q
     return out
 
-
-def bf16_bits(x) -> np.ndarray:
-    """Bit patterns (uint16) of values that are already bfloat16."""
-    x = np.asarray(x, dtype=np.float64).astype(np.float32)
-    return (x.view(np.uint32) >> 16).astype(np.uint16)

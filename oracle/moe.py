@@ -31,7 +31,7 @@ Readings where the pages are silent (each is listed in the design notes):
 from __future__ import annotations
 
 import dataclasses
-from typing import Callable, Optional, Sequence
+from typing import Callable, Optional
 
 import numpy as np
 
@@ -62,8 +62,10 @@ def rmsnorm(x, gamma, eps: float = 1e-6):
 def topk_select(scores, k: int):
     """Indices of the k largest scores of one token, ordered by descending
     score with ties to the lower index, and the gap between the k-th and the
-    (k+1)-th largest score (inf when k equals the number of experts)."""
+    (k+1)-th largest score (inf when k equals the number of experts).  A NaN
+    score (from a NaN router weight) ranks below every number."""
     s = np.asarray(scores, dtype=np.float64)
+    s = np.where(np.isnan(s), -np.inf, s)
     order = np.lexsort((np.arange(s.size), -s))     # primary: -s, then index
     idx = order[:k]
     gap = float(s[order[k - 1]] - s[order[k]]) if k < s.size else float("inf")
@@ -124,16 +126,6 @@ def nvfp4_expert_set(router, gate, up, down, gscale, sh_gate=None, sh_up=None, s
                 decode_source_matrix(down[e], layout, gscale[e, 2]))
 
     router = np.asarray(router, dtype=np.float64)
-    return ExpertSet(router=router, n_experts=router.shape[0], _loader=load)
-
-
-def dense_expert_set(router, experts: Sequence[tuple], shared: Optional[tuple]) -> ExpertSet:
-    """ExpertSet over float64 matrices given directly (W16A16 weights)."""
-    router = np.asarray(router, dtype=np.float64)
-
-    def load(e):
-        return shared if e is None else experts[e]
-
     return ExpertSet(router=router, n_experts=router.shape[0], _loader=load)
 
 

@@ -129,24 +129,22 @@ def test_repack_and_dense_validation_codes():
 def test_decode_path_rules():
     """Which kernels a decode call runs: host logic only, nothing enqueued."""
     flint = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
-    single = fm.FlintMoeShape(2048, 256, 512, 512, 6, fm.FLINT_SINGLE_BATCH, 1e-6)
     assert fm.flint_moe_decode_path(flint, 1) == fm.FLINT_PATH_SINGLE_ONE
-    assert fm.flint_moe_decode_path(single, 1) == fm.FLINT_PATH_SINGLE_ONE
     for b in range(2, 9):
-        assert fm.flint_moe_decode_path(flint, b) == fm.FLINT_PATH_SPLIT      # opt-in only
-        assert fm.flint_moe_decode_path(single, b) == fm.FLINT_PATH_SINGLE_BATCH
+        assert fm.flint_moe_decode_path(flint, b) == fm.FLINT_PATH_SPLIT
+    # the old single-launch batch flag is no longer accepted
+    with pytest.raises(fm.FlintError) as e:
+        fm.flint_moe_decode_path(fm.FlintMoeShape(2048, 256, 512, 512, 6, 0x20, 1e-6), 2)
+    assert e.value.status == fm.FLINT_ERR_UNSUPPORTED
     for flags in (fm.FLINT_SPLIT, fm.FLINT_W_BF16):
         s = fm.FlintMoeShape(2048, 256, 512, 512, 6, flags, 1e-6)
         assert fm.flint_moe_decode_path(s, 1) == fm.FLINT_PATH_SPLIT
         assert fm.flint_moe_decode_path(s, 8) == fm.FLINT_PATH_SPLIT
     tiny = fm.FlintMoeShape(512, 32, 128, 128, 4, 0, 1e-6)          # hidden not a multiple of 2048
     assert fm.flint_moe_decode_path(tiny, 1) == fm.FLINT_PATH_SPLIT
-    # h of every (token, expert) pair must fit the LDS pool (16384 words):
-    # 3 * 9 * 1024 / 2 fits, 4 * 9 * 1024 / 2 does not
-    wide = fm.FlintMoeShape(2048, 48, 512, 1024, 8, fm.FLINT_SINGLE_BATCH, 1e-6)
+    wide = fm.FlintMoeShape(2048, 48, 512, 1024, 8, 0, 1e-6)
     assert fm.flint_moe_decode_path(wide, 1) == fm.FLINT_PATH_SINGLE_ONE
-    assert fm.flint_moe_decode_path(wide, 3) == fm.FLINT_PATH_SINGLE_BATCH
-    assert fm.flint_moe_decode_path(wide, 4) == fm.FLINT_PATH_SPLIT
+    assert fm.flint_moe_decode_path(wide, 3) == fm.FLINT_PATH_SPLIT
     for b in (0, 9):
         with pytest.raises(fm.FlintError) as e:
             fm.flint_moe_decode_path(flint, b)
@@ -182,3 +180,34 @@ def test_decode_stack_validation_codes():
         assert st(shape=fm.FlintMoeShape(2048, 256, 512, 512, 6, flags, 1e-6)) == fm.FLINT_ERR_UNSUPPORTED
     # outside the one-token single-launch envelope (hidden 512)
     assert st(shape=fm.FlintMoeShape(512, 32, 128, 128, 4, 0, 1e-6), ws=v(4096)) == fm.FLINT_ERR_UNSUPPORTED
+
+
+def test_workspace_error_query_validation():
+    """flint_moe_workspace_error checks its arguments before enqueuing the
+    copy of the header's error word."""
+    L = fm.lib()
+    v = ctypes.c_void_p
+    assert L.flint_moe_workspace_error(None, 4096, v(64), None) == fm.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_workspace_error(v(4096), 4096, None, None) == fm.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_workspace_error(v(4100), 4096, v(64), None) == fm.FLINT_ERR_ALIGNMENT
+    assert L.flint_moe_workspace_error(v(4096), 4096, v(66), None) == fm.FLINT_ERR_ALIGNMENT
+    assert L.flint_moe_workspace_error(v(4096), 1000, v(64), None) == fm.FLINT_ERR_WORKSPACE
+    assert fm.WS_ERROR_OFFSET == 512 and fm.WS_WAIT_LIMIT_OFFSET == 768
+
+
+def test_decode_and_prefill_workspace_parts_do_not_overlap():
+    """The prefill part of a workspace starts after the whole decode part, so
+    one workspace serves both kinds of call: the size for T tokens is the
+    decode part plus a prefill part that grows with T."""
+    s = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
+    sizes = [fm.flint_moe_workspace_bytes(s, t) for t in (1, 2, 8, 9, 100, 8192)]
+    assert sizes == sorted(sizes) and len(set(sizes)) == len(sizes)
+    # the decode part alone: a prefill of one token needs more than it
+    L = fm.lib()
+    v = ctypes.c_void_p
+    w = _fake_weights()
+    dec_ok = _decode_status(s, w, ws=4096, ws_bytes=sizes[0])
+    assert dec_ok != fm.FLINT_ERR_WORKSPACE
+    st = L.flint_moe_prefill(ctypes.byref(s), ctypes.byref(w), v(16), 2, v(32), None, None, None,
+                             v(4096), sizes[0], None)
+    assert st == fm.FLINT_ERR_WORKSPACE                 # 2 tokens need more than the 1-token size

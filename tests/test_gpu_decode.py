@@ -90,10 +90,10 @@ def test_results_are_bit_reproducible_and_stages_compose(flint_layer):
     path and on the three-kernel one; running the three stages by hand equals
     one three-kernel call."""
     _, layer = flint_layer
-    runner = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    runner = fm.DecodeRunner(layer, FLINT.top_k, 0)
     split = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SPLIT)
-    assert fm.flint_moe_decode_path(runner.shape, 8) == fm.FLINT_PATH_SINGLE_BATCH
-    x = gen.activations(7, 8, FLINT.hidden).cuda()
+    assert fm.flint_moe_decode_path(runner.shape, 1) == fm.FLINT_PATH_SINGLE_ONE
+    x = gen.activations(7, 1, FLINT.hidden).cuda()
     a = runner(x)
     b = runner(x)
     s1 = split(x)
@@ -101,9 +101,13 @@ def test_results_are_bit_reproducible_and_stages_compose(flint_layer):
     c = torch.empty_like(x)
     for st in range(3):
         split.stage(st, x, c)
+    x8 = gen.activations(8, 8, FLINT.hidden).cuda()
+    d1 = runner(x8)
+    d2 = runner(x8)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(s1, s2) and torch.equal(s1, c)
+    assert torch.equal(d1, d2)
 
 
 def test_rotating_copies_and_workspace_reuse(flint_layer):

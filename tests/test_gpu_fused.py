@@ -1,6 +1,5 @@
-"""The single-launch decode paths (batch 1, and batch 2..8; hidden 2048 or
-4096, NVFP4) against the oracle and against the three-kernel path
-(FLINT_SPLIT)."""
+"""The single-launch decode path (batch 1; hidden 2048 or 4096, NVFP4)
+against the oracle and against the three-kernel path (FLINT_SPLIT)."""
 import pytest
 import torch
 
@@ -39,46 +38,6 @@ def test_fused_against_oracle(shape, flags):
                         runner=r)
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=SHAPE_IDS)
-@pytest.mark.parametrize("flags", FLAG_SETS)
-def test_fused_batch_against_oracle(shape, flags):
-    """Batch 2..8 in one launch; the grid is wider than E for the small
-    expert counts, so the arrival words are exercised too."""
-    src = gen.moe_layer_source(shape, 510 + shape.hidden + shape.n_experts)
-    layer = pack(src)
-    flags |= fm.FLINT_SINGLE_BATCH
-    r = fm.DecodeRunner(layer, shape.top_k, flags)
-    for seed, batch in ((1, 2), (2, 5), (3, 8)):
-        path = fm.flint_moe_decode_path(r.shape, batch)
-        want = fm.FLINT_PATH_SINGLE_BATCH
-        pairs = batch * (shape.top_k + (1 if shape.shared_inter else 0))
-        if pairs * max(shape.inter, shape.shared_inter) > 32768:
-            want = fm.FLINT_PATH_SPLIT          # the h of every pair would not fit in LDS
-        assert path == want
-        run_decode_case(DecodeCase(shape, seed=seed, batch=batch, flags=flags), src=src, layer=layer,
-                        runner=r)
-    assert fm.decode_error_word(r) == 0
-
-
-def test_fused_batch_matches_split_and_is_reproducible():
-    src = gen.moe_layer_source(FLINT, 603)
-    layer = pack(src)
-    fused = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
-    split = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SPLIT)
-    for i, b in enumerate([2, 3, 4, 6, 7, 8]):
-        x = gen.activations(710 + i, b, FLINT.hidden, "cpu", "correlated" if i % 2 else "iid").cuda()
-        ia = torch.empty((b, FLINT.top_k), dtype=torch.int32, device="cuda")
-        ib = torch.empty_like(ia)
-        a = fused(x, topk_idx=ia)
-        a2 = fused(x)
-        c = split(x, topk_idx=ib)
-        torch.cuda.synchronize()
-        assert torch.equal(a, a2)
-        assert torch.equal(ia, ib)
-        compare_outputs(a.cpu().float().numpy(), c.cpu().float().numpy(), "fused vs split")
-    assert fm.decode_error_word(fused) == 0
-
-
 def test_fused_matches_split_and_is_reproducible():
     src = gen.moe_layer_source(FLINT, 600)
     layer = pack(src)
@@ -95,11 +54,12 @@ def test_fused_matches_split_and_is_reproducible():
 
 
 def test_fused_and_split_share_a_workspace():
-    """Batch-1 and batch-n single launches and three-kernel calls alternate on
-    one workspace; the launch epoch keeps their hand-off words apart."""
+    """Batch-1 single launches and three-kernel calls (batch 1 with
+    FLINT_SPLIT, batches 2..8) alternate on one workspace; the launch epoch
+    keeps their hand-off words apart."""
     src = gen.moe_layer_source(FLINT, 601)
     layer = pack(src)
-    r = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    r = fm.DecodeRunner(layer, FLINT.top_k, 0)
     s = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SPLIT)
     s.ws = r.ws
     for i, (b, runner) in enumerate([(1, r), (8, r), (1, s), (1, r), (3, s), (3, r), (1, r), (8, s), (2, r)]):
@@ -110,10 +70,46 @@ def test_fused_and_split_share_a_workspace():
 def test_fused_error_word_stays_clear():
     src = gen.moe_layer_source(FLINT, 602)
     layer = pack(src)
-    r = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_SINGLE_BATCH)
+    r = fm.DecodeRunner(layer, FLINT.top_k, 0)
     for b in (1, 8):
         x = gen.activations(9, b, FLINT.hidden).cuda()
         for _ in range(20):
             r(x)
     torch.cuda.synchronize()
     assert fm.decode_error_word(r) == 0
+
+
+def test_bounded_wait_gives_up_and_sets_error_word():
+    """A wait limit of one reload, stored in the workspace header by the host,
+    makes the single-launch kernel's waits give up before most hand-off words
+    arrive: the kernel still exits and reports it in the error word.  Once the
+    workspace is zero-filled again, calls give the normal result."""
+    src = gen.moe_layer_source(FLINT, 604)
+    layer = pack(src)
+    for stack in (False, True):
+        r = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL)
+        gamma = gen.rmsnorm_gamma(13, FLINT.hidden, "cuda")
+        step = fm.DecodeStep([layer, layer], [gamma, gamma], [], [], FLINT.top_k, stack=True)
+        step.ws = r.ws
+        x = gen.activations(12, 1, FLINT.hidden).cuda()
+
+        def call():
+            if stack:
+                y = x.clone()
+                step(y)
+                return y
+            return r(x, gamma=gamma)
+
+        want = call().clone()
+        torch.cuda.synchronize()
+        assert fm.decode_error_word(r) == 0
+        lim = r.ws[fm.WS_WAIT_LIMIT_OFFSET:fm.WS_WAIT_LIMIT_OFFSET + 4].view(torch.int32)
+        lim.fill_(1)
+        call()
+        torch.cuda.synchronize()
+        assert fm.decode_error_word(r) == 1, f"stack={stack}"
+        r.ws.zero_()
+        got = call()
+        torch.cuda.synchronize()
+        assert fm.decode_error_word(r) == 0
+        assert torch.equal(got, want)

@@ -34,7 +34,10 @@ def run_prefill(shape, src, layer, T, seed, flags=0, x_kind="iid", sample=None, 
     xin = moe.rmsnorm(xo, gen.numpy_f64(gamma)) if flags & fm.FLINT_PRE_RMSNORM else xo
     # routing of every token
     r = moe.route(xin, ex.router, shape.top_k, renorm)
-    forced = check_routing(idx.cpu().numpy(), wts.cpu().numpy(), r, renorm)
+    idx_np = idx.cpu().numpy()
+    forced = check_routing(idx_np, wts.cpu().numpy(), r, renorm)
+    if callable(sample):
+        sample = sample(idx_np)
     toks = np.arange(T) if sample is None else np.asarray(sample)
     want, _ = moe.moe_layer(xin[toks], ex, shape.top_k, renorm, forced_idx=forced[toks])
     if flags & fm.FLINT_RESIDUAL:
@@ -82,14 +85,47 @@ def test_flint_prefill_1024(flint):
     run_prefill(FLINT, src, layer, 1024, 38, sample=np.arange(0, 1024, 7))
 
 
+TILE_ROWS = 128          # rows of one grouped-GEMM M-tile
+
+
+def tile_edge_tokens(idx: np.ndarray, with_shared: bool = True) -> np.ndarray:
+    """The tokens in the first and the last row of every M-tile of the
+    grouped GEMMs.  Expert e's rows are its (token, slot) pairs in token
+    order (the stable permutation by expert, then token), cut into tiles of
+    128 rows; the shared expert's rows are all tokens in order.  ``idx`` is
+    the GPU's routing, already checked against the oracle token by token."""
+    T = idx.shape[0]
+    out = set()
+    for e in np.unique(idx):
+        toks = np.nonzero((idx == e).any(1))[0]
+        for m0 in range(0, len(toks), TILE_ROWS):
+            out.add(int(toks[m0]))
+            out.add(int(toks[min(m0 + TILE_ROWS, len(toks)) - 1]))
+    if with_shared:
+        for m0 in range(0, T, TILE_ROWS):
+            out.update((m0, min(m0 + TILE_ROWS, T) - 1))
+    return np.array(sorted(out))
+
+
 @pytest.mark.parametrize("x_kind", ["iid", "correlated"])
 def test_flint_prefill_8192(flint, x_kind):
+    """Every M-tile of every expert group (several per expert, up to ~25 for
+    the hottest expert under skew) and of the shared group has its first and
+    last row compared with the oracle."""
     src, layer = flint
-    rng = np.random.default_rng(5)
-    sample = np.sort(rng.choice(8192, 48, replace=False))
+    seen = {}
+
+    def sample(idx):
+        seen["toks"] = tile_edge_tokens(idx)
+        return seen["toks"]
+
     idx = run_prefill(FLINT, src, layer, 8192, 39, fm.FLINT_RENORM, x_kind=x_kind, sample=sample)
     h = np.bincount(idx.reshape(-1), minlength=FLINT.n_experts)
     assert h.sum() == 8192 * FLINT.top_k
+    n_tiles = sum((c + TILE_ROWS - 1) // TILE_ROWS for c in h) + 8192 // TILE_ROWS
+    assert len(seen["toks"]) >= min(n_tiles, 8192) // 2
+    if x_kind == "correlated":
+        assert h.max() > 4 * TILE_ROWS          # several M-tiles for one expert
 
 
 def test_prefill_matches_decode(flint):

@@ -6,6 +6,7 @@ input, or an invariant the method implies (unselected experts contribute
 nothing, the shared expert is always added, prefill equals per-token decode).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -59,6 +60,23 @@ def test_topk_matches_rank_count_bruteforce(seed):
     assert gap == srt[k - 1] - srt[k]
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_nan_score_ranks_lowest(seed):
+    """A NaN score is never selected while k numbers remain: the selection
+    equals the top-k of the scores with the NaN entries taken out."""
+    rng = np.random.default_rng(100 + seed)
+    n, k = 256, 6
+    s = rng.random(n)
+    bad = rng.choice(n, 3, replace=False)
+    bad[0] = int(np.argmax(s))                     # the largest score becomes NaN
+    s[bad] = np.nan
+    keep = np.array([i for i in range(n) if i not in set(bad.tolist())])
+    idx, gap = moe.topk_select(s, k)
+    sub, sub_gap = moe.topk_select(s[keep], k)
+    assert list(idx) == list(keep[sub]) and gap == sub_gap
+    assert not set(idx.tolist()) & set(bad.tolist())
+
+
 def test_zero_input_ties_select_lowest_indices():
     src = gen.moe_layer_source(SH, 5)
     ex = _experts_from_source(src)
@@ -104,6 +122,19 @@ def test_rmsnorm_matches_torch_rms_norm_then_rounds():
     # constant input: x / rms(x) = sign(x) up to eps, so xn = gamma
     c = np.full((1, 512), 3.0)
     np.testing.assert_array_equal(moe.rmsnorm(c, gamma, 1e-6)[0], gamma)
+
+
+def test_rmsnorm_golden_small_mean_square():
+    """mean(x^2) of the order of eps: where eps sits decides the result
+    (hand-derived rows in tests/golden/rmsnorm_small_ms.txt)."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "rmsnorm_small_ms.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 2
+    for _, xs, gs, want in rows:
+        x = np.array([float.fromhex(v) for v in xs.split(",")])[None, :]
+        gamma = np.array([float(v) for v in gs.split(",")])
+        got = moe.rmsnorm(x, gamma, 1e-6)[0]
+        np.testing.assert_array_equal(got, np.array([float(v) for v in want.split(",")]))
 
 
 # ------------------------------------------------------- expert structure --

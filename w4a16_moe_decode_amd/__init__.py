@@ -34,11 +34,9 @@ FLINT_W_BF16 = 0x2
 FLINT_PRE_RMSNORM = 0x4
 FLINT_RESIDUAL = 0x8
 FLINT_SPLIT = 0x10
-FLINT_SINGLE_BATCH = 0x20
 
 FLINT_PATH_SPLIT = 0
 FLINT_PATH_SINGLE_ONE = 1
-FLINT_PATH_SINGLE_BATCH = 2
 
 FLINT_SRC_INTERLEAVED = 0
 FLINT_SRC_SCALES_FIRST = 1
@@ -49,11 +47,13 @@ FLINT_EPI_SWIGLU = 1
 FLINT_EPI_RESIDUAL = 2
 
 MAX_DECODE_BATCH = 8
+WS_ERROR_OFFSET = 512
+WS_WAIT_LIMIT_OFFSET = 768
 
 # Every symbol the header declares (checked by the CPU export test).
 EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
-    "flint_moe_workspace_bytes", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
+    "flint_moe_workspace_bytes", "flint_moe_workspace_error", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
     "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
     "flint_moe_prefill", "flint_dense_gemv",
 )
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.flint_nvfp4_packed_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.flint_moe_workspace_bytes.restype = i64
         L.flint_moe_workspace_bytes.argtypes = [ctypes.POINTER(FlintMoeShape), i32]
+        L.flint_moe_workspace_error.restype = i32
+        L.flint_moe_workspace_error.argtypes = [vp, i64, vp, vp]
         L.flint_moe_repack.restype = i32
         L.flint_moe_repack.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp]
         L.flint_moe_unpack.restype = i32
@@ -161,6 +163,13 @@ def flint_moe_workspace_bytes(shape: FlintMoeShape, max_tokens: int) -> int:
     if v < 0:
         raise FlintError("flint_moe_workspace_bytes", -v)
     return v
+
+
+def flint_moe_workspace_error(ws, ws_bytes, dst, stream=None):
+    """Enqueue a copy of the workspace's hand-off error word into ``dst``
+    (a device int32/uint32 tensor of at least one element)."""
+    _check("flint_moe_workspace_error",
+           lib().flint_moe_workspace_error(_p(ws), int(ws_bytes), _p(dst), _stream(stream)))
 
 
 def flint_moe_repack(src, n_mats, rows, cols, src_layout, dst_codes, dst_scales, dst_mat_stride=1,
@@ -364,10 +373,12 @@ def pack_moe_layer(router: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, d
 
 
 def decode_error_word(runner) -> int:
-    """The decode workspace's hand-off error word (1 if a bounded wait ever
-    timed out; it stays 0 in normal operation).  It is the third 256-byte
-    field of the workspace (after the ticket and the epoch)."""
-    return int(runner.ws[512:516].view(torch.int32).item())
+    """The workspace's hand-off error word (1 if a bounded wait ever timed
+    out; it stays 0 in normal operation), read through
+    flint_moe_workspace_error on the current stream."""
+    dst = torch.zeros(1, dtype=torch.int32, device=runner.ws.device)
+    flint_moe_workspace_error(runner.ws, runner.ws_bytes, dst)
+    return int(dst.item())
 
 
 class DecodeRunner:

@@ -28,8 +28,7 @@ int check_shape(const flint_moe_shape* s) {
   if (s->hidden > 4096) return FLINT_ERR_UNSUPPORTED;
   if (s->n_experts > FLINT_MAX_EXPERTS) return FLINT_ERR_UNSUPPORTED;
   if (s->top_k > FLINT_MAX_TOP_K || s->top_k > s->n_experts) return FLINT_ERR_UNSUPPORTED;
-  if (s->flags & ~(FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | FLINT_SPLIT |
-                   FLINT_SINGLE_BATCH))
+  if (s->flags & ~(FLINT_RENORM | FLINT_W_BF16 | FLINT_PRE_RMSNORM | FLINT_RESIDUAL | FLINT_SPLIT))
     return FLINT_ERR_UNSUPPORTED;
   if ((s->flags & FLINT_PRE_RMSNORM) && !(s->rms_eps >= 0.0f)) return FLINT_ERR_INVALID_ARG;
   return FLINT_OK;
@@ -124,14 +123,18 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
     off = align_up(off + bytes);
     return p;
   };
+  // the header: four words, 256 bytes apart (offsets fixed in the ABI)
   w.ticket = reinterpret_cast<uint32_t*>(take(4));
   w.epoch = reinterpret_cast<uint32_t*>(take(4));
   w.error = reinterpret_cast<uint32_t*>(take(4));
-  // 64 copies of every hand-off word for the single-launch path (its readers
-  // each take their own copy); the three-kernel path uses the first [B][E]
-  // (after the single-launch paths' 8 x 8 x E words: one arrival word per
-  // workgroup beyond E, at most 256)
-  w.logit_words = reinterpret_cast<uint64_t*>(take(((int64_t)64 * B * s.n_experts + 256) * 8));
+  w.wait_limit = reinterpret_cast<uint32_t*>(take(4));
+  static_assert(FLINT_WS_ERROR_OFFSET == 2 * kAlign && FLINT_WS_WAIT_LIMIT_OFFSET == 3 * kAlign &&
+                    FLINT_WS_HEADER_BYTES == 4 * kAlign,
+                "workspace header offsets");
+  // the single-launch path's logit words, [replicas][E] (its readers each
+  // take their own copy; the three-kernel path uses the first [B][E]),
+  // then one arrival word per workgroup beyond E, at most 256
+  w.logit_words = reinterpret_cast<uint64_t*>(take(((int64_t)8 * B * s.n_experts + 256) * 8));
   w.xn = reinterpret_cast<uint16_t*>(take((int64_t)B * s.hidden * 2));
   w.idx = reinterpret_cast<int32_t*>(take((int64_t)B * FLINT_MAX_TOP_K * 4));
   w.wgt = reinterpret_cast<float*>(take((int64_t)B * FLINT_MAX_TOP_K * 4));
@@ -139,7 +142,7 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
   w.slot_expert = reinterpret_cast<int32_t*>(take((int64_t)S * 4));
   w.slot_mask = reinterpret_cast<uint32_t*>(take((int64_t)S * 4));
   w.slot_w = reinterpret_cast<float*>(take((int64_t)S * B * 4));
-  w.h_words = reinterpret_cast<uint64_t*>(take((int64_t)64 * (FLINT_MAX_TOP_K + 1) * (imax / 2) * 8));
+  w.h_words = reinterpret_cast<uint64_t*>(take((int64_t)8 * (FLINT_MAX_TOP_K + 1) * (imax / 2) * 8));
   w.x_words = reinterpret_cast<uint64_t*>(take((int64_t)8 * (s.hidden / 2) * 8));
   w.h = reinterpret_cast<uint16_t*>(take((int64_t)S * B * imax * 2));
   w.bytes = off;
@@ -180,10 +183,18 @@ int64_t flint_moe_workspace_bytes(const flint_moe_shape* shape, int32_t max_toke
   const int st = check_shape(shape);
   if (st != FLINT_OK) return -(int64_t)st;
   if (max_tokens <= 0) return -(int64_t)FLINT_ERR_INVALID_ARG;
-  const int64_t pre = prefill_ws_bytes(*shape, max_tokens);
-  if (max_tokens > FLINT_MAX_DECODE_BATCH) return pre;
-  const int64_t dec = decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH);
-  return dec > pre ? dec : pre;
+  // the decode layout first (its launch counters and hand-off words), the
+  // prefill layout after it, so the two never overlap
+  return decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH) + prefill_ws_bytes(*shape, max_tokens);
+}
+
+int32_t flint_moe_workspace_error(const void* ws, int64_t ws_bytes, uint32_t* dst, void* stream) {
+  if (!ws || !dst) return FLINT_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return FLINT_ERR_ALIGNMENT;
+  if (!aligned4(dst)) return FLINT_ERR_ALIGNMENT;
+  if (ws_bytes < FLINT_WS_HEADER_BYTES) return FLINT_ERR_WORKSPACE;
+  return to_status(hipMemcpyAsync(dst, static_cast<const char*>(ws) + FLINT_WS_ERROR_OFFSET, 4,
+                                  hipMemcpyDefault, static_cast<hipStream_t>(stream)));
 }
 
 int32_t flint_moe_repack(const void* src, int64_t n_mats, int32_t rows, int32_t cols,
@@ -261,8 +272,6 @@ static int32_t decode_common(int32_t stage, const flint_moe_shape* shape,
   hipError_t e = hipSuccess;
   if (stage < 0 && !(shape->flags & FLINT_SPLIT)) {
     if (fused_decode_supported(a)) return to_status(launch_fused_decode(a, w, s));
-    if ((a.flags & FLINT_SINGLE_BATCH) && fused_decode_bn_supported(a))
-      return to_status(launch_fused_decode_bn(a, w, s));
   }
   if (stage < 0 || stage == 0) e = launch_route(a, w, s);
   if (e == hipSuccess && (stage < 0 || stage == 1)) e = launch_gate_up(a, w, false, false, s);
@@ -335,7 +344,6 @@ int32_t flint_moe_decode_path(const flint_moe_shape* shape, int32_t batch) {
   a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
   a.K = shape->top_k; a.B = batch; a.flags = shape->flags; a.eps = shape->rms_eps;
   if (fused_decode_supported(a)) return FLINT_PATH_SINGLE_ONE;
-  if ((a.flags & FLINT_SINGLE_BATCH) && fused_decode_bn_supported(a)) return FLINT_PATH_SINGLE_BATCH;
   return FLINT_PATH_SPLIT;
 }
 
@@ -357,8 +365,9 @@ int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_moe_weights*
   if (topk_w && !aligned4(topk_w)) return FLINT_ERR_ALIGNMENT;
   if (!ws) return FLINT_ERR_WORKSPACE;
   if (!aligned16(ws)) return FLINT_ERR_ALIGNMENT;
-  if (ws_bytes < prefill_ws_bytes(*shape, n_tokens)) return FLINT_ERR_WORKSPACE;
-  PrefillWs w = carve_prefill_ws(ws, *shape, n_tokens);
+  const int64_t dec = decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH);
+  if (ws_bytes < dec + prefill_ws_bytes(*shape, n_tokens)) return FLINT_ERR_WORKSPACE;
+  PrefillWs w = carve_prefill_ws(static_cast<char*>(ws) + dec, *shape, n_tokens);
   LayerArgs a = make_args(shape, weights, x, n_tokens < 8 ? n_tokens : 8, out, gamma);
   a.topk_idx = topk_idx ? topk_idx : w.idx;
   a.topk_w = topk_w ? topk_w : w.wgt;

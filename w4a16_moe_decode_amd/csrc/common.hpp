@@ -325,6 +325,7 @@ struct DecodeWs {
   uint32_t* ticket;      // [1] arrival counter of the route kernel, left at zero
   uint32_t* epoch;       // [1] number of route launches so far
   uint32_t* error;       // [1] set to 1 if a routing hand-off ever timed out
+  uint32_t* wait_limit;  // [1] bound of each wait in reloads (0: the default), set by the host
   uint64_t* logit_words; // [B][E] (epoch << 32) | fp32 logit bits
   uint16_t* xn;          // [B][H] BF16 normalised input (PRE_RMSNORM)
   int32_t* idx;          // [B][K] selected experts (when the caller passes none)
@@ -371,8 +372,6 @@ struct LayerArgs {
 hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 bool fused_decode_supported(const LayerArgs& a);
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
-bool fused_decode_bn_supported(const LayerArgs& a);
-hipError_t launch_fused_decode_bn(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 // A stack of MoE layers for one token in one launch (flint_moe_decode_stack).
 struct StackArgs {
   LayerArgs base;                      // shape, flags, eps; pointers set per layer

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void route_kernel(LayerArgs a, DecodeWs ws) {
         ptr[4 * h + q] = ws.logit_words + (size_t)(t < B ? t : 0) * E + (ex < E ? ex : 0);
       }
     }
-    poll_words<8>(wd, ptr, ok, epoch, ws.error);
+    poll_words<8>(wd, ptr, ok, epoch, ws.error, wait_limit(ws));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = wave + 4 * h;
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void route_batch_kernel(LayerArgs a, DecodeWs 
         ptr[4 * h + q] = ws.logit_words + (size_t)(t < B ? t : 0) * E + (ex < E ? ex : 0);
       }
     }
-    poll_words_pipelined<8, 1>(wd, ptr, ok, epoch, ws.error);
+    poll_words_pipelined<8, 1>(wd, ptr, ok, epoch, ws.error, wait_limit(ws));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = wave + 4 * h;

@@ -68,6 +68,7 @@ template <int NCH>
 struct LayerPre {
   uint4 gq[NCH], rq[NCH];
   uint32_t epoch0;                                 // the stored epoch
+  uint32_t lim;                                    // bound of each wait
 };
 
 template <int NCH>
@@ -146,6 +147,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   // the kernel arguments nor the loads above
   const uint32_t epoch =
       (PRE ? pre.epoch0 : __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) + 1u + layer;
+  const uint32_t lim = PRE ? pre.lim : wait_limit(ws);
   __shared__ double s_ss[4];
   if (norm) {                                      // this wave's part of sum(x^2)
     double ss0 = 0.0, ss1 = 0.0;
@@ -249,7 +251,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
         ptr[q] = lw + (ex < E ? ex : 0);
       }
       arrival_slots(ws, E, G, ptr + 4, ok + 4);   // workgroup 0 only
-      poll_words_pipelined<8, 1>(wd, ptr, ok, epoch, ws.error);
+      poll_words_pipelined<8, 1>(wd, ptr, ok, epoch, ws.error, lim);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int ex = lane + 64 * q;
@@ -389,7 +391,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
         ok[u] = q < nw && wq < inter / 2;
         ptr[u] = hw + (ok[u] ? (size_t)sl * hstride + wq : 0);
       }
-      poll_words<8>(wd, ptr, ok, epoch, ws.error);
+      poll_words<8>(wd, ptr, ok, epoch, ws.error, lim);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int q = q0 + 256 * u;
@@ -483,6 +485,7 @@ __global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa, Decod
   // end of layer l, before its output rows are exchanged)
   LayerPre<NCH> pre;
   pre.epoch0 = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  pre.lim = wait_limit(ws);
   layer_prefetch<NCH>(pre, sa.gammas, static_cast<const uint16_t*>(sa.layers[0].router), H, sa.base.E);
   __syncthreads();
   uint32_t epoch = 0;
@@ -537,7 +540,7 @@ __global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa, Decod
         ok[u] = q < H / 2;
         ptr[u] = xw + (ok[u] ? q : 0);
       }
-      poll_words<4>(wd, ptr, ok, epoch, ws.error);
+      poll_words<4>(wd, ptr, ok, epoch, ws.error, pre.lim);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (ok[u]) reinterpret_cast<uint32_t*>(s_x)[q0 + 256 * u] = (uint32_t)wd[u];
@@ -576,54 +579,81 @@ bool fused_config(const LayerArgs& a, FusedConfig& c) {
   return true;
 }
 
+// Calls f(kernel) with the instantiation of KERNEL (the single-launch layer
+// or the layer stack) that matches the tiling c.
+#define FLINT_FUSED_DISPATCH(KERNEL, c, f)                                              \
+  do {                                                                                 \
+    constexpr int MAXS_ = FLINT_MAX_TOP_K + 1;                                         \
+    if ((c).nch == 1) {                                                                \
+      switch ((c).gd) {                                                                \
+        case 8: if ((c).dw <= 1) f(KERNEL<1, 8, 1, MAXS_>); else f(KERNEL<1, 8, 2, MAXS_>); break;    \
+        case 16: if ((c).dw <= 1) f(KERNEL<1, 16, 1, MAXS_>); else f(KERNEL<1, 16, 2, MAXS_>); break; \
+        case 32: if ((c).dw <= 1) f(KERNEL<1, 32, 1, MAXS_>); else f(KERNEL<1, 32, 2, MAXS_>); break; \
+        default: if ((c).dw <= 1) f(KERNEL<1, 64, 1, MAXS_>); else f(KERNEL<1, 64, 2, MAXS_>); break; \
+      }                                                                                \
+    } else {                                                                           \
+      switch ((c).gd) {                                                                \
+        case 8: if ((c).dw <= 1) f(KERNEL<2, 8, 1, MAXS_>); else f(KERNEL<2, 8, 2, MAXS_>); break;    \
+        case 16: if ((c).dw <= 1) f(KERNEL<2, 16, 1, MAXS_>); else f(KERNEL<2, 16, 2, MAXS_>); break; \
+        case 32: if ((c).dw <= 1) f(KERNEL<2, 32, 1, MAXS_>); else f(KERNEL<2, 32, 2, MAXS_>); break; \
+        default: if ((c).dw <= 1) f(KERNEL<2, 64, 1, MAXS_>); else f(KERNEL<2, 64, 2, MAXS_>); break; \
+      }                                                                                \
+    }                                                                                  \
+  } while (0)
+
+// Whether the device can hold all G workgroups of this kernel at once (each
+// needs a compute unit's worth of registers and LDS; the persistent grid's
+// hand-offs assume every workgroup runs concurrently).  Asked once per
+// instantiation; where the runtime cannot answer (no device) the shape
+// rules alone decide.
+template <class K>
+bool grid_resident(K kernel, int G) {
+  static int per_cu = -1;                          // -1: not asked yet, -2: no answer
+  if (per_cu == -1) {
+    int ndev = 0, n = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0)
+      per_cu = -2;
+    else
+      per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) == hipSuccess ? n : -2;
+  }
+  return per_cu == -2 || (int64_t)per_cu * device_num_cu() >= G;
+}
+
+bool fused_resident(const FusedConfig& c, bool stack) {
+  bool ok = false;
+  auto check = [&](auto kernel) { ok = grid_resident(kernel, c.G); };
+  if (stack) FLINT_FUSED_DISPATCH(fused_stack_b1_kernel, c, check);
+  else FLINT_FUSED_DISPATCH(fused_decode_b1_kernel, c, check);
+  return ok;
+}
+
 }  // namespace
 
 bool fused_stack_supported(const LayerArgs& a) {
   FusedConfig c;
   if (!fused_config(a, c)) return false;
-  return (c.dw * (64 / c.gd)) % 2 == 0;          // rows are published in pairs
+  if ((c.dw * (64 / c.gd)) % 2) return false;      // rows are published in pairs
+  return fused_resident(c, true);
 }
 
 hipError_t launch_fused_stack(const StackArgs& sa, const DecodeWs& ws, hipStream_t st) {
   FusedConfig c;
   if (!fused_config(sa.base, c) || (c.dw * (64 / c.gd)) % 2) return hipErrorInvalidConfiguration;
-  constexpr int MAXS = FLINT_MAX_TOP_K + 1;
-#define FLINT_STACK(NCH_, GD_, DW_)                                                              \
-  hipLaunchKernelGGL((fused_stack_b1_kernel<NCH_, GD_, DW_, MAXS>), dim3(c.G), dim3(256), 0, st, sa, ws)
-#define FLINT_STACK_GD(NCH_)                                                         \
-  switch (c.gd) {                                                                    \
-    case 8: if (c.dw <= 1) FLINT_STACK(NCH_, 8, 1); else FLINT_STACK(NCH_, 8, 2); break;    \
-    case 16: if (c.dw <= 1) FLINT_STACK(NCH_, 16, 1); else FLINT_STACK(NCH_, 16, 2); break; \
-    case 32: if (c.dw <= 1) FLINT_STACK(NCH_, 32, 1); else FLINT_STACK(NCH_, 32, 2); break; \
-    default: FLINT_STACK(NCH_, 64, 2); break;                                        \
-  }
-  if (c.nch == 1) { FLINT_STACK_GD(1) } else { FLINT_STACK_GD(2) }
-#undef FLINT_STACK_GD
-#undef FLINT_STACK
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(c.G), dim3(256), 0, st, sa, ws); };
+  FLINT_FUSED_DISPATCH(fused_stack_b1_kernel, c, go);
   return hipGetLastError();
 }
 
 bool fused_decode_supported(const LayerArgs& a) {
   FusedConfig c;
-  return fused_config(a, c);
+  return fused_config(a, c) && fused_resident(c, false);
 }
 
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
   FusedConfig c;
   if (!fused_config(a, c)) return hipErrorInvalidConfiguration;
-  constexpr int MAXS = FLINT_MAX_TOP_K + 1;
-#define FLINT_FUSED(NCH_, GD_, DW_)                                                              \
-  hipLaunchKernelGGL((fused_decode_b1_kernel<NCH_, GD_, DW_, MAXS>), dim3(c.G), dim3(256), 0, st, a, ws)
-#define FLINT_FUSED_GD(NCH_)                                                    \
-  switch (c.gd) {                                                               \
-    case 8: if (c.dw <= 1) FLINT_FUSED(NCH_, 8, 1); else FLINT_FUSED(NCH_, 8, 2); break;    \
-    case 16: if (c.dw <= 1) FLINT_FUSED(NCH_, 16, 1); else FLINT_FUSED(NCH_, 16, 2); break; \
-    case 32: if (c.dw <= 1) FLINT_FUSED(NCH_, 32, 1); else FLINT_FUSED(NCH_, 32, 2); break; \
-    default: if (c.dw <= 1) FLINT_FUSED(NCH_, 64, 1); else FLINT_FUSED(NCH_, 64, 2); break; \
-  }
-  if (c.nch == 1) { FLINT_FUSED_GD(1) } else { FLINT_FUSED_GD(2) }
-#undef FLINT_FUSED_GD
-#undef FLINT_FUSED
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(c.G), dim3(256), 0, st, a, ws); };
+  FLINT_FUSED_DISPATCH(fused_decode_b1_kernel, c, go);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Pieces shared by the single-launch decode kernels (fused.hip: one token,
-// fused_bn.hip: 2..8 tokens): the epoch-tagged hand-off words, the gate/up
+// Pieces of the single-launch decode kernels (fused.hip): the epoch-tagged
+// hand-off words, the gate/up
 // row pairs of a selected expert and their loads, and the CU count.
 #pragma once
 #include "common.hpp"
@@ -7,11 +7,18 @@
 namespace flint {
 namespace {
 
+// Default bound of every wait for a hand-off word (reloads of one batch of
+// words); the workspace's wait-limit word, when not zero, replaces it.
 constexpr uint32_t kFusedSpin = 1u << 20;
 
-__device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch, uint32_t* err) {
+__device__ __forceinline__ uint32_t wait_limit(const DecodeWs& ws) {
+  const uint32_t v = *ws.wait_limit;
+  return v ? v : kFusedSpin;
+}
+
+__device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch, uint32_t* err, uint32_t lim) {
   uint64_t w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (uint32_t spin = 0; (uint32_t)(w >> 32) != epoch && spin < kFusedSpin; ++spin) {
+  for (uint32_t spin = 0; (uint32_t)(w >> 32) != epoch && spin < lim; ++spin) {
     __builtin_amdgcn_s_sleep(1);
     w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -27,13 +34,13 @@ __device__ __forceinline__ uint64_t poll_word(const uint64_t* p, uint32_t epoch,
 // to drain in the middle of the next batch of loads).
 template <int U>
 __device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* const (&p)[U],
-                                           const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
+                                           const bool (&ok)[U], uint32_t epoch, uint32_t* err, uint32_t lim) {
 #pragma unroll
   for (int u = 0; u < U; ++u) w[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
   for (int u = 0; u < U; ++u)
     if (!ok[u]) w[u] = (uint64_t)epoch << 32;
-  for (uint32_t spin = 0; spin < kFusedSpin; ++spin) {
+  for (uint32_t spin = 0; spin < lim; ++spin) {
     bool ready = true;
 #pragma unroll
     for (int u = 0; u < U; ++u) ready = ready && (uint32_t)(w[u] >> 32) == epoch;
@@ -55,7 +62,8 @@ __device__ __forceinline__ void poll_words(uint64_t (&w)[U], const uint64_t* con
 // Entries with ok[u] false are skipped; their pointers must still be valid.
 template <int U, int SLEEP>
 __device__ __forceinline__ void poll_words_pipelined(uint64_t (&w)[U], const uint64_t* const (&p)[U],
-                                                     const bool (&ok)[U], uint32_t epoch, uint32_t* err) {
+                                                     const bool (&ok)[U], uint32_t epoch, uint32_t* err,
+                                                     uint32_t lim) {
   uint64_t a[U], b[U];
   auto ready = [&](const uint64_t (&v)[U]) {
     bool r = true;
@@ -65,7 +73,7 @@ __device__ __forceinline__ void poll_words_pipelined(uint64_t (&w)[U], const uin
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) a[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (uint32_t spin = 0; spin < kFusedSpin; spin += 2) {
+  for (uint32_t spin = 0; spin < lim; spin += 2) {
     __builtin_amdgcn_s_sleep(SLEEP);
 #pragma unroll
     for (int u = 0; u < U; ++u) b[u] = __hip_atomic_load(p[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
