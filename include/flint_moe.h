@@ -316,6 +316,27 @@ FLINT_API int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const fli
  * 1..8 (-FLINT_ERR_UNSUPPORTED). */
 FLINT_API int32_t flint_moe_decode_path(const flint_moe_shape* shape, int32_t batch);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation:
+ * flint_moe_decode with the library's own device scratch (a static array of
+ * FLINT_NOALLOC_SCRATCH_BYTES per device, zero at load and held until the
+ * process ends) in place of the caller's workspace.  Same kernels, same
+ * results, same arguments otherwise; nothing is allocated or freed.
+ *   Returns FLINT_ERR_WORKSPACE when the shape's decode workspace
+ *   (flint_moe_workspace_bytes(shape, 1) minus its prefill part) exceeds the
+ *   scratch -- every shape with hidden <= 4096 and I, SI <= 2048 fits --
+ *   and FLINT_ERR_DEVICE if the scratch's device address cannot be found.
+ *   Every call on a device shares that device's scratch, which keeps the
+ *   last call's state: calls that may overlap on one device (other streams,
+ *   other host threads without ordering) race and must not be made; calls
+ *   ordered on one stream are fine.  The scratch's error word is not
+ *   readable through this entry point; a wait that gives up leaves it set
+ *   for the rest of the process. */
+#define FLINT_NOALLOC_SCRATCH_BYTES (4 << 20)
+FLINT_API int32_t flint_moe_decode_noalloc(const flint_moe_shape* shape, const flint_moe_weights* weights,
+                                           const void* x, int32_t batch, void* out, int32_t* topk_idx,
+                                           float* topk_w, const void* gamma, void* stream);
+
 /* ----------------------------------------------------------------- prefill -- */
 
 /* The same layer for any number of tokens ([D0] "Optimizations": the

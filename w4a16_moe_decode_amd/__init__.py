@@ -54,7 +54,7 @@ WS_WAIT_LIMIT_OFFSET = 768
 EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_workspace_error", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
-    "flint_moe_decode", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
+    "flint_moe_decode", "flint_moe_decode_noalloc", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
     "flint_moe_prefill", "flint_dense_gemv",
 )
 
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
                vp, vp, i64, vp]
         L.flint_moe_decode.restype = i32
         L.flint_moe_decode.argtypes = dec
+        L.flint_moe_decode_noalloc.restype = i32
+        L.flint_moe_decode_noalloc.argtypes = dec[:8] + [vp]
         L.flint_moe_decode_stage.restype = i32
         L.flint_moe_decode_stage.argtypes = [i32] + dec
         L.flint_moe_decode_path.restype = i32
@@ -194,6 +196,13 @@ def flint_moe_decode(shape, weights, x, batch, out, topk_idx, topk_w, gamma, ws,
     _check("flint_moe_decode", lib().flint_moe_decode(
         ctypes.byref(shape), ctypes.byref(weights), _p(x), batch, _p(out), _p(topk_idx), _p(topk_w),
         _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+
+
+def flint_moe_decode_noalloc(shape, weights, x, batch, out, topk_idx, topk_w, gamma, stream=None):
+    """flint_moe_decode on the library's own device scratch (no workspace)."""
+    _check("flint_moe_decode_noalloc", lib().flint_moe_decode_noalloc(
+        ctypes.byref(shape), ctypes.byref(weights), _p(x), batch, _p(out), _p(topk_idx), _p(topk_w),
+        _p(gamma), _stream(stream)))
 
 
 def flint_moe_decode_stage(stage, shape, weights, x, batch, out, topk_idx, topk_w, gamma, ws,

@@ -151,6 +151,44 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
 
 }  // namespace flint
 
+namespace flint {
+int32_t decode_common(int32_t stage, const flint_moe_shape* shape, const flint_moe_weights* weights,
+                      const void* x, int32_t batch, void* out, int32_t* topk_idx, float* topk_w,
+                      const void* gamma, void* ws, int64_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != FLINT_OK) return st;
+  st = check_weights(shape, weights);
+  if (st != FLINT_OK) return st;
+  if (batch <= 0) return FLINT_ERR_INVALID_ARG;
+  if (batch > FLINT_MAX_DECODE_BATCH) return FLINT_ERR_UNSUPPORTED;
+  if (stage < -1 || stage > 2) return FLINT_ERR_INVALID_ARG;
+  FLINT_NEED(x);
+  FLINT_NEED(out);
+  if (out == x && !(shape->flags & FLINT_RESIDUAL)) return FLINT_ERR_INVALID_ARG;
+  if (shape->flags & FLINT_PRE_RMSNORM) FLINT_NEED(gamma);
+  if (topk_idx && !aligned4(topk_idx)) return FLINT_ERR_ALIGNMENT;
+  if (topk_w && !aligned4(topk_w)) return FLINT_ERR_ALIGNMENT;
+  if (!ws) return FLINT_ERR_WORKSPACE;
+  if (!aligned16(ws)) return FLINT_ERR_ALIGNMENT;
+  const int64_t need = decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH);
+  if (ws_bytes < need) return FLINT_ERR_WORKSPACE;
+
+  DecodeWs w = carve_decode_ws(ws, *shape, FLINT_MAX_DECODE_BATCH);
+  LayerArgs a = make_args(shape, weights, x, batch, out, gamma);
+  a.topk_idx = topk_idx ? topk_idx : w.idx;
+  a.topk_w = topk_w ? topk_w : w.wgt;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (stage < 0 && !(shape->flags & FLINT_SPLIT)) {
+    if (fused_decode_supported(a)) return to_status(launch_fused_decode(a, w, s));
+  }
+  if (stage < 0 || stage == 0) e = launch_route(a, w, s);
+  if (e == hipSuccess && (stage < 0 || stage == 1)) e = launch_gate_up(a, w, false, false, s);
+  if (e == hipSuccess && (stage < 0 || stage == 2)) e = launch_down(a, w, false, 0, nullptr, nullptr, s);
+  return to_status(e);
+}
+}  // namespace flint
+
 using namespace flint;
 
 extern "C" {
@@ -242,42 +280,6 @@ int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int64_t n_mat
                                   tensor_scale, out, static_cast<hipStream_t>(stream)));
 }
 
-static int32_t decode_common(int32_t stage, const flint_moe_shape* shape,
-                             const flint_moe_weights* weights, const void* x, int32_t batch,
-                             void* out, int32_t* topk_idx, float* topk_w, const void* gamma,
-                             void* ws, int64_t ws_bytes, void* stream) {
-  int st = check_shape(shape);
-  if (st != FLINT_OK) return st;
-  st = check_weights(shape, weights);
-  if (st != FLINT_OK) return st;
-  if (batch <= 0) return FLINT_ERR_INVALID_ARG;
-  if (batch > FLINT_MAX_DECODE_BATCH) return FLINT_ERR_UNSUPPORTED;
-  if (stage < -1 || stage > 2) return FLINT_ERR_INVALID_ARG;
-  FLINT_NEED(x);
-  FLINT_NEED(out);
-  if (out == x && !(shape->flags & FLINT_RESIDUAL)) return FLINT_ERR_INVALID_ARG;
-  if (shape->flags & FLINT_PRE_RMSNORM) FLINT_NEED(gamma);
-  if (topk_idx && !aligned4(topk_idx)) return FLINT_ERR_ALIGNMENT;
-  if (topk_w && !aligned4(topk_w)) return FLINT_ERR_ALIGNMENT;
-  if (!ws) return FLINT_ERR_WORKSPACE;
-  if (!aligned16(ws)) return FLINT_ERR_ALIGNMENT;
-  const int64_t need = decode_ws_bytes(*shape, FLINT_MAX_DECODE_BATCH);
-  if (ws_bytes < need) return FLINT_ERR_WORKSPACE;
-
-  DecodeWs w = carve_decode_ws(ws, *shape, FLINT_MAX_DECODE_BATCH);
-  LayerArgs a = make_args(shape, weights, x, batch, out, gamma);
-  a.topk_idx = topk_idx ? topk_idx : w.idx;
-  a.topk_w = topk_w ? topk_w : w.wgt;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (stage < 0 && !(shape->flags & FLINT_SPLIT)) {
-    if (fused_decode_supported(a)) return to_status(launch_fused_decode(a, w, s));
-  }
-  if (stage < 0 || stage == 0) e = launch_route(a, w, s);
-  if (e == hipSuccess && (stage < 0 || stage == 1)) e = launch_gate_up(a, w, false, false, s);
-  if (e == hipSuccess && (stage < 0 || stage == 2)) e = launch_down(a, w, false, 0, nullptr, nullptr, s);
-  return to_status(e);
-}
 
 int32_t flint_moe_decode(const flint_moe_shape* shape, const flint_moe_weights* weights,
                          const void* x, int32_t batch, void* out, int32_t* topk_idx,

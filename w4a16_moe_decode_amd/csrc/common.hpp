@@ -369,6 +369,11 @@ struct LayerArgs {
   float* topk_w;           // [B][K]
 };
 
+// flint_moe_decode (stage -1) or one of its stages, on a given workspace.
+int32_t decode_common(int32_t stage, const flint_moe_shape* shape, const flint_moe_weights* weights,
+                      const void* x, int32_t batch, void* out, int32_t* topk_idx, float* topk_w,
+                      const void* gamma, void* ws, int64_t ws_bytes, void* stream);
+
 hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 bool fused_decode_supported(const LayerArgs& a);
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
