@@ -180,6 +180,7 @@ int32_t decode_common(int32_t stage, const flint_moe_shape* shape, const flint_m
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (stage < 0 && !(shape->flags & FLINT_SPLIT)) {
+    if (flint_b1_supported(a)) return to_status(launch_flint_b1(a, w, s));
     if (fused_decode_supported(a)) return to_status(launch_fused_decode(a, w, s));
   }
   if (stage < 0 || stage == 0) e = launch_route(a, w, s);
@@ -315,7 +316,8 @@ int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const flint_moe_wei
   a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
   a.K = shape->top_k; a.B = 1; a.eps = shape->rms_eps;
   a.flags = shape->flags | FLINT_PRE_RMSNORM | FLINT_RESIDUAL;
-  if (!fused_stack_supported(a)) return FLINT_ERR_UNSUPPORTED;
+  const bool flint = flint_b1_supported(a);
+  if (!flint && !fused_stack_supported(a)) return FLINT_ERR_UNSUPPORTED;
   sa.layers = layers;
   sa.gammas = static_cast<const uint16_t*>(gammas);
   sa.x_in = static_cast<const uint16_t*>(x);
@@ -324,7 +326,8 @@ int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const flint_moe_wei
   sa.topk_w = topk_w;
   sa.layer_out = static_cast<uint16_t*>(layer_out);
   sa.L = n_layers;
-  return to_status(launch_fused_stack(sa, w, static_cast<hipStream_t>(stream)));
+  return to_status(flint ? launch_flint_stack(sa, w, static_cast<hipStream_t>(stream))
+                         : launch_fused_stack(sa, w, static_cast<hipStream_t>(stream)));
 }
 
 int32_t flint_moe_decode_stage(int32_t stage, const flint_moe_shape* shape,
@@ -345,7 +348,7 @@ int32_t flint_moe_decode_path(const flint_moe_shape* shape, int32_t batch) {
   std::memset(&a, 0, sizeof(a));
   a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
   a.K = shape->top_k; a.B = batch; a.flags = shape->flags; a.eps = shape->rms_eps;
-  if (fused_decode_supported(a)) return FLINT_PATH_SINGLE_ONE;
+  if (flint_b1_supported(a) || fused_decode_supported(a)) return FLINT_PATH_SINGLE_ONE;
   return FLINT_PATH_SPLIT;
 }
 

@@ -376,6 +376,10 @@ int32_t decode_common(int32_t stage, const flint_moe_shape* shape, const flint_m
 
 hipError_t launch_route(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 bool fused_decode_supported(const LayerArgs& a);
+// The single-launch batch-1 layer specialised to the Flint shape (hidden
+// 2048, 256 experts, intermediate 512 routed and shared, top-k <= 8).
+bool flint_b1_supported(const LayerArgs& a);
+hipError_t launch_flint_b1(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 // A stack of MoE layers for one token in one launch (flint_moe_decode_stack).
 struct StackArgs {
@@ -390,6 +394,7 @@ struct StackArgs {
   int L;
 };
 bool fused_stack_supported(const LayerArgs& a);
+hipError_t launch_flint_stack(const StackArgs& sa, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_fused_stack(const StackArgs& sa, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_gate_up(const LayerArgs& a, const DecodeWs& ws, bool dense, bool norm_on_the_fly,
                           hipStream_t st);

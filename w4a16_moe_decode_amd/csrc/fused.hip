@@ -67,13 +67,14 @@ __device__ __forceinline__ uint32_t gu_finish(const GUItem<NCH>& it, const GURow
 template <int NCH>
 struct LayerPre {
   uint4 gq[NCH], rq[NCH];
+  GsPre gs;                                        // this thread's tensor-scale table entries
   uint32_t epoch0;                                 // the stored epoch
   uint32_t lim;                                    // bound of each wait
 };
 
 template <int NCH>
 __device__ __forceinline__ void layer_prefetch(LayerPre<NCH>& p, const uint16_t* gamma, const uint16_t* router,
-                                               int H, int E) {
+                                               const float* gscale, const float* sh_gscale, int H, int E) {
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e0 = (int)blockIdx.x < E ? (int)blockIdx.x : 0;
 #pragma unroll
@@ -82,10 +83,11 @@ __device__ __forceinline__ void layer_prefetch(LayerPre<NCH>& p, const uint16_t*
     p.gq[c] = ldg<uint4>(gamma + col);
     p.rq[c] = ldg<uint4>(router + (size_t)e0 * H + col);
   }
+  gs_prefetch(p.gs, gscale, sh_gscale, E);
 }
 
 template <int NCH, int GD, int DW, int MAXS, bool PRE>
-__device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const DecodeWs& ws, uint32_t layer,
+__device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const DecodeWs& ws, int G, uint32_t layer,
                                                    const LayerPre<NCH>& pre) {
   constexpr int GPW = 64 / GD;
   constexpr int DROWS = DW * GPW;                 // output rows per workgroup
@@ -99,9 +101,10 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   __shared__ float s_sel_w[MAXS];
   __shared__ uint32_t s_h[MAXS][IMAXW];           // h of every slot, packed BF16 pairs
   __shared__ float s_red[4][DROWS];
+  __shared__ float s_gs[FLINT_MAX_EXPERTS + 1][3]; // tensor scales: routed experts, then the shared one
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int G = gridDim.x, NWV = 4 * G, gw = blockIdx.x * 4 + wave;
+  const int NWV = 4 * G, gw = blockIdx.x * 4 + wave;
   const int H = a.H, E = a.E, K = a.K, I = a.I, SI = a.SI;
   const bool has_sh = SI > 0;
   const int sh = has_sh ? 1 : 0;
@@ -143,6 +146,13 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) xc[c] = load_x<FMT_NVFP4>(a.x, lane + 64 * c);
+  // The tensor-scale table goes to LDS, loaded with vector loads among the
+  // first loads: a scalar load from memory shares its wait counter with LDS
+  // accesses, so one still in flight would hold up every LDS access (and
+  // barrier) behind it by a memory round trip.
+  GsPre gsp;
+  if constexpr (PRE) gsp = pre.gs;
+  else gs_prefetch(gsp, a.gscale, SI > 0 ? a.sh_gscale : nullptr, E);
   // the launch epoch: a vector load, so that waiting for it holds up neither
   // the kernel arguments nor the loads above
   const uint32_t epoch =
@@ -168,7 +178,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   // the loads below that only some waves issue
 #pragma unroll
   for (int c = 0; c < NCH; ++c) asm volatile("" ::"v"(gq[c].x), "v"(rq[c].x));   // one register per load is enough
-  asm volatile("" ::"v"(epoch));
+  asm volatile("" ::"v"(epoch), "v"(lim));
+  gs_store(gsp, s_gs, E);
 
   // ---- phase 1: router quarter rows + shared expert gate/up ------------------
   // expert e is owned by workgroup e % G; its 4 waves take a quarter each
@@ -182,8 +193,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   const int sh_first = (gw % sh_stride == sh_off) ? gw / sh_stride : nsh_items;
   GUItem<NCH> shit;
   const bool my_sh = sh_first < nsh_items;
-  GURows Rsh;
-  if (has_sh) Rsh = gu_rows(a, -1);
+  GURows Rsh;                                      // its tensor scales are read after the barrier below
+  if (has_sh) Rsh = gu_rows(a, -1, nullptr);
   if (my_sh) gu_load<NCH>(shit, Rsh, sh_first, H);
 
   if (norm) {                                      // RMS, then this wave's normalised quarter
@@ -196,31 +207,38 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
       s_xn[wv][lane + 64 * c] = xq[c];
     }
   }
-  for (int e = blockIdx.x; e < E; e += G) {
-    if (e != (int)blockIdx.x) {                    // grids smaller than E only
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        rq[c] = ldg<uint4>(a.router + (size_t)e * H + 32 * (lane + 64 * c) + 8 * wv);
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      part = dot2_bf16(rq[c].x, xq[c].x, part);
-      part = dot2_bf16(rq[c].y, xq[c].y, part);
-      part = dot2_bf16(rq[c].z, xq[c].z, part);
-      part = dot2_bf16(rq[c].w, xq[c].w, part);
-    }
-    part = group_sum<64>(part);
-    if (lane == 0) s_logit_part[wave] = part;
-    __syncthreads();
-    if (wave == 0) {
-      const float l = s_logit_part[0] + s_logit_part[1] + s_logit_part[2] + s_logit_part[3];
-      put_word_all(lw_all, lstride, e, epoch, __float_as_uint(l));
-    }
-    __syncthreads();
+  // This workgroup's router row, already in registers, then (grids smaller
+  // than E only) further rows in a loop of their own: a load inside the
+  // first row's code path would make the compiler wait for every load in
+  // flight (wave 1's shared-expert rows among them) before the dot product.
+#define FLINT_ROUTER_ROW(E_)                                                         \
+  {                                                                                  \
+    float part = 0.f;                                                                \
+    _Pragma("unroll") for (int c = 0; c < NCH; ++c) {                                \
+      part = dot2_bf16(rq[c].x, xq[c].x, part);                                      \
+      part = dot2_bf16(rq[c].y, xq[c].y, part);                                      \
+      part = dot2_bf16(rq[c].z, xq[c].z, part);                                      \
+      part = dot2_bf16(rq[c].w, xq[c].w, part);                                      \
+    }                                                                                \
+    part = group_sum<64>(part);                                                      \
+    if (lane == 0) s_logit_part[wave] = part;                                        \
+    __syncthreads();                                                                 \
+    if (wave == 0) {                                                                 \
+      const float l = s_logit_part[0] + s_logit_part[1] + s_logit_part[2] + s_logit_part[3]; \
+      put_word_all(lw_all, lstride, (E_), epoch, __float_as_uint(l));                \
+    }                                                                                \
+    __syncthreads();                                                                 \
   }
+  if ((int)blockIdx.x < E) FLINT_ROUTER_ROW(blockIdx.x)
+  for (int e = blockIdx.x + G; e < E; e += G) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) rq[c] = ldg<uint4>(a.router + (size_t)e * H + 32 * (lane + 64 * c) + 8 * wv);
+    FLINT_ROUTER_ROW(e)
+  }
+#undef FLINT_ROUTER_ROW
+  if ((int)blockIdx.x >= E) __syncthreads();      // the scale table (and xn) complete
+  if (has_sh) { Rsh.g_scale = s_gs[E][0]; Rsh.u_scale = s_gs[E][1]; }
   if (norm) {                                      // the normalised token, from the four waves
-    if ((int)blockIdx.x >= E) __syncthreads();
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -260,12 +278,15 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
                        : 0ull;
       }
     }
-    topk_keys_to_lds(key, K, s_key);
-    const uint64_t my_key = lane < K ? s_key[lane] : 0ull;   // lane k: the k-th selected key
+    // the k-th selected key is the same in every lane (sel[k]); lane k
+    // takes it over, so no LDS round trip and no readlane chain is needed
+    uint64_t sel[FLINT_MAX_TOP_K];
+    topk_keys_uniform(key, K, sel);
+    uint64_t my_key = 0ull;
+#pragma unroll
+    for (int k = 0; k < FLINT_MAX_TOP_K; ++k) my_key = lane == k ? sel[k] : my_key;
     const int my_e = (int)~(uint32_t)my_key;
     const float my_s = lane < K ? 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(my_key >> 32)))) : 0.f;
-    // both loops unrolled to the largest K (lane indices are constants, so
-    // the readlanes issue back to back)
     float ssum = 0.f;
 #pragma unroll
     for (int k = 0; k < FLINT_MAX_TOP_K; ++k)     // selection order, like the split path
@@ -275,7 +296,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     int rank = 0;
 #pragma unroll
     for (int k = 0; k < FLINT_MAX_TOP_K; ++k)
-      if (k < K) rank += __builtin_amdgcn_readlane(my_e, k) < my_e ? 1 : 0;
+      if (k < K) rank += (int)~(uint32_t)sel[k] < my_e ? 1 : 0;
     if (lane < K) {
       s_exp[sh + rank] = my_e;
       s_w[sh + rank] = w;
@@ -317,8 +338,8 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
   const bool hasA = itA < iend, hasB = itB < iend;
   const int rA = hasA ? itA / ipw : 0, pA = hasA ? itA - rA * ipw : 0;
   const int rB = hasB ? itB / ipw : 0, pB = hasB ? itB - rB * ipw : 0;
-  const GURows RA = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rA]));
-  const GURows RB = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rB]));
+  const GURows RA = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rA]), s_gs);
+  const GURows RB = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rB]), s_gs);
   if (hasA) gu_load<NCH>(A, RA, pA, H);
   if (hasB) gu_load<NCH>(B, RB, pB, H);
 
@@ -363,11 +384,11 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     GUItem<NCH> C, D;
     const int itD = it0 + 4;
     const int rC = it0 / ipw, pC = it0 - rC * ipw;
-    const GURows RC = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rC]));
+    const GURows RC = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rC]), s_gs);
     gu_load<NCH>(C, RC, pC, H);
     const bool hasD = itD < iend;
     const int rD = hasD ? itD / ipw : rC, pD = hasD ? itD - rD * ipw : pC;
-    const GURows RD = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rD]));
+    const GURows RD = gu_rows(a, __builtin_amdgcn_readfirstlane(s_exp[sh + rD]), s_gs);
     if (hasD) gu_load<NCH>(D, RD, pD, H);
     put_word_all(hw_all, hrep, (size_t)(sh + rC) * hstride + pC, epoch, gu_finish<NCH>(C, RC, xc));
     if (hasD)
@@ -420,7 +441,7 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
     XChunk<FMT_NVFP4> hx;
 #pragma unroll
     for (int m = 0; m < 16; ++m) hx.v[m] = s_h[s][16 * j + m];
-    const float f = s_w[s] * ldg<float>(e < 0 ? a.sh_gscale + 2 : a.gscale + 3 * e + 2);
+    const float f = s_w[s] * s_gs[e < 0 ? E : e][2];
 #pragma unroll
     for (int rw = 0; rw < DW; ++rw) acc[rw] = fmaf(f, chunk_dot(decode_nvfp4(draw[u][rw], dsc[u][rw]), hx), acc[rw]);
   }
@@ -448,9 +469,12 @@ __device__ __forceinline__ uint32_t fused_layer_b1(const LayerArgs& a, const Dec
 }
 
 template <int NCH, int GD, int DW, int MAXS>
-__global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, DecodeWs ws) {
+__global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a_arg, DecodeWs ws_arg, int G_arg) {
+  const LayerArgs a = pin_layer_args(a_arg);
+  const DecodeWs ws = pin_decode_ws(ws_arg);
+  const int G = pin_sgpr(G_arg);                   // the grid size (gridDim.x would be another lazy load)
   const LayerPre<NCH> none{};
-  const uint32_t epoch = fused_layer_b1<NCH, GD, DW, MAXS, false>(a, ws, 0, none);
+  const uint32_t epoch = fused_layer_b1<NCH, GD, DW, MAXS, false>(a, ws, G, 0, none);
   // ---- advance the epoch for the next launch -----------------------------------
   // Every workgroup published a router logit or an arrival word tagged with
   // the epoch it read at its start, and workgroup 0 has seen all of them
@@ -470,48 +494,91 @@ __global__ __launch_bounds__(256) void fused_decode_b1_kernel(LayerArgs a, Decod
 // moves on to layer l + 1's hand-offs only after it has seen layer l's
 // logits (or arrival words) of every workgroup, each published after that
 // workgroup finished reading layer l's inputs.
+// A wave-uniform 64-bit value read from LDS, into scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+
 template <int NCH, int GD, int DW, int MAXS>
-__global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa, DecodeWs ws) {
+__global__ __launch_bounds__(256) void fused_stack_b1_kernel(StackArgs sa_arg, DecodeWs ws_arg, int G_arg) {
+  StackArgs sa = sa_arg;
+  sa.base.H = pin_sgpr(sa_arg.base.H); sa.base.E = pin_sgpr(sa_arg.base.E);
+  sa.base.I = pin_sgpr(sa_arg.base.I); sa.base.SI = pin_sgpr(sa_arg.base.SI);
+  sa.base.K = pin_sgpr(sa_arg.base.K); sa.base.flags = pin_sgpr(sa_arg.base.flags);
+  sa.base.eps = pin_sgpr(sa_arg.base.eps);
+  sa.layers = pin_sgpr(sa_arg.layers); sa.gammas = pin_sgpr(sa_arg.gammas);
+  sa.x_in = pin_sgpr(sa_arg.x_in); sa.x_out = pin_sgpr(sa_arg.x_out);
+  sa.topk_idx = pin_sgpr(sa_arg.topk_idx); sa.topk_w = pin_sgpr(sa_arg.topk_w);
+  sa.layer_out = pin_sgpr(sa_arg.layer_out); sa.L = pin_sgpr(sa_arg.L);
+  const DecodeWs ws = pin_decode_ws(ws_arg);
+  const int G = pin_sgpr(G_arg);
   constexpr int DROWS = DW * (64 / GD);
+  constexpr int NPTR = sizeof(flint_moe_weights) / sizeof(uint64_t);
+  static_assert(NPTR <= 16, "pointer table");
   __shared__ __align__(16) uint16_t s_x[4096];      // the residual entering the layer
   __shared__ __align__(16) uint16_t s_xo[4096];     // this workgroup's rows of its output
-  const int H = sa.base.H, K = sa.base.K;
+  // Weight pointers of layer l in slot l & 1.  They are read with vector
+  // loads one layer ahead (during the residual exchange before the layer
+  // that precedes them), never with scalar loads: a scalar load from memory
+  // in flight would hold up every LDS access behind it.
+  __shared__ uint64_t s_lp[2][16];
+  const int H = sa.base.H, K = sa.base.K, E = sa.base.E;
   const int n0 = blockIdx.x * DROWS;
   const int rep = blockIdx.x % kReplicas;
   const size_t xrep = (size_t)H / 2;
+  const uint64_t* tab = reinterpret_cast<const uint64_t*>(sa.layers);
   for (int q = threadIdx.x; q < H / 8; q += 256)
     reinterpret_cast<uint4*>(s_x)[q] = reinterpret_cast<const uint4*>(sa.x_in)[q];
+  if (threadIdx.x < NPTR) {
+    s_lp[0][threadIdx.x] = ldg<uint64_t>(tab + threadIdx.x);
+    s_lp[1][threadIdx.x] = ldg<uint64_t>(tab + (size_t)(sa.L > 1 ? 1 : 0) * NPTR + threadIdx.x);
+  }
+  __syncthreads();
   // layer 0's input-independent first loads (layer l + 1's are issued at the
   // end of layer l, before its output rows are exchanged)
   LayerPre<NCH> pre;
   pre.epoch0 = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   pre.lim = wait_limit(ws);
-  layer_prefetch<NCH>(pre, sa.gammas, static_cast<const uint16_t*>(sa.layers[0].router), H, sa.base.E);
-  __syncthreads();
+  layer_prefetch<NCH>(pre, sa.gammas, reinterpret_cast<const uint16_t*>(uniform_u64(s_lp[0][0])),
+                      reinterpret_cast<const float*>(uniform_u64(s_lp[0][5])),
+                      sa.base.SI > 0 ? reinterpret_cast<const float*>(uniform_u64(s_lp[0][10])) : nullptr, H, E);
+  uint64_t nxt = 0;                                // layer l + 2's pointer (lanes < NPTR of wave 0)
   uint32_t epoch = 0;
   for (int l = 0; l < sa.L; ++l) {
+    // layer l + 1's pointers, loaded during the previous exchange, go to the
+    // slot layer l - 1 used
+    if (l >= 1 && l + 1 < sa.L && threadIdx.x < NPTR) s_lp[(l + 1) & 1][threadIdx.x] = nxt;
+    const uint64_t* lp = s_lp[l & 1];
     LayerArgs a = sa.base;
-    const flint_moe_weights& w = sa.layers[l];
-    a.router = static_cast<const uint16_t*>(w.router);
-    a.gu_codes = static_cast<const uint8_t*>(w.gu_codes);
-    a.gu_scales = static_cast<const uint8_t*>(w.gu_scales);
-    a.d_codes = static_cast<const uint8_t*>(w.d_codes);
-    a.d_scales = static_cast<const uint8_t*>(w.d_scales);
-    a.gscale = w.gscale;
-    a.sh_gu_codes = static_cast<const uint8_t*>(w.sh_gu_codes);
-    a.sh_gu_scales = static_cast<const uint8_t*>(w.sh_gu_scales);
-    a.sh_d_codes = static_cast<const uint8_t*>(w.sh_d_codes);
-    a.sh_d_scales = static_cast<const uint8_t*>(w.sh_d_scales);
-    a.sh_gscale = w.sh_gscale;
+    a.router = reinterpret_cast<const uint16_t*>(uniform_u64(lp[0]));
+    a.gu_codes = reinterpret_cast<const uint8_t*>(uniform_u64(lp[1]));
+    a.gu_scales = reinterpret_cast<const uint8_t*>(uniform_u64(lp[2]));
+    a.d_codes = reinterpret_cast<const uint8_t*>(uniform_u64(lp[3]));
+    a.d_scales = reinterpret_cast<const uint8_t*>(uniform_u64(lp[4]));
+    a.gscale = reinterpret_cast<const float*>(uniform_u64(lp[5]));
+    a.sh_gu_codes = reinterpret_cast<const uint8_t*>(uniform_u64(lp[6]));
+    a.sh_gu_scales = reinterpret_cast<const uint8_t*>(uniform_u64(lp[7]));
+    a.sh_d_codes = reinterpret_cast<const uint8_t*>(uniform_u64(lp[8]));
+    a.sh_d_scales = reinterpret_cast<const uint8_t*>(uniform_u64(lp[9]));
+    a.sh_gscale = reinterpret_cast<const float*>(uniform_u64(lp[10]));
     a.gamma = sa.gammas + (size_t)l * H;
     a.x = s_x;
     a.out = s_xo;
     a.topk_idx = sa.topk_idx + (size_t)l * K;
     a.topk_w = sa.topk_w + (size_t)l * K;
-    epoch = fused_layer_b1<NCH, GD, DW, MAXS, true>(a, ws, (uint32_t)l, pre);
-    if (l + 1 < sa.L)
-      layer_prefetch<NCH>(pre, sa.gammas + (size_t)(l + 1) * H,
-                          static_cast<const uint16_t*>(sa.layers[l + 1].router), H, sa.base.E);
+    epoch = fused_layer_b1<NCH, GD, DW, MAXS, true>(a, ws, G, (uint32_t)l, pre);
+    if (l + 1 < sa.L) {
+      const uint64_t* ln = s_lp[(l + 1) & 1];
+      layer_prefetch<NCH>(pre, sa.gammas + (size_t)(l + 1) * H, reinterpret_cast<const uint16_t*>(uniform_u64(ln[0])),
+                          reinterpret_cast<const float*>(uniform_u64(ln[5])),
+                          sa.base.SI > 0 ? reinterpret_cast<const float*>(uniform_u64(ln[10])) : nullptr, H, E);
+      // unconditional (clamped): a conditional load merged with the old value
+      // would be waited for at once
+      const int l2 = l + 2 < sa.L ? l + 2 : sa.L - 1;
+      const int f = (int)threadIdx.x < NPTR ? (int)threadIdx.x : NPTR - 1;
+      nxt = ldg<uint64_t>(tab + (size_t)l2 * NPTR + f);
+    }
     __syncthreads();                               // this workgroup's rows of x_{l+1} are in s_xo
     if (sa.layer_out)
       for (int r = threadIdx.x; r < DROWS; r += 256)
@@ -639,7 +706,7 @@ bool fused_stack_supported(const LayerArgs& a) {
 hipError_t launch_fused_stack(const StackArgs& sa, const DecodeWs& ws, hipStream_t st) {
   FusedConfig c;
   if (!fused_config(sa.base, c) || (c.dw * (64 / c.gd)) % 2) return hipErrorInvalidConfiguration;
-  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(c.G), dim3(256), 0, st, sa, ws); };
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(c.G), dim3(256), 0, st, sa, ws, c.G); };
   FLINT_FUSED_DISPATCH(fused_stack_b1_kernel, c, go);
   return hipGetLastError();
 }
@@ -652,7 +719,7 @@ bool fused_decode_supported(const LayerArgs& a) {
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
   FusedConfig c;
   if (!fused_config(a, c)) return hipErrorInvalidConfiguration;
-  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(c.G), dim3(256), 0, st, a, ws); };
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(c.G), dim3(256), 0, st, a, ws, c.G); };
   FLINT_FUSED_DISPATCH(fused_decode_b1_kernel, c, go);
   return hipGetLastError();
 }

@@ -7,12 +7,59 @@
 namespace flint {
 namespace {
 
+// A kernel argument the compiler must hold in scalar registers from here on.
+// Kernel arguments are otherwise loaded lazily, each with a scalar load
+// where it is first needed, and the wait for such a load (its counter is
+// shared with LDS accesses) stalls the next LDS access or barrier by a
+// memory round trip; pinning every argument a kernel uses at its start
+// makes all of them one batch of loads and one wait.
+template <class T>
+__device__ __forceinline__ T pin_sgpr(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+// Pointers are pinned as global-memory pointers, so the compiler still knows
+// that loads through them are global loads (a generic pointer of unknown
+// origin would make them flat loads, which count against the LDS counter).
+template <class T>
+__device__ __forceinline__ T* pin_sgpr(T* p) {
+  typedef __attribute__((address_space(1))) T GT;
+  GT* g = (GT*)p;
+  asm volatile("" : "+s"(g));
+  return (T*)g;
+}
+
+// The fields of the layer arguments the single-launch kernels use, pinned.
+__device__ __forceinline__ LayerArgs pin_layer_args(const LayerArgs& in) {
+  LayerArgs a = in;
+  a.H = pin_sgpr(in.H); a.E = pin_sgpr(in.E); a.I = pin_sgpr(in.I); a.SI = pin_sgpr(in.SI);
+  a.K = pin_sgpr(in.K); a.flags = pin_sgpr(in.flags); a.eps = pin_sgpr(in.eps);
+  a.router = pin_sgpr(in.router);
+  a.gu_codes = pin_sgpr(in.gu_codes); a.gu_scales = pin_sgpr(in.gu_scales);
+  a.d_codes = pin_sgpr(in.d_codes); a.d_scales = pin_sgpr(in.d_scales); a.gscale = pin_sgpr(in.gscale);
+  a.sh_gu_codes = pin_sgpr(in.sh_gu_codes); a.sh_gu_scales = pin_sgpr(in.sh_gu_scales);
+  a.sh_d_codes = pin_sgpr(in.sh_d_codes); a.sh_d_scales = pin_sgpr(in.sh_d_scales);
+  a.sh_gscale = pin_sgpr(in.sh_gscale);
+  a.x = pin_sgpr(in.x); a.gamma = pin_sgpr(in.gamma); a.out = pin_sgpr(in.out);
+  a.topk_idx = pin_sgpr(in.topk_idx); a.topk_w = pin_sgpr(in.topk_w);
+  return a;
+}
+__device__ __forceinline__ DecodeWs pin_decode_ws(const DecodeWs& in) {
+  DecodeWs w = in;
+  w.epoch = pin_sgpr(in.epoch); w.error = pin_sgpr(in.error); w.wait_limit = pin_sgpr(in.wait_limit);
+  w.logit_words = pin_sgpr(in.logit_words); w.h_words = pin_sgpr(in.h_words);
+  w.x_words = pin_sgpr(in.x_words);
+  return w;
+}
+
 // Default bound of every wait for a hand-off word (reloads of one batch of
 // words); the workspace's wait-limit word, when not zero, replaces it.
 constexpr uint32_t kFusedSpin = 1u << 20;
 
+// A vector load: a scalar load from memory would share its wait counter
+// with every LDS access that follows it.
 __device__ __forceinline__ uint32_t wait_limit(const DecodeWs& ws) {
-  const uint32_t v = *ws.wait_limit;
+  const uint32_t v = __hip_atomic_load(ws.wait_limit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v ? v : kFusedSpin;
 }
 
@@ -119,7 +166,10 @@ struct GURows {            // gate and up rows of one selected expert
   int inter;
 };
 
-__device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert /* -1 = shared */) {
+// Rows of a selected expert (-1 = the shared one); the tensor scales come
+// from the LDS table `gs` ([E][3] routed, then the shared expert's), or are
+// left for the caller to fill when gs is null.
+__device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert, const float (*gs)[3]) {
   GURows r;
   const int H = a.H;
   if (expert < 0) {
@@ -127,15 +177,38 @@ __device__ __forceinline__ GURows gu_rows(const LayerArgs& a, int expert /* -1 =
     const size_t mc = (size_t)a.SI * H / 2, ms = (size_t)a.SI * H / 16;
     r.gc = a.sh_gu_codes; r.uc = a.sh_gu_codes + mc;
     r.gs = a.sh_gu_scales; r.us = a.sh_gu_scales + ms;
-    r.g_scale = ldg<float>(a.sh_gscale); r.u_scale = ldg<float>(a.sh_gscale + 1);
+    r.g_scale = gs ? gs[a.E][0] : 0.f; r.u_scale = gs ? gs[a.E][1] : 0.f;
   } else {
     r.inter = a.I;
     const size_t mc = (size_t)a.I * H / 2, ms = (size_t)a.I * H / 16;
     r.gc = a.gu_codes + (size_t)(2 * expert) * mc; r.uc = r.gc + mc;
     r.gs = a.gu_scales + (size_t)(2 * expert) * ms; r.us = r.gs + ms;
-    r.g_scale = ldg<float>(a.gscale + 3 * expert); r.u_scale = ldg<float>(a.gscale + 3 * expert + 1);
+    r.g_scale = gs[expert][0]; r.u_scale = gs[expert][1];
   }
   return r;
+}
+
+// This thread's entries (threadIdx.x and threadIdx.x + 256) of the tensor
+// scale table: routed experts 0..E-1, then the shared expert at E.  Vector
+// loads (the addresses differ per lane), unconditional (clamped pointers).
+struct GsPre { float v[2][3]; };
+__device__ __forceinline__ void gs_prefetch(GsPre& g, const float* gscale, const float* sh_gscale, int E) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    const float* p = i < E ? gscale + 3 * i : (i == E && sh_gscale ? sh_gscale : gscale);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) g.v[q][j] = ldg<float>(p + j);
+  }
+}
+__device__ __forceinline__ void gs_store(const GsPre& g, float (*gs)[3], int E) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + 256 * q;
+    if (i <= E)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) gs[i][j] = g.v[q][j];
+  }
 }
 
 // One gate/up item: rows 2p and 2p+1 of a selected expert, a whole wave per
@@ -243,6 +316,31 @@ __device__ __forceinline__ void topk_keys_to_lds(uint64_t (&key)[4], int K, uint
       s_key[k] = key[0];
       key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull;
     }
+  }
+}
+
+// The same selection with the result in registers: sel[k] (equal in every
+// lane) is the k-th selected key for k < K, 0 beyond.
+__device__ __forceinline__ void topk_keys_uniform(uint64_t (&key)[4], int K, uint64_t (&sel)[FLINT_MAX_TOP_K]) {
+#define FLINT_CSWAP(i, j) { const uint64_t hi_ = key[i] > key[j] ? key[i] : key[j]; \
+                            const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
+  FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
+#undef FLINT_CSWAP
+#pragma unroll
+  for (int k = 0; k < FLINT_MAX_TOP_K; ++k) {
+    sel[k] = 0ull;
+    if (k >= K) continue;                         // the same in every lane
+    const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+    const uint32_t mhi = wave_max_u32_all(hi);
+    const bool at = hi == mhi;
+    const unsigned long long bal = __ballot(at);
+    uint32_t mlo;
+    if (__popcll(bal) == 1)
+      mlo = __builtin_amdgcn_readlane(lo, __ffsll((long long)bal) - 1);
+    else                                          // equal logits: the lower index wins
+      mlo = wave_max_u32_all(at ? lo : 0u);
+    sel[k] = ((uint64_t)mhi << 32) | mlo;
+    if (key[0] == sel[k]) { key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0ull; }
   }
 }
 
