@@ -313,7 +313,8 @@ __device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const Decode
   if (has_d2) down_load(d2, a.d_codes + (size_t)de2 * DC, a.d_scales + (size_t)de2 * DS, FL_ROWS * b, lane);
   {
     const uint64_t* hw = hw_all + (size_t)rep * HREP;
-    constexpr int NPOLL = (FL_SLOTS * FL_IW + 511) / 512;   // words per thread at k = 8
+    // words per thread: (1 + k) slots of 256 words over 512 threads
+    constexpr int NPOLL = ((1 + (KC ? KC : FLINT_MAX_TOP_K)) * FL_IW + 511) / 512;
     const int nw = (1 + K) * FL_IW;
     uint64_t wd[NPOLL];
     const uint64_t* ptr[NPOLL];
