@@ -77,6 +77,7 @@ extern "C" {
 /* decode paths reported by flint_moe_decode_path */
 #define FLINT_PATH_SPLIT        0  /* three kernels: route, gate/up, down    */
 #define FLINT_PATH_SINGLE_ONE   1  /* one launch, batch 1                    */
+#define FLINT_PATH_SINGLE_BATCH 2  /* one launch, batch 2..8 (Flint shape)   */
 
 /* source NVFP4 super-block byte orders accepted by the repack */
 #define FLINT_SRC_INTERLEAVED   0  /* 4 x [scale byte, 8 code bytes]          */
@@ -260,7 +261,9 @@ FLINT_API int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int
  * runs the three kernels instead when it cannot), and the caller must not
  * run other kernels on the device concurrently (on other streams or in
  * other processes) while it runs; a caller that does should set
- * FLINT_SPLIT.  Every other call enqueues three kernels: route (RMSNorm,
+ * FLINT_SPLIT.  At the Flint shape (hidden 2048, 256 experts, I = SI = 512,
+ * NVFP4) a call of batch 2..8 is one launch of the same kind, on a device
+ * with at least 256 compute units.  Every other call enqueues three kernels: route (RMSNorm,
  * router GEMV, top-k, expert set), gate/up (+SiLU*up), down (weighted
  * combine, shared expert, residual).  flint_moe_decode_path tells which.
  * All paths give the same result up to fp32 summation order. */
@@ -310,7 +313,7 @@ FLINT_API int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const fli
                                          int64_t ws_bytes, void* stream);
 
 /* Which kernels flint_moe_decode runs for this shape (flags included) and
- * batch: FLINT_PATH_SPLIT or FLINT_PATH_SINGLE_ONE.
+ * batch: FLINT_PATH_SPLIT, FLINT_PATH_SINGLE_ONE or FLINT_PATH_SINGLE_BATCH.
  * Reads only the shape; enqueues nothing.  Returns -status for an invalid
  * shape (-FLINT_ERR_INVALID_ARG, -FLINT_ERR_UNSUPPORTED) or a batch outside
  * 1..8 (-FLINT_ERR_UNSUPPORTED). */

@@ -131,7 +131,14 @@ def test_decode_path_rules():
     flint = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
     assert fm.flint_moe_decode_path(flint, 1) == fm.FLINT_PATH_SINGLE_ONE
     for b in range(2, 9):
-        assert fm.flint_moe_decode_path(flint, b) == fm.FLINT_PATH_SPLIT
+        assert fm.flint_moe_decode_path(flint, b) == fm.FLINT_PATH_SINGLE_BATCH
+    for k in (1, 8):                                # any top-k up to the maximum
+        s = fm.FlintMoeShape(2048, 256, 512, 512, k, 0, 1e-6)
+        assert fm.flint_moe_decode_path(s, 8) == fm.FLINT_PATH_SINGLE_BATCH
+    for other in (fm.FlintMoeShape(2048, 256, 512, 1024, 6, 0, 1e-6),
+                  fm.FlintMoeShape(2048, 128, 512, 512, 6, 0, 1e-6),
+                  fm.FlintMoeShape(4096, 256, 512, 512, 6, 0, 1e-6)):
+        assert fm.flint_moe_decode_path(other, 4) == fm.FLINT_PATH_SPLIT
     # the old single-launch batch flag is no longer accepted
     with pytest.raises(fm.FlintError) as e:
         fm.flint_moe_decode_path(fm.FlintMoeShape(2048, 256, 512, 512, 6, 0x20, 1e-6), 2)

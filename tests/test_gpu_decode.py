@@ -5,13 +5,15 @@ modes, both source byte orders, every UE4M3 mantissa, non-power-of-two
 tensor scales, ragged shapes (row tiles with tails, lane groups with idle
 lanes), no shared expert, a shared expert of another width, the all-tie
 zero input, pre-norm + residual, and BF16 weights."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import gen
 import w4a16_moe_decode_amd as fm
-from _parity import DecodeCase, pack, run_decode_case
+from _parity import DecodeCase, compare_outputs, pack, run_decode_case
 from oracle import moe
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +54,10 @@ def test_ragged_and_edge_shapes(shape, batch):
     run_decode_case(DecodeCase(shape, seed=22, batch=batch, wbf16=True, flags=fm.FLINT_RENORM))
 
 
+def abi(sh, flags):
+    return fm.FlintMoeShape(sh.hidden, sh.n_experts, sh.inter, sh.shared_inter, sh.top_k, flags, 1e-6)
+
+
 @pytest.fixture(scope="module")
 def flint_layer():
     src = gen.moe_layer_source(FLINT, 100, "cpu")
@@ -60,13 +66,35 @@ def flint_layer():
 
 
 @pytest.mark.parametrize("batch,flags", [
-    (1, 0), (1, fm.FLINT_RENORM), (8, 0), (8, fm.FLINT_RENORM), (4, 0),
-    (8, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL),
+    (1, 0), (1, fm.FLINT_RENORM), (8, 0), (8, fm.FLINT_RENORM), (4, 0), (2, 0), (3, fm.FLINT_RENORM),
+    (5, 0), (7, fm.FLINT_RENORM), (8, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL),
+    (3, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL | fm.FLINT_RENORM),
+    (8, fm.FLINT_SPLIT), (5, fm.FLINT_SPLIT | fm.FLINT_RENORM),
+    (8, fm.FLINT_SPLIT | fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL),
 ])
 def test_flint_layer(flint_layer, batch, flags):
+    """Batch 1 runs as one launch, batch 2..8 as the batch single launch,
+    FLINT_SPLIT as three kernels."""
     src, layer = flint_layer
+    want = (fm.FLINT_PATH_SPLIT if flags & fm.FLINT_SPLIT else
+            fm.FLINT_PATH_SINGLE_ONE if batch == 1 else fm.FLINT_PATH_SINGLE_BATCH)
+    assert fm.flint_moe_decode_path(abi(FLINT, flags), batch) == want
     run_decode_case(DecodeCase(FLINT, seed=100 + batch + flags, batch=batch, flags=flags),
                     src=src, layer=layer)
+
+
+@pytest.mark.parametrize("top_k,batch", [(8, 8), (8, 3), (1, 8), (2, 2), (6, 8)])
+def test_flint_batch_top_k(top_k, batch):
+    """The batch single launch with a top-k other than the usual 6 (its
+    general variant) and with 6 against a fresh layer: up to 64 routed slots
+    at k = 8, one routed expert per token at k = 1."""
+    sh = dataclasses.replace(FLINT, top_k=top_k)
+    assert fm.flint_moe_decode_path(abi(sh, 0), batch) == fm.FLINT_PATH_SINGLE_BATCH
+    src = gen.moe_layer_source(sh, 150 + top_k, "cpu")
+    layer = pack(src)
+    for flags in (0, fm.FLINT_RENORM):
+        run_decode_case(DecodeCase(sh, seed=160 + top_k + batch + flags, batch=batch, flags=flags),
+                        src=src, layer=layer)
 
 
 def test_flint_layer_bf16_weights(flint_layer):
@@ -104,10 +132,13 @@ def test_results_are_bit_reproducible_and_stages_compose(flint_layer):
     x8 = gen.activations(8, 8, FLINT.hidden).cuda()
     d1 = runner(x8)
     d2 = runner(x8)
+    e1 = split(x8)
+    e2 = split(x8)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(s1, s2) and torch.equal(s1, c)
-    assert torch.equal(d1, d2)
+    assert torch.equal(d1, d2) and torch.equal(e1, e2)
+    compare_outputs(d1.cpu().float().numpy(), e1.cpu().float().numpy(), "batch single launch vs split")
 
 
 def test_rotating_copies_and_workspace_reuse(flint_layer):

@@ -80,7 +80,9 @@ def _plant_nan_scale(src, expert, matrix, row):
 
 # ------------------------------------------------------------ decode paths --
 
-PATHS = {"fused": (1, 0), "split": (1, fm.FLINT_SPLIT), "batch": (8, 0)}
+PATHS = {"fused": (1, 0), "split": (1, fm.FLINT_SPLIT), "batch": (8, 0), "batch_split": (8, fm.FLINT_SPLIT)}
+WANT_PATH = {"fused": fm.FLINT_PATH_SINGLE_ONE, "split": fm.FLINT_PATH_SPLIT,
+             "batch": fm.FLINT_PATH_SINGLE_BATCH, "batch_split": fm.FLINT_PATH_SPLIT}
 
 
 def _run_decode(src, x, path, renorm=False):
@@ -89,8 +91,7 @@ def _run_decode(src, x, path, renorm=False):
     flags |= fm.FLINT_RENORM if renorm else 0
     layer = pack(src)
     runner = fm.DecodeRunner(layer, K, flags)
-    want_path = fm.FLINT_PATH_SINGLE_ONE if path == "fused" else fm.FLINT_PATH_SPLIT
-    assert fm.flint_moe_decode_path(runner.shape, batch) == want_path
+    assert fm.flint_moe_decode_path(runner.shape, batch) == WANT_PATH[path]
     idx = torch.full((batch, K), -1, dtype=torch.int32, device="cuda")
     w = torch.zeros((batch, K), dtype=torch.float32, device="cuda")
     out = runner(x.cuda(), topk_idx=idx, topk_w=w)

@@ -86,12 +86,12 @@ def test_bounded_wait_gives_up_and_sets_error_word():
     workspace is zero-filled again, calls give the normal result."""
     src = gen.moe_layer_source(FLINT, 604)
     layer = pack(src)
-    for stack in (False, True):
+    for stack, batch in ((False, 1), (True, 1), (False, 8)):
         r = fm.DecodeRunner(layer, FLINT.top_k, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL)
         gamma = gen.rmsnorm_gamma(13, FLINT.hidden, "cuda")
         step = fm.DecodeStep([layer, layer], [gamma, gamma], [], [], FLINT.top_k, stack=True)
         step.ws = r.ws
-        x = gen.activations(12, 1, FLINT.hidden).cuda()
+        x = gen.activations(12, batch, FLINT.hidden).cuda()
 
         def call():
             if stack:
@@ -107,7 +107,7 @@ def test_bounded_wait_gives_up_and_sets_error_word():
         lim.fill_(1)
         call()
         torch.cuda.synchronize()
-        assert fm.decode_error_word(r) == 1, f"stack={stack}"
+        assert fm.decode_error_word(r) == 1, f"stack={stack} batch={batch}"
         r.ws.zero_()
         got = call()
         torch.cuda.synchronize()

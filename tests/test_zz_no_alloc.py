@@ -1,7 +1,7 @@
 """flint_moe_decode_noalloc -- the decode layer on the library's static
 device scratch instead of a caller's workspace -- against flint_moe_decode
 on the same inputs: two calls in a row, the second with a smaller input,
-for the one-launch batch-1 kernel and the three-kernel path."""
+for the one-launch batch-1 and batch kernels and the three-kernel path."""
 import numpy as np
 import pytest
 import torch
@@ -35,14 +35,16 @@ def _pair(layer, shape, flags, batch, seed, gamma):
     return x, res
 
 
-@pytest.mark.parametrize("flags", [0, fm.FLINT_RENORM | fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL])
+@pytest.mark.parametrize("flags", [0, fm.FLINT_RENORM | fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL, fm.FLINT_SPLIT])
 def test_noalloc_matches_workspace_entry_point(flags):
     src = gen.moe_layer_source(FLINT, 950, "cuda")
     layer = pack(src)
     gamma = gen.rmsnorm_gamma(951, FLINT.hidden, "cuda")
-    # batch 8 (three kernels), then batch 1 (one launch): the second call's
-    # input is smaller and the scratch still holds the first call's state
-    for batch, path in ((8, fm.FLINT_PATH_SPLIT), (1, fm.FLINT_PATH_SINGLE_ONE), (3, fm.FLINT_PATH_SPLIT)):
+    # batch 8, then batch 1, then 3: each call's input is smaller than the
+    # first's and the scratch still holds the previous call's state
+    for batch in (8, 1, 3):
+        path = (fm.FLINT_PATH_SPLIT if flags & fm.FLINT_SPLIT else
+                fm.FLINT_PATH_SINGLE_ONE if batch == 1 else fm.FLINT_PATH_SINGLE_BATCH)
         assert fm.flint_moe_decode_path(layer.shape(FLINT.top_k, flags), batch) == path
         x, ((o1, i1, w1), (o2, i2, w2)) = _pair(layer, FLINT, flags, batch, 952 + flags, gamma)
         assert torch.equal(i1, i2) and torch.equal(w1, w2), f"routing, batch {batch}"

@@ -37,6 +37,7 @@ FLINT_SPLIT = 0x10
 
 FLINT_PATH_SPLIT = 0
 FLINT_PATH_SINGLE_ONE = 1
+FLINT_PATH_SINGLE_BATCH = 2
 
 FLINT_SRC_INTERLEAVED = 0
 FLINT_SRC_SCALES_FIRST = 1

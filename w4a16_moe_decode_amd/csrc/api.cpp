@@ -145,6 +145,13 @@ DecodeWs carve_decode_ws(void* base, const flint_moe_shape& s, int max_batch) {
   w.h_words = reinterpret_cast<uint64_t*>(take((int64_t)8 * (FLINT_MAX_TOP_K + 1) * (imax / 2) * 8));
   w.x_words = reinterpret_cast<uint64_t*>(take((int64_t)8 * (s.hidden / 2) * 8));
   w.h = reinterpret_cast<uint16_t*>(take((int64_t)S * B * imax * 2));
+  // the batch single launch's routed h words and partial sums (Flint shape only)
+  w.hb_words = w.p_words = nullptr;
+  if (flint_b8_shape(s)) {
+    const int routed = S - (s.shared_inter > 0 ? 1 : 0);
+    w.hb_words = reinterpret_cast<uint64_t*>(take((int64_t)routed * B * (imax / 2) * 8));
+    w.p_words = reinterpret_cast<uint64_t*>(take((int64_t)B * (FLINT_MAX_TOP_K + 1) * s.hidden * 8));
+  }
   w.bytes = off;
   return w;
 }
@@ -181,6 +188,7 @@ int32_t decode_common(int32_t stage, const flint_moe_shape* shape, const flint_m
   hipError_t e = hipSuccess;
   if (stage < 0 && !(shape->flags & FLINT_SPLIT)) {
     if (flint_b1_supported(a)) return to_status(launch_flint_b1(a, w, s));
+    if (flint_b8_supported(a)) return to_status(launch_flint_b8(a, w, s));
     if (fused_decode_supported(a)) return to_status(launch_fused_decode(a, w, s));
   }
   if (stage < 0 || stage == 0) e = launch_route(a, w, s);
@@ -349,6 +357,7 @@ int32_t flint_moe_decode_path(const flint_moe_shape* shape, int32_t batch) {
   a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
   a.K = shape->top_k; a.B = batch; a.flags = shape->flags; a.eps = shape->rms_eps;
   if (flint_b1_supported(a) || fused_decode_supported(a)) return FLINT_PATH_SINGLE_ONE;
+  if (flint_b8_supported(a)) return FLINT_PATH_SINGLE_BATCH;
   return FLINT_PATH_SPLIT;
 }
 

@@ -336,6 +336,9 @@ struct DecodeWs {
   float* slot_w;         // [S][8] combine weight of token t at routed slot r
   uint64_t* h_words;     // [K+1][Imax/2] (epoch << 32) | two BF16 of h, single-launch path
   uint64_t* x_words;     // [8][H/2] (epoch << 32) | two BF16 of the residual, layer stack
+  uint64_t* hb_words;    // [S_routed][8][Imax/2] (epoch << 32) | two BF16 of h, batch single launch
+  uint64_t* p_words;     // [8][K_max+1][H] (epoch << 32) | fp32 partial sum, batch single launch
+                         // (both null unless the shape takes that path)
   uint16_t* h;           // [S][8][Imax] BF16 SiLU(g)*u per slot and token; slot 0
                          // is the shared expert when there is one, routed
                          // slot r is slot r + (shared ? 1 : 0)
@@ -379,6 +382,9 @@ bool fused_decode_supported(const LayerArgs& a);
 // The single-launch batch-1 layer specialised to the Flint shape (hidden
 // 2048, 256 experts, intermediate 512 routed and shared, top-k <= 8).
 bool flint_b1_supported(const LayerArgs& a);
+bool flint_b8_shape(const flint_moe_shape& s);
+bool flint_b8_supported(const LayerArgs& a);   // the workspace of such a shape holds its buffers
+hipError_t launch_flint_b8(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_flint_b1(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 hipError_t launch_fused_decode(const LayerArgs& a, const DecodeWs& ws, hipStream_t st);
 // A stack of MoE layers for one token in one launch (flint_moe_decode_stack).

@@ -27,38 +27,12 @@
 //
 // Hand-offs between workgroups are the epoch-tagged 64-bit words of the
 // general kernel (one copy per XCD), with the same bounded waits.
-#include "fused_common.hpp"
+#include "flint_common.hpp"
 
 namespace flint {
 namespace {
 
-constexpr int FL_H = 2048, FL_E = 256, FL_I = 512;
-constexpr int FL_G = 256;                          // workgroups (one per compute unit)
-constexpr int FL_NW = 8;                           // waves per workgroup
-constexpr int FL_ROWS = FL_H / FL_G;               // output rows per workgroup
-constexpr int FL_IW = FL_I / 2;                    // h words (BF16 pairs) per slot
 constexpr int FL_SLOTS = FLINT_MAX_TOP_K + 1;      // shared slot 0, routed slots 1..K
-
-static_assert(FL_G == FL_E, "one router row per workgroup");
-static_assert(FL_H / 32 == 64, "one 32-column chunk of the token per lane");
-static_assert(FL_I / 32 == 16 && FL_ROWS == 8, "down rows: 16 lanes per row, 4 rows per load, 2 loads");
-
-// The 16 bytes of codes and 2 scale bytes of a lane's chunk of two down rows
-// (rows 8b + grp and 8b + 4 + grp, chunk li) of one slot.
-struct DownRows {
-  uint4 c[2];
-  uint32_t s[2];
-};
-
-__device__ __forceinline__ void down_load(DownRows& d, const uint8_t* codes, const uint8_t* scales, int row0, int lane) {
-  const int grp = lane >> 4, li = lane & 15;
-#pragma unroll
-  for (int rw = 0; rw < 2; ++rw) {
-    const int n = row0 + 4 * rw + grp;
-    d.c[rw] = ldg<uint4>(codes + (size_t)n * (FL_I / 2) + 16 * li);
-    d.s[rw] = ldg<uint16_t>(scales + (size_t)n * (FL_I / 16) + 2 * li);
-  }
-}
 
 // acc[rw] += f * (down row chunk . h chunk) for the lane's two rows.
 __device__ __forceinline__ void down_dot(float (&acc)[2], const DownRows& d, const uint32_t* hrow, float f, int lane) {
@@ -219,39 +193,11 @@ __device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const Decode
   float my_logit = 0.f;
   int my_e = 0, my_rank = 0;
   if (wave == 0) {
-    const uint64_t* lw = lw_all + (size_t)rep * FL_E + 4 * lane;
     uint64_t wd[4];
-    for (uint32_t spin = 0;; ++spin) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wd[q] = __hip_atomic_load(lw + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bool ok = true;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ok = ok && (uint32_t)(wd[q] >> 32) == epoch;
-      if (__all(ok)) break;
-      if (spin >= lim) { *ws.error = 1u; break; }
-    }
+    poll_lane_words4(wd, lw_all + (size_t)rep * FL_E, epoch, ws.error, lim);
     uint64_t key[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      key[q] = ((uint64_t)float_order_key(__uint_as_float((uint32_t)wd[q])) << 32) | (uint32_t)~(uint32_t)(4 * lane + q);
-#define FLINT_CSWAP(i, j) { const uint64_t hi_ = key[i] > key[j] ? key[i] : key[j]; \
-                            const uint64_t lo_ = key[i] > key[j] ? key[j] : key[i]; key[i] = hi_; key[j] = lo_; }
-    FLINT_CSWAP(0, 1) FLINT_CSWAP(2, 3) FLINT_CSWAP(0, 2) FLINT_CSWAP(1, 3) FLINT_CSWAP(1, 2)
-#undef FLINT_CSWAP
-    uint64_t my_key = 0ull;                        // lane k: the k-th selected key
-#pragma unroll
-    for (int k = 0; k < (KC ? KC : FLINT_MAX_TOP_K); ++k) {
-      if (!KC && k >= K) break;                    // the same in every lane
-      const uint32_t hi = (uint32_t)(key[0] >> 32);
-      const uint32_t mhi = wave_max_u32_all(hi);
-      const int wl = __ffsll((long long)__ballot(hi == mhi)) - 1;
-      const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)key[0], wl);
-      const uint64_t sk = ((uint64_t)mhi << 32) | mlo;
-      my_key = lane == k ? sk : my_key;
-      const bool win = lane == wl;
-      key[0] = win ? key[1] : key[0]; key[1] = win ? key[2] : key[1];
-      key[2] = win ? key[3] : key[2]; key[3] = win ? 0ull : key[3];
-    }
+    logit_keys(key, wd);
+    const uint64_t my_key = topk_lane_key<KC>(key, K);   // lane k: the k-th selected key
     my_e = (int)~(uint32_t)my_key;
     my_logit = float_from_order_key((uint32_t)(my_key >> 32));
 #pragma unroll

@@ -48,7 +48,7 @@ __device__ __forceinline__ DecodeWs pin_decode_ws(const DecodeWs& in) {
   DecodeWs w = in;
   w.epoch = pin_sgpr(in.epoch); w.error = pin_sgpr(in.error); w.wait_limit = pin_sgpr(in.wait_limit);
   w.logit_words = pin_sgpr(in.logit_words); w.h_words = pin_sgpr(in.h_words);
-  w.x_words = pin_sgpr(in.x_words);
+  w.x_words = pin_sgpr(in.x_words); w.hb_words = pin_sgpr(in.hb_words); w.p_words = pin_sgpr(in.p_words);
   return w;
 }
 
