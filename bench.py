@@ -13,19 +13,25 @@ Reported (one JSON line):
                returned expert indices), the router matrix, and the
                activations in and out
   roofline     the dominant kernel: at batch 1 the whole layer is one launch
-               (fused_decode_b1_kernel), so its algorithmic bytes per launch
-               over its average duration (HIP events around the graph of
-               back-to-back launches on the launch stream) against 8 TB/s;
-               the three-kernel path's per-stage times are reported beside
+               (flint_b1_kernel), so its algorithmic bytes per launch over
+               its average duration (HIP events around the graph replays on
+               the launch stream) against 8 TB/s, and against the best rate
+               of a plain read of the same number of bytes
+               (flint_stream_read); the three-kernel path's per-stage times
+               are reported beside
   cpu_baseline the float64 NumPy oracle on a bounded sample of the same
-               workload, on the host, one thread
-  batch8       the same layer at batch 8 (up to 48 distinct experts)
+               workload, on the host, with all of its threads and with one
+  batch8       the same layer at batch 8 (up to 48 distinct experts), one
+               launch of flint_b8_kernel per layer
   decode_step  the 49-sublayer decode step (47 MoE + 2 dense, RMSNorm,
                residual) at batch 1, NVFP4 and BF16 weights
   prefill      8,192 tokens through one layer: TFLOP/s against the BF16
                MFMA peak, for i.i.d. and for skewed (correlated) tokens
   lm_head      an NVFP4 LM-head GEMV (2048 -> 150,144, 173 MB) through
                flint_dense_gemv at batch 1 and 8: TB/s against 8 TB/s
+The timed calls are replays of a HIP graph of back-to-back layer calls (host
+launch cost is not on the clock), on activations and layer copies that the
+warm-up calls did not use; the decode error word is checked after them.
 The timed loops replay HIP graphs of the layer calls, so host launch cost is
 not on the clock.
 """
@@ -104,22 +110,24 @@ class Bench:
         r = self.runners[i % len(self.runners)]
         r(self.x[i], out=self.out[i], topk_idx=self.idx[i], topk_w=self.w[i])
 
-    def graph(self, n_steps):
+    def graph(self, n_steps, first=0):
+        """A graph of calls first .. first + n_steps - 1 (call i: activations
+        i, layer copy i mod copies)."""
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for i in range(min(n_steps, 3)):     # eager warm-up before capture
+            for i in range(first, first + min(n_steps, 3)):     # eager warm-up before capture
                 self.call(i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(n_steps):
+            for i in range(first, first + n_steps):
                 self.call(i)
         return g
 
-    def distinct(self, n_steps):
-        idx = self.idx[:n_steps].cpu()
+    def distinct(self, n_steps, first=0):
+        idx = self.idx[first:first + n_steps].cpu()
         return [len(set(idx[i].reshape(-1).tolist())) for i in range(n_steps)]
 
     def stage_times(self, n_launch=256, ws_per_copy=4, flags=fm.FLINT_SPLIT):
@@ -312,6 +320,63 @@ def bench_prefill(layer, shape, seed, T=8192, reps=5):
     return out
 
 
+def timed_replays(graph, reps):
+    """Seconds of each of `reps` back-to-back replays (HIP events on the
+    launch stream between them), and of all of them together."""
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        graph.replay()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    each = [ev[r].elapsed_time(ev[r + 1]) * 1e-3 for r in range(reps)]
+    return each, ev[0].elapsed_time(ev[reps]) * 1e-3
+
+
+def percentiles(xs):
+    ys = sorted(xs)
+    def q(f):
+        return ys[min(len(ys) - 1, int(round(f * (len(ys) - 1))))]
+    return q(0.1), q(0.5), q(0.9)
+
+
+def read_ceiling(dev, nbytes, n_bufs=None, reps=50):
+    """The best rate of flint_stream_read over a few launch shapes for a read
+    of nbytes (rotating buffers totalling > 600 MB, past the 256 MB cache)."""
+    nbytes = int(nbytes) // 16 * 16
+    n_bufs = n_bufs or max(2, int(600e6 // nbytes) + 1)
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(n_bufs)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    n16 = nbytes // 16
+    shapes = [(256, 8, (n16 + 2047) // 2048), (64, 8, (n16 + 511) // 512), (512, 8, 256), (512, 16, 256),
+              (768, 27, 256), (1024, 16, 512)]
+    best = None
+    for threads, loads, blocks in shapes:
+        def body(n):
+            for i in range(n):
+                fm.flint_stream_read(bufs[i % n_bufs], nbytes, threads, loads, blocks, sink)
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            body(n_bufs)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body(reps)
+        g.replay()
+        secs = timed(g) / reps
+        if best is None or secs < best[0]:
+            best = (secs, threads, loads, blocks)
+        del g
+    del bufs
+    secs, threads, loads, blocks = best
+    return {"bytes": nbytes, "us": round(secs * 1e6, 2), "tb_s": round(nbytes / secs / 1e12, 3),
+            "frac_hbm_peak": round(nbytes / secs / 1e9 / HBM_PEAK_GBS, 4),
+            "launch": f"{blocks} x {threads} threads, {loads} 16-byte loads per thread per pass"}
+
+
 def timed(graph, reps=1):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -324,54 +389,86 @@ def timed(graph, reps=1):
     return t0.elapsed_time(t1) * 1e-3     # seconds
 
 
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(layer_src, shape, budget_s: float):
-    """The oracle, one thread, on batch-1 calls of copy 0 until the time
-    budget is spent; TB/s of algorithmic bytes, like the GPU value."""
+    """The oracle (float64 NumPy) on batch-1 calls of copy 0 until the time
+    budget is spent, with all of the host's threads and with one thread;
+    TB/s of algorithmic bytes, like the GPU value."""
     from threadpoolctl import threadpool_limits
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _parity import oracle_experts
     from oracle import moe
 
-    with threadpool_limits(1):
-        torch.set_num_threads(1)
-        t_start = time.perf_counter()
-        n, nbytes = 0, 0
-        while time.perf_counter() - t_start < budget_s:
-            ex = oracle_experts(layer_src)    # decode from the source bytes every call
-            x = gen.numpy_f64(gen.activations(gen.seed_for(0, "cpu", n), 1, shape.hidden))
-            _, r = moe.moe_layer(x, ex, shape.top_k, False)
-            nbytes += step_bytes(shape, 1, len(set(r.idx.reshape(-1).tolist())))[0]
-            n += 1
-        el = time.perf_counter() - t_start
-    return {"value": nbytes / el / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} batch-1 decode calls of one Flint-shaped layer (copy 0), "
-                      f"{el:.1f} s, float64 NumPy, 1 thread",
-            "us_per_layer": el / n * 1e6}
+    def run(threads):
+        with threadpool_limits(threads):
+            torch.set_num_threads(threads)
+            t_start = time.perf_counter()
+            n, nbytes = 0, 0
+            while time.perf_counter() - t_start < budget_s:
+                ex = oracle_experts(layer_src)    # decode from the source bytes every call
+                x = gen.numpy_f64(gen.activations(gen.seed_for(0, "cpu", n), 1, shape.hidden))
+                _, r = moe.moe_layer(x, ex, shape.top_k, False)
+                nbytes += step_bytes(shape, 1, len(set(r.idx.reshape(-1).tolist())))[0]
+                n += 1
+            el = time.perf_counter() - t_start
+        return n, nbytes, el
+
+    host = host_cpu()
+    n_all = host["cpu_count"] or 1
+    n, nbytes, el = run(n_all)
+    n1, nbytes1, el1 = run(1)
+    torch.set_num_threads(n_all)
+    return {"value": nbytes / el / 1e12, "unit": "TB/s", "cores": n_all, "kind": "oracle",
+            "sample": f"{n} batch-1 decode calls of one Flint-shaped layer (copy 0), {el:.1f} s, "
+                      f"float64 NumPy, {n_all} threads",
+            "us_per_layer": el / n * 1e6,
+            "one_thread": {"value": nbytes1 / el1 / 1e12, "cores": 1, "us_per_layer": el1 / n1 * 1e6,
+                           "sample": f"{n1} calls, {el1:.1f} s"},
+            "host": host}
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_decode_b1_flint_hbm_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_moe_decode_amd", "csrc", f) for f in ("fused.hip", "fused_common.hpp", "common.hpp")]
+CSRC = os.path.join(ROOT, "w4a16_moe_decode_amd", "csrc")
+# per kernel: the committed counter summary and the sources it was taken from
+TRAFFIC = {
+    "flint_b1_kernel": (os.path.join(ROOT, "profiles", "flint_b1_kernel_decode_b1_hbm_traffic.txt"),
+                        ("flint_b1.hip", "flint_common.hpp", "fused_common.hpp", "common.hpp")),
+    "flint_b8_kernel": (os.path.join(ROOT, "profiles", "flint_b8_kernel_decode_b8_hbm_traffic.txt"),
+                        ("flint_b8.hip", "flint_common.hpp", "fused_common.hpp", "common.hpp")),
+}
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(files) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the single-launch layer from the committed
-    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
-    counter's reading for a plain copy of known size), or None when the
-    kernel's source has changed since the counters were taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of a kernel from its committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    plain copy of known size), or None when the kernel's source has changed
+    since the counters were taken."""
+    path, files = TRAFFIC[kernel]
     try:
-        with open(TRAFFIC_SUMMARY) as fh:
+        with open(path) as fh:
             kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith("#"))
     except OSError:
         return None
-    if kv.get("kernel_source_sha256_16", "").strip() != kernel_source_digest():
+    if kv.get("kernel_source_sha256_16", "").strip() != kernel_source_digest(files):
         return None
     return {"bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
             "read_bytes": float(kv["read_bytes_per_launch"]),
@@ -382,8 +479,10 @@ def measured_traffic():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--steps", type=int, default=2048,
+                    help="timed layer calls: replays of a graph of --graph-calls calls")
     ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--graph-calls", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copies", type=int, default=N_COPIES)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -416,38 +515,55 @@ def main():
     print(f"[bench] generating {args.copies} layer copies on the GPU", file=sys.stderr, flush=True)
     layers, src0 = build_copies(shape, args.copies, args.seed, dev)
 
+    G = args.graph_calls
+    reps = max(1, args.steps // G)
+    steps = reps * G
     res = {}
     for batch in ([1] if args.no_batch8 else [1, 8]):
-        b = Bench(layers, shape, batch, max(args.steps, args.warmup), args.seed)
-        gw = b.graph(args.warmup)
-        gt = b.graph(args.steps)
+        # warm-up calls 0 .. W-1 and timed calls W .. W+G-1 use different
+        # activations (and so different experts) of the rotating copies
+        b = Bench(layers, shape, batch, args.warmup + G, args.seed)
+        gw = b.graph(args.warmup, 0)
+        gt = b.graph(G, args.warmup)
         gw.replay()
-        torch.cuda.synchronize()
-        secs = timed(gt)
-        dist = b.distinct(args.steps)
-        nbytes = sum(step_bytes(shape, batch, d)[0] for d in dist)
+        each, secs = timed_replays(gt, reps)
+        err = fm.decode_error_word(b.runners[0])
+        if err != 0:
+            raise SystemExit(f"decode error word {err} after the timed batch-{batch} calls")
+        dist = b.distinct(G, args.warmup)
+        nb_graph = sum(step_bytes(shape, batch, d)[0] for d in dist)
+        nbytes = nb_graph * reps
         gu_bytes = sum(step_bytes(shape, batch, d)[1] for d in dist) / len(dist)
+        p10, p50, p90 = percentiles([e / G * 1e6 for e in each])
         st_us = b.stage_times()
         res[batch] = dict(secs=secs, nbytes=nbytes, gu_bytes=gu_bytes, stage_us=st_us,
-                          distinct=sum(dist) / len(dist))
-        print(f"[bench] batch {batch}: {secs / args.steps * 1e6:.2f} us/layer, "
-              f"{nbytes / secs / 1e12:.3f} TB/s, stages {['%.2f' % s for s in st_us]} us, "
-              f"distinct experts {res[batch]['distinct']:.2f}", file=sys.stderr, flush=True)
+                          distinct=sum(dist) / len(dist), pct=(p10, p50, p90),
+                          path=fm.flint_moe_decode_path(b.runners[0].shape, batch))
+        print(f"[bench] batch {batch}: {secs / steps * 1e6:.2f} us/layer (replays p10/p50/p90 "
+              f"{p10:.2f}/{p50:.2f}/{p90:.2f}), {nbytes / secs / 1e12:.3f} TB/s, split-path stages "
+              f"{['%.2f' % s for s in st_us]} us, distinct experts {res[batch]['distinct']:.2f}",
+              file=sys.stderr, flush=True)
         del b, gw, gt
 
+    ceil = {}
+    for batch, r in res.items():
+        ceil[batch] = read_ceiling(dev, r["nbytes"] / steps)
+        print(f"[bench] plain read of {ceil[batch]['bytes'] / 1e6:.1f} MB: {ceil[batch]['us']} us, "
+              f"{ceil[batch]['tb_s']} TB/s ({ceil[batch]['launch']})", file=sys.stderr, flush=True)
+
     r1 = res[1]
-    us = r1["secs"] / args.steps * 1e6
+    us = r1["secs"] / steps * 1e6
     gu_us = r1["stage_us"][1]
     # batch 1 runs as one kernel launch per layer: the dominant (only) kernel
     # is the single-launch layer, timed by the graph of back-to-back calls
     achieved = r1["nbytes"] / r1["secs"] / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic("flint_b1_kernel")
     line = {
         "metric": METRIC,
         "value": round(r1["nbytes"] / r1["secs"] / 1e12, 4),
         "unit": "TB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 6),
         "higher_is_better": True,
@@ -461,25 +577,37 @@ def main():
                    "weights": "nvfp4 (e2m1 + ue4m3/16 + fp32 per expert)", "activations": "bf16",
                    "layer_copies": args.copies, "parallelism": "single-gpu"},
         "us_per_layer": round(us, 3),
+        "us_per_layer_replays_p10_p50_p90": [round(v, 3) for v in r1["pct"]],
         "tokens_per_s_per_layer": round(1e6 / us, 1),
+        "timing": f"{reps} timed replays of a graph of {G} back-to-back calls (calls {args.warmup}.."
+                  f"{args.warmup + G - 1}: activations and layer copies not used by the {args.warmup} "
+                  f"warm-up calls); HIP events on the launch stream; percentiles of the per-replay means",
         "split_path_stage_us": {"route": round(r1["stage_us"][0], 3), "gate_up": round(gu_us, 3),
                                 "down": round(r1["stage_us"][2], 3)},
-        "roofline": {"bound": "hbm", "kernel": "fused_decode_b1_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "flint_b1_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "traffic_read_write": [traffic["read_bytes"], traffic["write_bytes"]] if traffic else None,
-                     "algorithmic_bytes_per_launch": round(r1["nbytes"] / args.steps)},
+                     "algorithmic_bytes_per_launch": round(r1["nbytes"] / steps),
+                     "read_ceiling": ceil[1],
+                     "frac_of_read_ceiling": round(achieved / 1e3 / ceil[1]["tb_s"], 4)},
     }
     if 8 in res:
         r8 = res[8]
-        us8 = r8["secs"] / args.steps * 1e6
-        gu8 = r8["gu_bytes"] / (r8["stage_us"][1] * 1e-6) / 1e9
+        us8 = r8["secs"] / steps * 1e6
+        a8 = r8["nbytes"] / r8["secs"] / 1e9
         line["batch8"] = {"us_per_layer": round(us8, 3),
-                          "tb_s": round(r8["nbytes"] / r8["secs"] / 1e12, 4),
+                          "us_per_layer_replays_p10_p50_p90": [round(v, 3) for v in r8["pct"]],
+                          "tb_s": round(a8 / 1e3, 4),
+                          "kernel": "flint_b8_kernel" if r8["path"] == fm.FLINT_PATH_SINGLE_BATCH else "three kernels",
+                          "frac_hbm_peak": round(a8 / HBM_PEAK_GBS, 4),
+                          "read_ceiling": ceil[8],
+                          "frac_of_read_ceiling": round(a8 / 1e3 / ceil[8]["tb_s"], 4),
                           "tokens_per_s_per_layer": round(8e6 / us8, 1),
                           "distinct_experts": round(r8["distinct"], 2),
-                          "stage_us": [round(v, 3) for v in r8["stage_us"]],
-                          "gate_up_frac": round(gu8 / HBM_PEAK_GBS, 4)}
+                          "algorithmic_bytes_per_call": round(r8["nbytes"] / steps),
+                          "traffic": (measured_traffic("flint_b8_kernel") or {}).get("bytes_per_launch"),
+                          "split_path_stage_us": [round(v, 3) for v in r8["stage_us"]]}
     if not args.no_prefill:
         line["prefill"] = bench_prefill(layers[0], shape, args.seed)
     if not args.no_lm_head:

@@ -379,6 +379,20 @@ FLINT_API int32_t flint_dense_gemv(const void* codes, const void* scales, const 
                          const void* x, int32_t batch, void* y, int32_t epilogue,
                          const void* aux, const void* gamma, float rms_eps, void* stream);
 
+/* Measurement utility (not part of the layer computation): a plain read of
+ * `bytes` of device memory at `src`, for the achievable HBM read rate of a
+ * transfer of that size, against which the decode kernels' rates are
+ * compared.  Each of blocks x threads threads reads `loads` 16-byte words
+ * per pass of a grid-stride loop, all issued before any is used.
+ *   src      (device) 16-byte aligned; bytes > 0, a multiple of 16
+ *   threads  64..1024, a multiple of 64;  loads 4, 8, 16 or 27;  blocks >= 1
+ *   sink     (device) uint32 [1]: written only if the fold of the data equals
+ *            0x9e3779b9 (so the reads are not dropped)
+ * Returns FLINT_ERR_INVALID_ARG / _ALIGNMENT / _UNSUPPORTED for bad
+ * arguments (nothing enqueued), FLINT_ERR_DEVICE on a launch error. */
+FLINT_API int32_t flint_stream_read(const void* src, int64_t bytes, int32_t threads, int32_t loads,
+                                    int32_t blocks, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -218,3 +218,19 @@ def test_decode_and_prefill_workspace_parts_do_not_overlap():
     st = L.flint_moe_prefill(ctypes.byref(s), ctypes.byref(w), v(16), 2, v(32), None, None, None,
                              v(4096), sizes[0], None)
     assert st == fm.FLINT_ERR_WORKSPACE                 # 2 tokens need more than the 1-token size
+
+
+def test_stream_read_validation_codes():
+    """The measurement read checks its arguments before enqueuing anything."""
+    L = fm.lib()
+    v = ctypes.c_void_p
+    s = L.flint_stream_read
+    assert s(None, 64, 256, 8, 1, v(16), None) == fm.FLINT_ERR_INVALID_ARG
+    assert s(v(16), 0, 256, 8, 1, v(16), None) == fm.FLINT_ERR_INVALID_ARG
+    assert s(v(16), 24, 256, 8, 1, v(16), None) == fm.FLINT_ERR_INVALID_ARG     # not whole 16-byte words
+    assert s(v(16), 64, 256, 8, 0, v(16), None) == fm.FLINT_ERR_INVALID_ARG
+    assert s(v(16), 64, 256, 8, 1, None, None) == fm.FLINT_ERR_INVALID_ARG
+    assert s(v(24), 64, 256, 8, 1, v(16), None) == fm.FLINT_ERR_ALIGNMENT
+    assert s(v(16), 64, 96, 8, 1, v(16), None) == fm.FLINT_ERR_UNSUPPORTED      # threads not 64k
+    assert s(v(16), 64, 2048, 8, 1, v(16), None) == fm.FLINT_ERR_UNSUPPORTED
+    assert s(v(16), 64, 256, 5, 1, v(16), None) == fm.FLINT_ERR_UNSUPPORTED     # loads not 4/8/16/27

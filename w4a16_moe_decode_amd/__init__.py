@@ -56,7 +56,7 @@ EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_workspace_error", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
     "flint_moe_decode", "flint_moe_decode_noalloc", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
-    "flint_moe_prefill", "flint_dense_gemv",
+    "flint_moe_prefill", "flint_dense_gemv", "flint_stream_read",
 )
 
 
@@ -123,6 +123,8 @@ def lib() -> ctypes.CDLL:
         L.flint_dense_gemv.restype = i32
         L.flint_dense_gemv.argtypes = [vp, vp, vp, vp, i32, i32, u32, vp, i32, vp, i32, vp, vp,
                                        ctypes.c_float, vp]
+        L.flint_stream_read.restype = i32
+        L.flint_stream_read.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -250,6 +252,12 @@ def flint_dense_gemv(codes, scales, gscale, w_bf16, rows, cols, flags, x, batch,
     _check("flint_dense_gemv", lib().flint_dense_gemv(
         _p(codes), _p(scales), _p(gscale), _p(w_bf16), rows, cols, flags, _p(x), batch, _p(y),
         epilogue, _p(aux), _p(gamma), ctypes.c_float(rms_eps), _stream(stream)))
+
+
+def flint_stream_read(src, nbytes, threads, loads, blocks, sink, stream=None):
+    """A plain read of nbytes of device memory (a measurement utility)."""
+    _check("flint_stream_read", lib().flint_stream_read(_p(src), int(nbytes), threads, loads, blocks,
+                                                         _p(sink), _stream(stream)))
 
 
 # ------------------------------------------------------------ conveniences --
