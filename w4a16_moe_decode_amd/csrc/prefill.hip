@@ -17,7 +17,9 @@
 //   scatter   stable permutation of (token, slot) pairs by (expert, token)
 //   gate_up   grouped GEMM per expert (shared expert = last group, all
 //             tokens): rows gathered from xn, NVFP4 weight tiles decoded
-//             into LDS as exact BF16, MFMA, then SiLU(g) * u -> h (BF16)
+//             into LDS as exact BF16, MFMA, then SiLU(g) * u -> h (BF16);
+//             all column tiles of a row tile on one XCD (its L2 serves
+//             the gathered rows)
 //   down      grouped GEMM h . W_d^T -> y (fp32, tensor scale applied)
 //   combine   out_t = BF16(sum_k w_tk y[pos(t,k)] + y[shared row of t])
 //             (+ residual)
@@ -206,6 +208,21 @@ __device__ __forceinline__ void gemm_k_loop(Acc& acc, uint16_t (&la)[2][BM * LDS
     k_step<3>(acc, la, lb, ring, kt0 + 3, nk);
   }
 }
+
+// --------------------------------------------------- XCD-aware tile order --
+// Workgroup i of a launch runs on XCD i mod 8, and each XCD has its own L2.
+// The grouped GEMMs take a 1-D grid in which workgroup i computes row tile
+// 8 (i / 8 / ntn) + i mod 8 and column tile (i / 8) mod ntn: all column
+// tiles of a row tile run on one XCD, one after the other, so its gathered
+// A rows are fetched from memory once per XCD and then served from that
+// L2, instead of being fetched by every column tile on all eight XCDs.
+struct TileIdx { int m, n; };
+__device__ __forceinline__ TileIdx tile_of_block(int ntn) {
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const int mg = slot / ntn;
+  return TileIdx{mg * 8 + xcd, slot - mg * ntn};
+}
+inline unsigned grouped_grid(int max_tiles, int ntn) { return (unsigned)(((max_tiles + 7) / 8) * 8 * ntn); }
 
 // ---------------------------------------------------------- workspaces ----
 }  // namespace
@@ -502,13 +519,15 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(LayerArgs a, Prefi
                                                               const uint16_t* xin) {
   __shared__ uint16_t la[2][BM * LDS_STRIDE];
   __shared__ uint16_t lb[2][BN * LDS_STRIDE];
-  if ((int)blockIdx.x >= *ws.ntiles) return;
-  const int2 tile = ws.tiles[blockIdx.x];
+  const int imax0 = a.I > a.SI ? a.I : a.SI;
+  const TileIdx ti = tile_of_block((imax0 + BN / 2 - 1) / (BN / 2));
+  if (ti.m >= *ws.ntiles) return;
+  const int2 tile = ws.tiles[ti.m];
   const int g = tile.x, m0 = tile.y;
   const int E = a.E, K = a.K, H = a.H;
   const bool shared = g == E;
   const int inter = shared ? a.SI : a.I;
-  const int i0 = blockIdx.y * (BN / 2);
+  const int i0 = ti.n * (BN / 2);
   if (i0 >= inter) return;
   const int cnt = shared ? T : ws.counts[g];
   const int base = shared ? 0 : ws.offsets[g];
@@ -587,13 +606,14 @@ template <int WF>
 __global__ __launch_bounds__(256) void prefill_down_kernel(LayerArgs a, PrefillWs ws, int T) {
   __shared__ uint16_t la[2][BM * LDS_STRIDE];
   __shared__ uint16_t lb[2][BN * LDS_STRIDE];
-  if ((int)blockIdx.x >= *ws.ntiles) return;
-  const int2 tile = ws.tiles[blockIdx.x];
+  const TileIdx ti = tile_of_block((a.H + BN - 1) / BN);
+  if (ti.m >= *ws.ntiles) return;
+  const int2 tile = ws.tiles[ti.m];
   const int g = tile.x, m0 = tile.y;
   const int E = a.E, K = a.K, H = a.H;
   const bool shared = g == E;
   const int inter = shared ? a.SI : a.I;
-  const int n0 = blockIdx.y * BN;
+  const int n0 = ti.n * BN;
   const int cnt = shared ? T : ws.counts[g];
   const size_t base = shared ? (size_t)T * K : (size_t)ws.offsets[g];
   const int imax = a.I > a.SI ? a.I : a.SI;
@@ -707,8 +727,8 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
-  const dim3 ggu(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2));
-  const dim3 gdn(ws.max_tiles, (a.H + BN - 1) / BN);
+  const dim3 ggu(grouped_grid(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2)));
+  const dim3 gdn(grouped_grid(ws.max_tiles, (a.H + BN - 1) / BN));
   if (bf) {
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_BF16>, ggu, dim3(256), 0, st, a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_kernel<FMT_BF16>, gdn, dim3(256), 0, st, a, ws, T);
