@@ -16,9 +16,11 @@ Modules:
   bf16     float64 -> bfloat16 round-to-nearest-even
   moe      RMSNorm, router + sigmoid top-k, SwiGLU expert, combine, the
            decode layer, dense MLP, the multi-layer decode step, prefill
+  attn     per-head Q/K RMSNorm, rotate-half RoPE and the KV-cache write
+           of an attention layer's projected heads
 
 Parity pins (tests/test_oracle_*.py) tie every function to something other
 than itself.  Parity against values printed on the pages is unpinned: the
 pages print no worked numerical example of the layer.
 """
-from . import bf16, formats, moe  # noqa: F401
+from . import attn, bf16, formats, moe  # noqa: F401
