@@ -29,6 +29,8 @@ Reported (one JSON line):
                MFMA peak, for i.i.d. and for skewed (correlated) tokens
   lm_head      an NVFP4 LM-head GEMV (2048 -> 150,144, 173 MB) through
                flint_dense_gemv at batch 1 and 8: TB/s against 8 TB/s
+  qk_norm_rope_kv  the fused per-head Q/K RMSNorm + RoPE + KV-cache write
+               (flint_qk_norm_rope_kv) for 8 and 8,192 tokens
 The timed calls are replays of a HIP graph of back-to-back layer calls (host
 launch cost is not on the clock), on activations and layer copies that the
 warm-up calls did not use; the decode error word is checked after them.
@@ -276,6 +278,56 @@ def bench_lm_head(dev, seed, n_copies=3, reps=30):
     return out
 
 
+def bench_attn_prep(dev, seed, reps=50):
+    """The fused per-head Q/K RMSNorm + RoPE + KV-cache write
+    (flint_qk_norm_rope_kv) at the Flint attention shape (GQA 32/4, d 128):
+    8 decode tokens, and 8,192 prefill tokens over 3 rotating input copies
+    (each 84 MB in, 84 MB out).  Bytes: projection rows and table rows read,
+    q rows and K/V cache rows written."""
+    sh = gen.ATTN_FLINT
+    D = sh.head_dim
+    table = gen.rope_table(600, D, device=dev)
+    gq = gen.rmsnorm_gamma(gen.seed_for(seed, "attn-gq"), D, dev)
+    gk = gen.rmsnorm_gamma(gen.seed_for(seed, "attn-gk"), D, dev)
+    shape = fm.FlintAttnShape(sh.n_q_heads, sh.n_kv_heads, D, fm.FLINT_ATTN_ROPE, 1e-6)
+    out = {"shape": "32 q / 4 kv heads, d 128, RoPE"}
+    for T, n_copies in ((8, 1), (8192, 3)):
+        g = torch.Generator(device="cpu").manual_seed(gen.seed_for(seed, "attn", T))
+        sets = []
+        for c in range(n_copies):
+            qkv = gen.attn_rows(gen.seed_for(seed, "attn-qkv", T, c), T, sh, dev)
+            pos = torch.randint(0, 600, (T,), generator=g, dtype=torch.int32).to(dev)
+            slots = torch.randperm(max(T, 1024), generator=g)[:T].to(torch.int32).to(dev)
+            kc = torch.empty((max(T, 1024), sh.n_kv_heads, D), dtype=torch.bfloat16, device=dev)
+            vc = torch.empty_like(kc)
+            q = torch.empty((T, sh.n_q_heads, D), dtype=torch.bfloat16, device=dev)
+            sets.append((qkv, pos, slots, kc, vc, q))
+
+        def body(n):
+            for i in range(n):
+                qkv, pos, slots, kc, vc, q = sets[i % n_copies]
+                fm.flint_qk_norm_rope_kv(shape, qkv, T, pos, table, 600, slots, kc, vc, kc.shape[0], gq, gk, q)
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            body(n_copies)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            body(reps)
+        gr.replay()
+        secs = timed(gr) / reps
+        nb = T * ((sh.n_q_heads + 2 * sh.n_kv_heads) * D * 2 + D * 4 + 8 + sh.n_q_heads * D * 2
+                  + 2 * sh.n_kv_heads * D * 2)
+        out[f"tokens{T}"] = {"us": round(secs * 1e6, 2), "tb_s": round(nb / secs / 1e12, 3),
+                             "frac_hbm_peak": round(nb / secs / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] q/k norm + rope + kv write, {T} tokens: {secs * 1e6:.2f} us, "
+              f"{nb / secs / 1e12:.3f} TB/s", file=sys.stderr, flush=True)
+        del gr, sets
+    return out
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -491,6 +543,7 @@ def main():
     ap.add_argument("--no-step", action="store_true", help="skip the 49-layer decode step")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8,192-token prefill")
     ap.add_argument("--no-lm-head", action="store_true", help="skip the NVFP4 LM-head GEMV")
+    ap.add_argument("--no-attn", action="store_true", help="skip the fused Q/K norm + RoPE + KV write")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy (fp32 negate) of this many MiB three "
                          "times, so that a counter run can scale FETCH_SIZE / WRITE_SIZE by it")
@@ -610,6 +663,8 @@ def main():
                           "split_path_stage_us": [round(v, 3) for v in r8["stage_us"]]}
     if not args.no_prefill:
         line["prefill"] = bench_prefill(layers[0], shape, args.seed)
+    if not args.no_attn:
+        line["qk_norm_rope_kv"] = bench_attn_prep(dev, args.seed)
     if not args.no_lm_head:
         line["lm_head"] = bench_lm_head(dev, args.seed)
     if not args.no_step:

@@ -197,6 +197,38 @@ def dense_mlp_source(hidden: int, inter: int, seed: int, device="cpu", layout: s
             tensor_scales(seed_for(seed, "gscale"), 1, gscale_mode))
 
 
+# ------------------------------------------------------------- attention --
+
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int = 128
+
+
+ATTN_FLINT = AttnShape(n_q_heads=32, n_kv_heads=4, head_dim=128)   # GQA 32/4, d 128
+
+
+def rope_table(n_pos: int, head_dim: int = 128, base: float = 10000.0, device="cpu") -> torch.Tensor:
+    """A caller's rotary table, float32 [n_pos][head_dim]: row p holds the
+    cosines of the head_dim / 2 angles p * base^(-2i / head_dim), then their
+    sines (angles and functions in float64, stored as float32)."""
+    i = torch.arange(head_dim // 2, dtype=torch.float64)
+    inv = base ** (-2.0 * i / head_dim)
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).to(device)
+
+
+def attn_rows(seed: int, n_tokens: int, shape: AttnShape, device="cpu") -> torch.Tensor:
+    """Projection rows [T][(n_q + 2 n_kv) d] BF16 ~ N(0,1), heads with
+    per-head scales spread over two decades so that the norms matter."""
+    g = _gen(seed, device)
+    n_heads = shape.n_q_heads + 2 * shape.n_kv_heads
+    z = torch.randn((n_tokens, n_heads, shape.head_dim), generator=g, device=device, dtype=torch.float32)
+    sc = 10.0 ** (2.0 * torch.rand((n_tokens, n_heads, 1), generator=g, device=device) - 1.0)
+    return (z * sc).reshape(n_tokens, -1).to(torch.bfloat16)
+
+
 def numpy_u8(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").numpy()
 

@@ -379,6 +379,56 @@ FLINT_API int32_t flint_dense_gemv(const void* codes, const void* scales, const 
                          const void* x, int32_t batch, void* y, int32_t epilogue,
                          const void* aux, const void* gamma, float rms_eps, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Attention-side step of the same layers: per-head Q/K RMSNorm, rotary
+ * position embedding and the BF16 KV-cache write, fused into one kernel
+ * ([D0] "Optimizations", first bullet: one kernel instead of three;
+ * "Model architecture": GQA, 32 query and 4 KV heads of dimension 128,
+ * per-head Q/K RMSNorm, RoPE on the 35 sliding-window layers and none on
+ * the 14 full-context layers, BF16 KV cache).
+ * ---------------------------------------------------------------------- */
+#define FLINT_ATTN_ROPE  0x1u   /* rotate Q and K (sliding-window layers); without it
+                                   the heads are only normalised (NoPE layers) */
+
+typedef struct flint_attn_shape {
+  int32_t n_q_heads;    /* query heads (32), a multiple of n_kv_heads      */
+  int32_t n_kv_heads;   /* KV heads (4)                                    */
+  int32_t head_dim;     /* 128, the only value supported                   */
+  uint32_t flags;       /* FLINT_ATTN_ROPE or 0                            */
+  float rms_eps;        /* RMSNorm epsilon of the per-head norms (1e-6)    */
+} flint_attn_shape;
+
+/* For each of n_tokens tokens, from its projection row
+ *   qkv        (device) BF16 [n_tokens][(n_q + 2 n_kv) * 128]: the q heads,
+ *              then the k heads, then the v heads
+ * computes, per q and k head h, y = BF16(BF16(x_h / sqrt(mean(x_h^2) + eps))
+ * * gamma) and, with FLINT_ATTN_ROPE, the rotate-half rotation of the pairs
+ * (y_i, y_{i+64}), i < 64, by the angles of table row positions[t]:
+ * (y_i c_i - y_{i+64} s_i, y_{i+64} c_i + y_i s_i), rounded to BF16 once.
+ *   positions  (device) int32 [n_tokens], with FLINT_ATTN_ROPE (else unused,
+ *              may be NULL); a position outside 0..n_positions-1 is an error
+ *   cos_sin    (device) float32 [n_positions][128]: row p holds cos of the
+ *              64 angles of position p, then their sines (the caller's
+ *              rotary table); with FLINT_ATTN_ROPE, else may be NULL
+ *   slots      (device) int32 [n_tokens]: the KV-cache row of each token; a
+ *              negative slot writes no K or V (a padding token); a slot >=
+ *              n_slots is an error
+ *   k_cache, v_cache (device) BF16 [n_slots][n_kv][128]: row slots[t] gets
+ *              the token's normalised (and rotated) k heads and its v heads
+ *              unchanged; other rows are not touched
+ *   gamma_q, gamma_k (device) BF16 [128], shared by the heads of each role
+ *   q_out      (device) BF16 [n_tokens][n_q][128], must not overlap qkv
+ *   error      (device) int32 [1] or NULL: set to 1 when a token's position or
+ *              slot is out of range; nothing of that token is written
+ * Pointers 16-byte aligned (positions, slots, error: 4-byte).  Returns
+ * FLINT_ERR_INVALID_ARG / _UNSUPPORTED / _ALIGNMENT before enqueuing
+ * anything, FLINT_ERR_DEVICE on a launch error.  Asynchronous on `stream`. */
+FLINT_API int32_t flint_qk_norm_rope_kv(const flint_attn_shape* shape, const void* qkv, int32_t n_tokens,
+                                        const int32_t* positions, const float* cos_sin, int32_t n_positions,
+                                        const int32_t* slots, void* k_cache, void* v_cache, int32_t n_slots,
+                                        const void* gamma_q, const void* gamma_k, void* q_out, int32_t* error,
+                                        void* stream);
+
 /* Measurement utility (not part of the layer computation): a plain read of
  * `bytes` of device memory at `src`, for the achievable HBM read rate of a
  * transfer of that size, against which the decode kernels' rates are

@@ -234,3 +234,33 @@ def test_stream_read_validation_codes():
     assert s(v(16), 64, 96, 8, 1, v(16), None) == fm.FLINT_ERR_UNSUPPORTED      # threads not 64k
     assert s(v(16), 64, 2048, 8, 1, v(16), None) == fm.FLINT_ERR_UNSUPPORTED
     assert s(v(16), 64, 256, 5, 1, v(16), None) == fm.FLINT_ERR_UNSUPPORTED     # loads not 4/8/16/27
+
+
+def test_qk_norm_rope_kv_validation_codes():
+    """The fused Q/K norm + RoPE + KV write checks its arguments before
+    enqueuing anything."""
+    L = fm.lib()
+    v = ctypes.c_void_p
+    f = L.flint_qk_norm_rope_kv
+    ok = fm.FlintAttnShape(32, 4, 128, fm.FLINT_ATTN_ROPE, 1e-6)
+    nope = fm.FlintAttnShape(32, 4, 128, 0, 1e-6)
+    args = lambda sh, **kw: [ctypes.byref(sh), kw.get("qkv", v(16)), kw.get("T", 8), kw.get("pos", v(32)),
+                             kw.get("cs", v(48)), kw.get("P", 600), kw.get("slots", v(64)), kw.get("kc", v(80)),
+                             kw.get("vc", v(96)), kw.get("S", 100), kw.get("gq", v(112)), kw.get("gk", v(128)),
+                             kw.get("q", v(144)), kw.get("err", None), None]
+    assert f(*args(ok, qkv=None)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, slots=None)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, T=0)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, S=0)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, pos=None)) == fm.FLINT_ERR_INVALID_ARG          # RoPE needs positions and a table
+    assert f(*args(ok, cs=None)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, P=0)) == fm.FLINT_ERR_INVALID_ARG
+    for bad in (fm.FlintAttnShape(32, 4, 64, 0, 1e-6), fm.FlintAttnShape(30, 4, 128, 0, 1e-6),
+                fm.FlintAttnShape(32, 4, 128, 0x2, 1e-6), fm.FlintAttnShape(32, 4, 128, 0, -1.0)):
+        assert f(*args(bad)) == fm.FLINT_ERR_UNSUPPORTED
+    assert f(*args(ok, qkv=v(18))) == fm.FLINT_ERR_ALIGNMENT
+    assert f(*args(ok, slots=v(66))) == fm.FLINT_ERR_ALIGNMENT
+    assert f(*args(ok, cs=v(52))) == fm.FLINT_ERR_ALIGNMENT
+    assert f(*args(ok, err=v(34))) == fm.FLINT_ERR_ALIGNMENT
+    # without RoPE the table and positions are not needed (and not checked)
+    assert f(*args(nope, qkv=None, pos=None, cs=None, P=0)) == fm.FLINT_ERR_INVALID_ARG

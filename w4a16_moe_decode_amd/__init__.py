@@ -47,6 +47,8 @@ FLINT_EPI_NONE = 0
 FLINT_EPI_SWIGLU = 1
 FLINT_EPI_RESIDUAL = 2
 
+FLINT_ATTN_ROPE = 0x1
+
 MAX_DECODE_BATCH = 8
 WS_ERROR_OFFSET = 512
 WS_WAIT_LIMIT_OFFSET = 768
@@ -56,7 +58,7 @@ EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_workspace_error", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
     "flint_moe_decode", "flint_moe_decode_noalloc", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
-    "flint_moe_prefill", "flint_dense_gemv", "flint_stream_read",
+    "flint_moe_prefill", "flint_dense_gemv", "flint_qk_norm_rope_kv", "flint_stream_read",
 )
 
 
@@ -70,6 +72,11 @@ class FlintMoeShape(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("flags", ctypes.c_uint32), ("rms_eps", ctypes.c_float)]
+
+
+class FlintAttnShape(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("rms_eps", ctypes.c_float)]
 
 
 class FlintMoeWeights(ctypes.Structure):
@@ -123,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.flint_dense_gemv.restype = i32
         L.flint_dense_gemv.argtypes = [vp, vp, vp, vp, i32, i32, u32, vp, i32, vp, i32, vp, vp,
                                        ctypes.c_float, vp]
+        L.flint_qk_norm_rope_kv.restype = i32
+        L.flint_qk_norm_rope_kv.argtypes = [ctypes.POINTER(FlintAttnShape), vp, i32, vp, vp, i32, vp, vp, vp,
+                                            i32, vp, vp, vp, vp, vp]
         L.flint_stream_read.restype = i32
         L.flint_stream_read.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         _lib = L
@@ -252,6 +262,15 @@ def flint_dense_gemv(codes, scales, gscale, w_bf16, rows, cols, flags, x, batch,
     _check("flint_dense_gemv", lib().flint_dense_gemv(
         _p(codes), _p(scales), _p(gscale), _p(w_bf16), rows, cols, flags, _p(x), batch, _p(y),
         epilogue, _p(aux), _p(gamma), ctypes.c_float(rms_eps), _stream(stream)))
+
+
+def flint_qk_norm_rope_kv(shape: FlintAttnShape, qkv, n_tokens, positions, cos_sin, n_positions, slots,
+                          k_cache, v_cache, n_slots, gamma_q, gamma_k, q_out, error=None, stream=None):
+    """Per-head Q/K RMSNorm, RoPE (with FLINT_ATTN_ROPE) and the KV-cache
+    write of n_tokens projection rows (see include/flint_moe.h)."""
+    _check("flint_qk_norm_rope_kv", lib().flint_qk_norm_rope_kv(
+        ctypes.byref(shape), _p(qkv), n_tokens, _p(positions), _p(cos_sin), n_positions, _p(slots),
+        _p(k_cache), _p(v_cache), n_slots, _p(gamma_q), _p(gamma_k), _p(q_out), _p(error), _stream(stream)))
 
 
 def flint_stream_read(src, nbytes, threads, loads, blocks, sink, stream=None):
