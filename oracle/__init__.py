@@ -17,7 +17,8 @@ Modules:
   moe      RMSNorm, router + sigmoid top-k, SwiGLU expert, combine, the
            decode layer, dense MLP, the multi-layer decode step, prefill
   attn     per-head Q/K RMSNorm, rotate-half RoPE and the KV-cache write
-           of an attention layer's projected heads
+           of an attention layer's projected heads; decode attention with
+           learned sinks over a sliding window or the whole context
 
 Parity pins (tests/test_oracle_*.py) tie every function to something other
 than itself.  Parity against values printed on the pages is unpinned: the

@@ -1,5 +1,6 @@
 """Per-head Q/K RMSNorm, rotary position embedding and the KV-cache write of
-one attention layer's projected heads (oracle).
+one attention layer's projected heads, and decode attention with learned
+sinks over a sliding window or the full context (oracle).
 
 TEST INFRASTRUCTURE: see the package docstring for who may use it.
 
@@ -25,6 +26,22 @@ Readings where the pages are silent (each is listed in the design notes):
   * the fused projection row is [q heads | k heads | v heads]; V goes to the
     cache unchanged, K after its norm and RoPE; cache layout
     [slot][kv head][d]; a negative slot writes nothing (a padding token).
+
+Decode attention.  The pages fix: "Model architecture", first two bullets
+(35 layers see a 513-token window, the current token and the 512 before it;
+14 layers see the whole context; GQA 32/4, head dimension 128; learned
+attention sinks) and "Optimizations", fifth bullet (a decode attention
+kernel with sinks and sliding windows).  Readings:
+  * query head h reads KV head h // (n_q / n_kv) (consecutive query heads
+    share a KV head);
+  * score = scale * (q . k); a sink is one learned logit per query head that
+    joins the softmax's normaliser and carries no value:
+        out = sum_p exp(s_p) v_p / (sum_p exp(s_p) + exp(sink));
+  * a sequence of context length L (its newest token included) attends to
+    positions max(0, L - W) .. L - 1 for a window W, or 0 .. L - 1 when W is
+    0 (the full-context layers); position p lives in cache row
+    base + (p mod C), for the sequence's first row ``base`` and C rows per
+    sequence (C >= the attended span; a ring buffer when C is the window).
 """
 from __future__ import annotations
 
@@ -82,3 +99,47 @@ def qk_norm_rope_kv(qkv, n_q: int, n_kv: int, d: int, positions, slots, gamma_q,
             k_cache[slots[t]] = kn[t]
             v_cache[slots[t]] = v[t]
     return qn
+
+
+def attended_positions(length: int, window: int):
+    """Positions a decode token at context length ``length`` attends to."""
+    lo = max(0, length - window) if window > 0 else 0
+    return np.arange(lo, length)
+
+
+def decode_attention(q, k_cache, v_cache, seq_base, seq_len, ring: int, window: int, sinks, scale: float,
+                     with_abs: bool = False):
+    """One decode token per sequence.
+
+    q        [B][n_q][d] queries (after norm and RoPE)
+    k_cache, v_cache [S][n_kv][d]
+    seq_base [B] first cache row of each sequence; seq_len [B] its length
+    ring     cache rows per sequence; window 0 for the whole context
+    sinks    [n_q] one logit per query head
+
+    Returns out [B][n_q][d] (float64, unrounded); with ``with_abs`` also the
+    same mixture taken of |v| (sum_p w_p |v_p|, w the softmax weights), the
+    scale of the rounding error of any mixture of the values."""
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, n_q, d = q.shape
+    n_kv = kc.shape[1]
+    group = n_q // n_kv
+    out = np.zeros((B, n_q, d))
+    mix_abs = np.zeros((B, n_q, d))
+    for b in range(B):
+        pos = attended_positions(int(seq_len[b]), window)
+        rows = int(seq_base[b]) + pos % ring
+        for h in range(n_q):
+            g = h // group
+            k = kc[rows, g]                           # [n][d]
+            v = vc[rows, g]
+            s = scale * (k @ q[b, h])                 # [n]
+            m = max(np.max(s), float(sinks[h]))
+            e = np.exp(s - m)
+            z = np.sum(e) + np.exp(float(sinks[h]) - m)
+            w = e / z
+            out[b, h] = w @ v
+            mix_abs[b, h] = w @ np.abs(v)
+    return (out, mix_abs) if with_abs else out

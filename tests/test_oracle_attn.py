@@ -129,3 +129,156 @@ def test_fused_row_layout_q_then_k_then_v():
     np.testing.assert_array_equal(q, np.ones((1, n_q, d)))              # a constant head normalises to 1
     np.testing.assert_array_equal(kc, np.full((1, n_kv, d), 2.0))     # then times gamma_k
     np.testing.assert_array_equal(vc, np.full((1, n_kv, d), 0.5))
+
+
+# ---------------------------------------------------------------- decode attention
+
+def _attn_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "decode_attention_small.txt")
+    cases, cur = [], None
+    for ln in open(path):
+        ln = ln.strip()
+        if not ln or ln.startswith("#"):
+            continue
+        key, *vals = ln.split()
+        if key == "case":
+            cur = {"name": vals[0], "rows": []}
+            cases.append(cur)
+        elif key == "row":
+            cur["rows"].append((int(vals[0]), vals[1], vals[2]))
+        else:
+            cur[key] = vals
+    return cases
+
+
+def _num(v):
+    return float.fromhex(v) if "x" in v else float(v)
+
+
+def _vecs(vals):
+    return np.array([[_num(x) for x in v.split(",")] for v in vals])
+
+
+def test_decode_attention_golden():
+    cases = _attn_golden()
+    assert [c["name"] for c in cases] == ["full", "window", "gqa"]
+    for c in cases:
+        n_q, n_kv = int(c["n_q"][0]), int(c["n_kv"][0])
+        q = _vecs(c["q"])[None]                              # [1][n_q][d]
+        d = q.shape[-1]
+        n_rows = max(r for r, _, _ in c["rows"]) + 1
+        kc = np.full((n_rows + 2, n_kv, d), 100.0)           # unlisted rows must not matter
+        vc = np.full((n_rows + 2, n_kv, d), -100.0)
+        for r, k, v in c["rows"]:
+            kc[r] = _vecs(k.split(";"))
+            vc[r] = _vecs(v.split(";"))
+        out = attn.decode_attention(q, kc, vc, [int(c["base"][0])], [int(c["len"][0])], int(c["ring"][0]),
+                                    int(c["window"][0]), [_num(s) for s in c["sinks"]], _num(c["scale"][0]))
+        np.testing.assert_allclose(out[0], _vecs(c["out"]), rtol=1e-14, atol=1e-14, err_msg=c["name"])
+
+
+def _random_cache(rng, n_rows, n_kv, d):
+    return rng.standard_normal((n_rows, n_kv, d)), rng.standard_normal((n_rows, n_kv, d))
+
+
+def test_decode_attention_without_sinks_is_textbook_attention():
+    """Sinks at -inf: plain scaled dot-product attention over the attended
+    rows, computed by torch's SDPA in float64 with the KV heads repeated
+    for their query heads."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(11)
+    n_q, n_kv, d, B = 8, 2, 16, 3
+    kc, vc = _random_cache(rng, 200, n_kv, d)
+    q = rng.standard_normal((B, n_q, d))
+    base, lens, ring = [0, 60, 130], [7, 45, 60], 64
+    scale = 1 / np.sqrt(d)
+    out = attn.decode_attention(q, kc, vc, base, lens, ring, 0, np.full(n_q, -np.inf), scale)
+    for b in range(B):
+        rows = base[b] + np.arange(lens[b]) % ring
+        k = torch.from_numpy(kc[rows]).permute(1, 0, 2).repeat_interleave(n_q // n_kv, 0)[None]
+        v = torch.from_numpy(vc[rows]).permute(1, 0, 2).repeat_interleave(n_q // n_kv, 0)[None]
+        want = F.scaled_dot_product_attention(torch.from_numpy(q[b])[None, :, None], k, v, scale=scale)
+        np.testing.assert_allclose(out[b], want[0, :, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_attention_sink_is_a_key_with_zero_value():
+    """A sink acts as one more key whose score is the sink logit and whose
+    value is zero: SDPA over the rows plus a zero key, with the sink added
+    to that key's score by an additive mask."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(12)
+    n_q, n_kv, d = 4, 4, 8
+    kc, vc = _random_cache(rng, 32, n_kv, d)
+    q = rng.standard_normal((1, n_q, d))
+    sinks = rng.standard_normal(n_q) * 2
+    scale = 0.3
+    L, W = 20, 9
+    out = attn.decode_attention(q, kc, vc, [5], [L], 27, W, sinks, scale)
+    rows = 5 + np.arange(L - W, L) % 27
+    k = np.concatenate([kc[rows], np.zeros((1, n_kv, d))]).transpose(1, 0, 2)
+    v = np.concatenate([vc[rows], np.zeros((1, n_kv, d))]).transpose(1, 0, 2)
+    mask = np.zeros((n_q, 1, W + 1))
+    mask[:, 0, W] = sinks
+    want = F.scaled_dot_product_attention(torch.from_numpy(q[0])[:, None], torch.from_numpy(k),
+                                          torch.from_numpy(v), attn_mask=torch.from_numpy(mask), scale=scale)
+    np.testing.assert_allclose(out[0], want[:, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_attention_window_and_ring():
+    """Only the window's rows matter (every other row can change freely),
+    and a ring of C >= W rows gives the result of a contiguous layout."""
+    rng = np.random.default_rng(13)
+    n_q, n_kv, d, L, W = 4, 2, 8, 50, 13
+    kc, vc = _random_cache(rng, L, n_kv, d)
+    q = rng.standard_normal((1, n_q, d))
+    sinks = rng.standard_normal(n_q)
+    ref = attn.decode_attention(q, kc, vc, [0], [L], L, W, sinks, 0.5)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[: L - W] = rng.standard_normal(kc2[: L - W].shape) * 50
+    vc2[: L - W] = 1e6
+    np.testing.assert_array_equal(attn.decode_attention(q, kc2, vc2, [0], [L], L, W, sinks, 0.5), ref)
+    for C in (W, W + 3, 64):
+        kr = np.zeros((7 + C, n_kv, d))
+        vr = np.zeros((7 + C, n_kv, d))
+        for p in range(L - W, L):
+            kr[7 + p % C], vr[7 + p % C] = kc[p], vc[p]
+        np.testing.assert_allclose(attn.decode_attention(q, kr, vr, [7], [L], C, W, sinks, 0.5), ref,
+                                   rtol=1e-14, atol=1e-15)
+    # a window at least as long as the context is the full context
+    np.testing.assert_array_equal(attn.decode_attention(q, kc, vc, [0], [L], L, L + 5, sinks, 0.5),
+                                  attn.decode_attention(q, kc, vc, [0], [L], L, 0, sinks, 0.5))
+
+
+def test_decode_attention_gqa_head_mapping():
+    """Query head h reads KV head h // (n_q / n_kv): with a constant value
+    row per KV head and no sink, head h returns KV head h // group's
+    constant exactly."""
+    rng = np.random.default_rng(14)
+    n_q, n_kv, d = 12, 3, 8
+    kc = rng.standard_normal((10, n_kv, d))
+    vc = np.zeros((10, n_kv, d))
+    for g in range(n_kv):
+        vc[:, g, :] = float(g + 1)
+    q = rng.standard_normal((2, n_q, d))
+    out = attn.decode_attention(q, kc, vc, [0, 4], [4, 6], 6, 0, np.full(n_q, -np.inf), 1.0)
+    for h in range(n_q):
+        np.testing.assert_allclose(out[:, h], float(h // 4 + 1), rtol=1e-15)
+
+
+def test_decode_attention_uniform_scores_closed_form():
+    """Equal keys give equal scores s: out = mean(v) * L / (L + exp(sink - s));
+    the |v| mixture equals the mixture itself for non-negative values."""
+    rng = np.random.default_rng(15)
+    n_q, n_kv, d, L = 2, 1, 8, 9
+    kc = np.tile(rng.standard_normal(d), (L, n_kv, 1))
+    vc = np.abs(rng.standard_normal((L, n_kv, d)))
+    q = rng.standard_normal((1, n_q, d))
+    sinks = np.array([0.7, -2.0])
+    out, mix = attn.decode_attention(q, kc, vc, [0], [L], L, 0, sinks, 0.25, with_abs=True)
+    for h in range(n_q):
+        s = 0.25 * kc[0, 0] @ q[0, h]
+        want = vc[:, 0].mean(axis=0) * L / (L + np.exp(sinks[h] - s))
+        np.testing.assert_allclose(out[0, h], want, rtol=1e-13)
+    np.testing.assert_array_equal(mix, out)
