@@ -31,6 +31,9 @@ Reported (one JSON line):
                flint_dense_gemv at batch 1 and 8: TB/s against 8 TB/s
   qk_norm_rope_kv  the fused per-head Q/K RMSNorm + RoPE + KV-cache write
                (flint_qk_norm_rope_kv) for 8 and 8,192 tokens
+  decode_attention  decode attention with learned sinks
+               (flint_decode_attention): a 100K-context full layer at batch
+               1 and a 513-token window layer at batch 1 and 8
 The timed calls are replays of a HIP graph of back-to-back layer calls (host
 launch cost is not on the clock), on activations and layer copies that the
 warm-up calls did not use; the decode error word is checked after them.
@@ -42,6 +45,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -325,6 +329,59 @@ def bench_attn_prep(dev, seed, reps=50):
         print(f"[bench] q/k norm + rope + kv write, {T} tokens: {secs * 1e6:.2f} us, "
               f"{nb / secs / 1e12:.3f} TB/s", file=sys.stderr, flush=True)
         del gr, sets
+    return out
+
+
+def bench_attn_decode(dev, seed):
+    """Decode attention with learned sinks (flint_decode_attention) at the
+    Flint attention shape (GQA 32/4, d 128), one query per sequence:
+    a full-context (NoPE) layer at 100K context, batch 1 (the pages' decode
+    measurement context), and a 513-token window layer at batch 1 and 8.
+    Each case rotates independently drawn KV caches whose total passes the
+    256 MB cache.  Bytes: the attended K and V rows, q and the output."""
+    n_q, n_kv, d = 32, 4, 128
+    shape = fm.FlintAttnShape(n_q, n_kv, d, 0, 0.0)
+    scale = 1.0 / math.sqrt(d)
+    out = {"shape": "32 q / 4 kv heads, d 128, learned sinks"}
+    for name, batch, L, window, n_copies in (("full_100k_b1", 1, 100000, 0, 3),
+                                             ("window513_b1", 1, 100000, 513, 320),
+                                             ("window513_b8", 8, 100000, 513, 40)):
+        ring = window if window else L
+        cases = [gen.decode_attn_case(gen.seed_for(seed, "attn-dec", name, c), n_q, n_kv, [L] * batch, ring, dev,
+                                      gap=0) for c in range(n_copies)]
+        wsb = fm.flint_decode_attention_workspace_bytes(shape, window, batch, L)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        o = torch.empty((batch, n_q, d), dtype=torch.bfloat16, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        reps = max(30, n_copies)
+
+        def body(n):
+            for i in range(n):
+                c = cases[i % n_copies]
+                fm.flint_decode_attention(shape, window, ring, scale, c.q, batch, c.k_cache, c.v_cache, c.n_rows,
+                                          c.seq_base, c.seq_len, L, c.sinks, o, ws if wsb else None, wsb, err)
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            body(n_copies)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            body(reps)
+        gr.replay()
+        secs = timed(gr) / reps
+        if int(err.item()) != 0:
+            raise RuntimeError(f"decode attention {name}: error word set")
+        span = min(L, window) if window else L
+        nb = batch * (span * n_kv * d * 2 * 2 + 2 * n_q * d * 2)
+        out[name] = {"us": round(secs * 1e6, 2), "tb_s": round(nb / secs / 1e12, 3),
+                     "frac_hbm_peak": round(nb / secs / 1e9 / HBM_PEAK_GBS, 4), "bytes": nb,
+                     "batch": batch, "context": L, "window": window}
+        print(f"[bench] decode attention {name}: {secs * 1e6:.2f} us, {nb / secs / 1e12:.3f} TB/s",
+              file=sys.stderr, flush=True)
+        del gr, cases
+        torch.cuda.empty_cache()
     return out
 
 
@@ -665,6 +722,7 @@ def main():
         line["prefill"] = bench_prefill(layers[0], shape, args.seed)
     if not args.no_attn:
         line["qk_norm_rope_kv"] = bench_attn_prep(dev, args.seed)
+        line["decode_attention"] = bench_attn_decode(dev, args.seed)
     if not args.no_lm_head:
         line["lm_head"] = bench_lm_head(dev, args.seed)
     if not args.no_step:

@@ -229,6 +229,38 @@ def attn_rows(seed: int, n_tokens: int, shape: AttnShape, device="cpu") -> torch
     return (z * sc).reshape(n_tokens, -1).to(torch.bfloat16)
 
 
+@dataclasses.dataclass
+class DecodeAttnCase:
+    q: torch.Tensor          # [B][n_q][d] BF16
+    k_cache: torch.Tensor    # [n_rows][n_kv][d] BF16
+    v_cache: torch.Tensor
+    seq_base: torch.Tensor   # [B] int32
+    seq_len: torch.Tensor    # [B] int32
+    sinks: torch.Tensor      # [n_q] float32
+    ring: int
+    n_rows: int
+
+
+def decode_attn_case(seed: int, n_q: int, n_kv: int, lens, ring: int, device="cpu", d: int = 128,
+                     gap: int = 3) -> DecodeAttnCase:
+    """One decode query per sequence over a BF16 KV cache: sequence b owns
+    rows b (ring + gap) .. + ring - 1 (gap rows between sequences that no
+    sequence reads); every row of the cache, read or not, holds draws.
+    Queries ~ N(0, 2^2) (after their norm and RoPE the heads are O(1) with
+    gamma near 1; the factor makes the softmax peaky), K and V ~ N(0, 1),
+    sinks ~ N(0, 2^2)."""
+    g = _gen(seed, device)
+    B = len(lens)
+    n_rows = B * (ring + gap)
+    q = (2.0 * torch.randn((B, n_q, d), generator=g, device=device)).to(torch.bfloat16)
+    k = torch.randn((n_rows, n_kv, d), generator=g, device=device).to(torch.bfloat16)
+    v = torch.randn((n_rows, n_kv, d), generator=g, device=device).to(torch.bfloat16)
+    sinks = 2.0 * torch.randn((n_q,), generator=g, device=device)
+    base = torch.arange(B, dtype=torch.int32, device=device) * (ring + gap)
+    lens_t = torch.tensor(list(lens), dtype=torch.int32, device=device)
+    return DecodeAttnCase(q, k, v, base, lens_t, sinks.to(torch.float32), ring, n_rows)
+
+
 def numpy_u8(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").numpy()
 

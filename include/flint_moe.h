@@ -429,6 +429,50 @@ FLINT_API int32_t flint_qk_norm_rope_kv(const flint_attn_shape* shape, const voi
                                         const void* gamma_q, const void* gamma_k, void* q_out, int32_t* error,
                                         void* stream);
 
+/* Decode attention with learned sinks ("Day-0 Support for Flint on vLLM",
+ * "Model architecture", first two bullets: 35 layers attend to a 513-token
+ * sliding window (the current token and the 512 before it), 14 to the whole
+ * context; GQA with 32 query and 4 KV heads of dimension 128; learned
+ * attention sinks.  "Optimizations", fifth bullet: a decode attention kernel
+ * with sinks and sliding windows).  One query token per sequence b:
+ *   out[b][h] = sum_p w_p V[row(p)][g],  w_p = exp(s_p) / (sum_p' exp(s_p') +
+ *   exp(sinks[h])),  s_p = scale * (q[b][h] . K[row(p)][g]),  g = h / (n_q / n_kv)
+ * over the positions p = max(0, L - window) .. L - 1 (0 .. L - 1 when window
+ * is 0), L = seq_len[b], row(p) = seq_base[b] + (p mod ring).
+ *   shape      n_q_heads, n_kv_heads (n_q / n_kv in 1..16), head_dim 128,
+ *              flags 0; rms_eps unused
+ *   window     0 (whole context) or the window length (513 on Flint)
+ *   ring       cache rows per sequence: at least the attended span (a ring
+ *              of `window` rows for a window layer, the context for a
+ *              full layer); else the sequence is an error
+ *   scale      the score scale (1/sqrt(128)), finite and > 0
+ *   q          (device) BF16 [batch][n_q][128], after the Q norm and RoPE
+ *   k_cache, v_cache (device) BF16 [n_rows][n_kv][128] (the layout
+ *              flint_qk_norm_rope_kv writes); n_rows * n_kv * 128 < 2^32
+ *   seq_base, seq_len (device) int32 [batch]: first row and context length
+ *              (newest token included, its K/V already in the cache) of each
+ *              sequence; a length outside 1..max_len, base < 0, or base + ring
+ *              > n_rows is an error
+ *   max_len    (host) the largest seq_len of the call: sizes the split of the
+ *              context over workgroups
+ *   sinks      (device) float32 [n_q], one logit per query head (-inf: none)
+ *   out        (device) BF16 [batch][n_q][128]
+ *   workspace  (device) flint_decode_attention_workspace_bytes(...) bytes (0
+ *              when the split has one chunk: NULL allowed); caller-owned,
+ *              needs no initialisation
+ *   error      (device) int32 [1] or NULL: set to 1 for an invalid sequence,
+ *              whose output is all zeros
+ * Scores and the softmax are float32 (base-2 exponentials of pre-scaled
+ * scores); the weights enter the V product as BF16; output rounded to BF16
+ * once.  Returns FLINT_OK or a FLINT_ERR_* code (host-side checks only). */
+FLINT_API int64_t flint_decode_attention_workspace_bytes(const flint_attn_shape* shape, int32_t window,
+                                                         int32_t batch, int32_t max_len);
+FLINT_API int32_t flint_decode_attention(const flint_attn_shape* shape, int32_t window, int32_t ring,
+                                         float scale, const void* q, int32_t batch, const void* k_cache,
+                                         const void* v_cache, int32_t n_rows, const int32_t* seq_base,
+                                         const int32_t* seq_len, int32_t max_len, const float* sinks, void* out,
+                                         void* workspace, int64_t workspace_bytes, int32_t* error, void* stream);
+
 /* Measurement utility (not part of the layer computation): a plain read of
  * `bytes` of device memory at `src`, for the achievable HBM read rate of a
  * transfer of that size, against which the decode kernels' rates are

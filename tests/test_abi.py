@@ -264,3 +264,41 @@ def test_qk_norm_rope_kv_validation_codes():
     assert f(*args(ok, err=v(34))) == fm.FLINT_ERR_ALIGNMENT
     # without RoPE the table and positions are not needed (and not checked)
     assert f(*args(nope, qkv=None, pos=None, cs=None, P=0)) == fm.FLINT_ERR_INVALID_ARG
+
+
+def test_decode_attention_validation_codes():
+    """Decode attention checks its arguments before enqueuing anything, and
+    sizes its workspace from the shape, window, batch and longest context."""
+    L = fm.lib()
+    v = ctypes.c_void_p
+    f = L.flint_decode_attention
+    ok = fm.FlintAttnShape(32, 4, 128, 0, 0.0)
+    args = lambda sh, **kw: [ctypes.byref(sh), kw.get("W", 0), kw.get("ring", 1000), kw.get("scale", 0.088),
+                             kw.get("q", v(16)), kw.get("B", 1), kw.get("kc", v(32)), kw.get("vc", v(48)),
+                             kw.get("rows", 1000), kw.get("base", v(64)), kw.get("len", v(80)),
+                             kw.get("max_len", kw.get("ML", 1000)), kw.get("sinks", v(96)), kw.get("out", v(112)),
+                             kw.get("ws", v(128)), kw.get("wsb", 1 << 30), kw.get("err", None), None]
+    assert f(*args(ok, q=None)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, sinks=None)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, B=0)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, ML=0)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, W=-1)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, ring=0)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, scale=0.0)) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, scale=float("inf"))) == fm.FLINT_ERR_INVALID_ARG
+    assert f(*args(ok, scale=float("nan"))) == fm.FLINT_ERR_INVALID_ARG
+    for bad in (fm.FlintAttnShape(32, 4, 64, 0, 0.0), fm.FlintAttnShape(30, 4, 128, 0, 0.0),
+                fm.FlintAttnShape(32, 1, 128, 0, 0.0), fm.FlintAttnShape(32, 4, 128, fm.FLINT_ATTN_ROPE, 0.0)):
+        assert f(*args(bad)) == fm.FLINT_ERR_UNSUPPORTED               # group > 16, rope flag, head dim
+    assert f(*args(ok, rows=1 << 24)) == fm.FLINT_ERR_UNSUPPORTED       # 32-bit element offsets
+    assert f(*args(ok, q=v(18))) == fm.FLINT_ERR_ALIGNMENT
+    assert f(*args(ok, base=v(66))) == fm.FLINT_ERR_ALIGNMENT
+    assert f(*args(ok, err=v(34))) == fm.FLINT_ERR_ALIGNMENT
+    wsb = fm.flint_decode_attention_workspace_bytes(ok, 0, 1, 100000)
+    assert wsb > 0 and wsb % 16 == 0
+    assert f(*args(ok, ML=100000, ring=100000, rows=100000, wsb=wsb - 16)) == fm.FLINT_ERR_WORKSPACE
+    assert f(*args(ok, ML=100000, ring=100000, rows=100000, ws=None)) == fm.FLINT_ERR_WORKSPACE
+    # one chunk per sequence needs no workspace
+    assert fm.flint_decode_attention_workspace_bytes(ok, 513, 1, 100) == 0
+    assert fm.flint_decode_attention_workspace_bytes(ok, 513, 8, 100000) > 0
+    assert L.flint_decode_attention_workspace_bytes(ctypes.byref(fm.FlintAttnShape(32, 4, 64, 0, 0.0)), 0, 1, 10) < 0

@@ -58,7 +58,8 @@ EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_workspace_error", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
     "flint_moe_decode", "flint_moe_decode_noalloc", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
-    "flint_moe_prefill", "flint_dense_gemv", "flint_qk_norm_rope_kv", "flint_stream_read",
+    "flint_moe_prefill", "flint_dense_gemv", "flint_qk_norm_rope_kv", "flint_decode_attention",
+    "flint_decode_attention_workspace_bytes", "flint_stream_read",
 )
 
 
@@ -133,6 +134,11 @@ def lib() -> ctypes.CDLL:
         L.flint_qk_norm_rope_kv.restype = i32
         L.flint_qk_norm_rope_kv.argtypes = [ctypes.POINTER(FlintAttnShape), vp, i32, vp, vp, i32, vp, vp, vp,
                                             i32, vp, vp, vp, vp, vp]
+        L.flint_decode_attention_workspace_bytes.restype = i64
+        L.flint_decode_attention_workspace_bytes.argtypes = [ctypes.POINTER(FlintAttnShape), i32, i32, i32]
+        L.flint_decode_attention.restype = i32
+        L.flint_decode_attention.argtypes = [ctypes.POINTER(FlintAttnShape), i32, i32, ctypes.c_float, vp, i32,
+                                             vp, vp, i32, vp, vp, i32, vp, vp, vp, i64, vp, vp]
         L.flint_stream_read.restype = i32
         L.flint_stream_read.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         _lib = L
@@ -262,6 +268,23 @@ def flint_dense_gemv(codes, scales, gscale, w_bf16, rows, cols, flags, x, batch,
     _check("flint_dense_gemv", lib().flint_dense_gemv(
         _p(codes), _p(scales), _p(gscale), _p(w_bf16), rows, cols, flags, _p(x), batch, _p(y),
         epilogue, _p(aux), _p(gamma), ctypes.c_float(rms_eps), _stream(stream)))
+
+
+def flint_decode_attention_workspace_bytes(shape: FlintAttnShape, window: int, batch: int, max_len: int) -> int:
+    n = lib().flint_decode_attention_workspace_bytes(ctypes.byref(shape), window, batch, max_len)
+    if n < 0:
+        raise FlintError("flint_decode_attention_workspace_bytes", FLINT_ERR_UNSUPPORTED)
+    return n
+
+
+def flint_decode_attention(shape: FlintAttnShape, window, ring, scale, q, batch, k_cache, v_cache, n_rows,
+                           seq_base, seq_len, max_len, sinks, out, workspace=None, workspace_bytes=0,
+                           error=None, stream=None):
+    """Decode attention with learned sinks over a window or the whole
+    context (see include/flint_moe.h)."""
+    _check("flint_decode_attention", lib().flint_decode_attention(
+        ctypes.byref(shape), window, ring, scale, _p(q), batch, _p(k_cache), _p(v_cache), n_rows, _p(seq_base),
+        _p(seq_len), max_len, _p(sinks), _p(out), _p(workspace), workspace_bytes, _p(error), _stream(stream)))
 
 
 def flint_qk_norm_rope_kv(shape: FlintAttnShape, qkv, n_tokens, positions, cos_sin, n_positions, slots,

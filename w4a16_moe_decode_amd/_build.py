@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libflint_moe.so")
-SOURCES = ["repack.hip", "decode.hip", "prefill.hip", "fused.hip", "flint_b1.hip", "flint_b8.hip", "noalloc.hip", "stream.hip", "attn_prep.hip", "api.cpp"]
+SOURCES = ["repack.hip", "decode.hip", "prefill.hip", "fused.hip", "flint_b1.hip", "flint_b8.hip", "noalloc.hip", "stream.hip", "attn_prep.hip", "attn_decode.hip", "api.cpp"]
 ARCH = "gfx950"
 NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
