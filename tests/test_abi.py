@@ -299,6 +299,6 @@ def test_decode_attention_validation_codes():
     assert f(*args(ok, ML=100000, ring=100000, rows=100000, wsb=wsb - 16)) == fm.FLINT_ERR_WORKSPACE
     assert f(*args(ok, ML=100000, ring=100000, rows=100000, ws=None)) == fm.FLINT_ERR_WORKSPACE
     # one chunk per sequence needs no workspace
-    assert fm.flint_decode_attention_workspace_bytes(ok, 513, 1, 100) == 0
+    assert fm.flint_decode_attention_workspace_bytes(ok, 513, 1, 32) == 0
     assert fm.flint_decode_attention_workspace_bytes(ok, 513, 8, 100000) > 0
     assert L.flint_decode_attention_workspace_bytes(ctypes.byref(fm.FlintAttnShape(32, 4, 64, 0, 0.0)), 0, 1, 10) < 0
