@@ -19,7 +19,11 @@ from typing import Optional
 
 import torch
 
-from ._build import LIB_PATH
+from ._build import LIB_PATH as _DEFAULT_LIB
+
+# FLINT_MOE_LIB names another build of the library to load (the host-sanitizer
+# build for CPU-only checks of the C ABI); unset, the in-tree library.
+LIB_PATH = os.environ.get("FLINT_MOE_LIB") or _DEFAULT_LIB
 
 # ---------------------------------------------------------------- constants --
 FLINT_OK = 0
