@@ -37,8 +37,6 @@ Reported (one JSON line):
 The timed calls are replays of a HIP graph of back-to-back layer calls (host
 launch cost is not on the clock), on activations and layer copies that the
 warm-up calls did not use; the decode error word is checked after them.
-The timed loops replay HIP graphs of the layer calls, so host launch cost is
-not on the clock.
 """
 from __future__ import annotations
 
