@@ -148,17 +148,21 @@ __device__ __forceinline__ void gu4_h2(const GU4& v, const uint4* xa, const uint
   hb = round_bf16(silu_f32(round_bf16(group_sum<16>(bg) * gsg))) * round_bf16(group_sum<16>(bu) * gsu);
 }
 
-// Publishes h of a unit's four rows (lanes 0, 16, 32, 48) for token t as
-// two tagged words.
-__device__ __forceinline__ void put_unit_h(uint64_t* hb_words, int r, int t, int u, float h, uint32_t epoch) {
+// h of a unit's four rows (lanes 0, 16, 32, 48) for token t as two tagged
+// words, kept in this wave's LDS queue (word index << 32 | payload) and
+// published after the wave's last unit: a device-scope store issued between
+// two units' loads holds back the later loads until it is acknowledged
+// (loads and stores complete in order), which cost 0.8 us per layer.
+__device__ __forceinline__ void stash_unit_h(uint64_t* q, int& n, int r, int t, int u, float h) {
   const int lane = threadIdx.x & 63;
   const float h0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), 0));
   const float h1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), 16));
   const float h2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), 32));
   const float h3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), 48));
   if (lane < 2)
-    put_word(hb_words + ((size_t)r * FLINT_MAX_DECODE_BATCH + t) * FL_IW + 2 * (u % (FL_I / 4)) + lane, epoch,
-             lane ? pack_bf16x2(h2, h3) : pack_bf16x2(h0, h1));
+    q[n + lane] = ((uint64_t)(((uint32_t)r * FLINT_MAX_DECODE_BATCH + t) * FL_IW + 2 * (u % (FL_I / 4)) + lane) << 32) |
+                  (lane ? pack_bf16x2(h2, h3) : pack_bf16x2(h0, h1));
+  n += 2;
 }
 
 // A lane's chunk li of down rows row0 + 2 grp and row0 + 2 grp + 1 (so that
@@ -206,6 +210,7 @@ __global__ __launch_bounds__(512) void flint_b8_kernel(LayerArgs a_arg, DecodeWs
   __shared__ uint64_t s_pair[F8_MAXPAIR];
   __shared__ __align__(16) uint32_t s_h[F8_MAXPAIR][FL_IW];
   __shared__ float s_pp[F8_BT * F8_PK][FL_ROWS];
+  __shared__ uint64_t s_hq[FL_NW][2 * F8_BT * ((F8_BT * FLINT_MAX_TOP_K / 2 + 1 + FL_NW - 1) / FL_NW)];   // h words per wave
 
   const LayerArgs a = pin_layer_args(a_arg);
   const DecodeWs ws = pin_decode_ws(ws_arg);
@@ -405,6 +410,7 @@ __global__ __launch_bounds__(512) void flint_b8_kernel(LayerArgs a_arg, DecodeWs
                       FL_ROWS * (j & (F8_TILES - 1)), lane);
     }
   };
+  int n_hq = 0;                                    // words in this wave's h queue
   unit_load(0);
   if (U > 1) unit_load(1);
 #pragma unroll
@@ -421,12 +427,12 @@ __global__ __launch_bounds__(512) void flint_b8_kernel(LayerArgs a_arg, DecodeWs
         const int ta = (tokp >> (4 * q)) & 15, tb = (tokp >> (4 * q + 4)) & 15;
         float ha, hb;
         gu4_h2(gu[j & 1], s_x + ta * F8_Q, s_x + tb * F8_Q, gsg, gsu, li, ha, hb);
-        put_unit_h(ws.hb_words, r, ta, u, ha, epoch);
-        put_unit_h(ws.hb_words, r, tb, u, hb, epoch);
+        stash_unit_h(s_hq[wave], n_hq, r, ta, u, ha);
+        stash_unit_h(s_hq[wave], n_hq, r, tb, u, hb);
       }
       if (q < n) {
         const int t = (tokp >> (4 * q)) & 15;
-        put_unit_h(ws.hb_words, r, t, u, gu4_h(gu[j & 1], s_x + t * F8_Q, gsg, gsu, li), epoch);
+        stash_unit_h(s_hq[wave], n_hq, r, t, u, gu4_h(gu[j & 1], s_x + t * F8_Q, gsg, gsu, li));
       }
     }
     if (j + 2 < U) {
@@ -439,6 +445,11 @@ __global__ __launch_bounds__(512) void flint_b8_kernel(LayerArgs a_arg, DecodeWs
 #pragma unroll
       for (int m = D1; m < DI; ++m) item_load(m);
     }
+  }
+
+  for (int k = lane; k < n_hq; k += 64) {          // the queued h words
+    const uint64_t e = s_hq[wave][k];
+    put_word(ws.hb_words + (e >> 32), epoch, (uint32_t)e);
   }
 
   // ---- phase 5: the shared expert's h, its down partial sums ------------------
