@@ -100,6 +100,12 @@ __device__ __forceinline__ uint4 rms_norm_8(uint4 x, uint4 g, const Rms& r) {
 
 // SiLU(z) = z / (1 + e^-z) in fp32 (expf: the HIP device function).
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// SiLU from the hardware base-2 exponential and reciprocal (each within about
+// 1 ulp): within a few fp32 ulps of silu_f32, for epilogues that round the
+// result to BF16 right after.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 
 // ------------------------------------------------------------ NVFP4 ------
 

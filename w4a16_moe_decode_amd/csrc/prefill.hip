@@ -659,6 +659,296 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(LayerArgs a, PrefillW
       }
 }
 
+// ------------------------------------ Flint-shape NVFP4 grouped GEMMs --
+// Hidden 2048, intermediate 512 (routed and shared), NVFP4 weights.  Tile:
+// 128 rows (tokens of one group) x 256 output columns, 4 waves; wave w owns
+// columns 64 w .. 64 w + 63 of all 128 rows as 4 x 2 blocks of MFMA
+// 32x32x16.  K steps of 128:
+//   A  the gathered BF16 rows go straight into LDS (global_load_lds: no
+//      registers), double-buffered; 16-byte chunk c of tile row r sits at
+//      slot c ^ (r & 15), so the operand reads of 16 consecutive rows hit
+//      16 different bank groups.  Each lane copies the same 8 (row, chunk)
+//      pairs every step: its 32-bit offsets are fixed and only the
+//      workgroup-uniform base advances.
+//   B  the NVFP4 weights never pass through LDS.  Within a step, MFMA j's
+//      k index 8 h + e (lane half h) stands for column 64 h + 8 j + e (the
+//      same order for A and B), so lane (h, n) needs 64 consecutive codes
+//      (32 bytes) and their 4 scale bytes of weight row n per step: loaded
+//      two steps ahead into a ring of three, decoded to exact BF16 (E2M1 x
+//      UE4M3 has at most 6 significant bits) just before each MFMA.
+// Each B value is decoded once per 128 rows: 2 VALU per value against 16
+// MFMA rows, and LDS carries only A.
+constexpr int FBM = 128, FBN = 256, FBK = 128;
+constexpr int FH = 2048, FI = 512;
+
+struct FBRaw {
+  uint4 c[2][2];     // [N block][first, second 16 bytes of the lane's 32]
+  uint32_t s[2];     // [N block] 4 scale bytes
+};
+
+template <int NK>
+struct FbRows {      // this lane's weight rows (codes, scales) of its two N blocks
+  const uint8_t* c[2];
+  const uint8_t* s[2];
+};
+
+template <int NK>
+__device__ __forceinline__ void fb_load(FBRaw& r, const FbRows<NK>& b, int t, int h) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    r.c[nb][0] = ldg<uint4>(b.c[nb] + 64 * t + 32 * h);
+    r.c[nb][1] = ldg<uint4>(b.c[nb] + 64 * t + 32 * h + 16);
+    r.s[nb] = ldg<uint32_t>(b.s[nb] + 8 * t + 4 * h);
+  }
+}
+
+// the 8 codes of word j (columns 64 h + 8 j .. + 7) times their UE4M3 scale
+template <int J>
+__device__ __forceinline__ bf16x8_t fb_decode(const FBRaw& r, int nb) {
+  const uint4 q = r.c[nb][J / 4];
+  const uint32_t w = (J % 4) == 0 ? q.x : (J % 4) == 1 ? q.y : (J % 4) == 2 ? q.z : q.w;
+  const float sc = e4m3_to_f32<J / 2>(r.s[nb]);
+  const f32x2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2_rne(f0.x * sc, f0.y * sc),
+                                                 pack_bf16x2_rne(f1.x * sc, f1.y * sc),
+                                                 pack_bf16x2_rne(f2.x * sc, f2.y * sc),
+                                                 pack_bf16x2_rne(f3.x * sc, f3.y * sc)));
+}
+
+struct FAcc { f32x16 c[4][2]; };   // [M block][N block]
+
+// One K step on A stage `la` (128 rows x 256 bytes, swizzled) and B ring entry r.
+__device__ __forceinline__ void fb_step(FAcc& acc, const uint8_t* la, const FBRaw& r, int lane) {
+  const int h = lane >> 5, m = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bf16x8_t av[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int row = 32 * mb + m;
+      av[mb] = *reinterpret_cast<const bf16x8_t*>(la + row * 256 + 16 * ((8 * h + j) ^ (m & 15)));
+    }
+    bf16x8_t bv[2];
+#define FB_DEC(JJ) { bv[0] = fb_decode<JJ>(r, 0); bv[1] = fb_decode<JJ>(r, 1); }
+    switch (j) {
+      case 0: FB_DEC(0) break; case 1: FB_DEC(1) break; case 2: FB_DEC(2) break; case 3: FB_DEC(3) break;
+      case 4: FB_DEC(4) break; case 5: FB_DEC(5) break; case 6: FB_DEC(6) break; default: FB_DEC(7) break;
+    }
+#undef FB_DEC
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc.c[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc.c[mb][nb], 0, 0, 0);
+  }
+}
+
+// The K loop: NK steps, A stages double-buffered in s_a, B ring of three.
+// a_src: workgroup-uniform base of step 0's A elements; a_off[i]: this
+// lane's element offset of its i-th copy; each step advances by FBK.
+template <int NK>
+__device__ __forceinline__ void fb_gemm(FAcc& acc, uint8_t (&s_a)[2][FBM * 256], const uint16_t* a_src,
+                                        const uint32_t (&a_off)[8], const FbRows<NK>& brows) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
+  // byte offsets on a workgroup-uniform base: the copies take the scalar
+  // base + 32-bit offset form, so no address register of a copy in flight is
+  // ever rewritten (the compiler would wait for the copy first)
+  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(a_src);
+  auto copy_a = [&](int t, int buf) {
+    // the step's base as an opaque scalar pair: folded into the per-lane
+    // offsets it would make 64-bit addresses again
+    uint64_t sb = reinterpret_cast<uint64_t>(a_base + (size_t)t * FBK * 2);
+    asm volatile("" : "+s"(sb));
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(sb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(src + (uint64_t)a_off[i], &s_a[buf][(8 * wave + i) * 1024], 16, 0, 0);
+  };
+  // Per step t: wait for everything in flight (the copies and B rows of step
+  // t, issued one step earlier), barrier, issue copies(t + 1) and B rows(t + 1),
+  // then multiply.  Waiting for everything leaves the compiler no wait of its
+  // own to add: with a copy into LDS in flight it could only wait for all
+  // loads (it cannot tell the copies' memory counts from the loads').  One
+  // step of latency is covered by the other workgroup on the CU.
+  FBRaw ring[2];
+  fb_load(ring[0], brows, 0, h);
+  copy_a(0, 0);
+#pragma unroll
+  for (int t = 0; t < NK; ++t) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // a bare barrier: a workgroup fence would add nothing here
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < NK) {
+      copy_a(t + 1, (t + 1) & 1);
+      fb_load(ring[(t + 1) & 1], brows, t + 1, h);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fb_step(acc, s_a[t & 1], ring[t & 1], lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// the lane's 8 A copies (byte offsets): copy i of wave w fills tile row
+// 32 w + 4 i + lane / 16, slot lane % 16 <- chunk (lane % 16) ^ (row & 15);
+// row_off(r) is the element offset of tile row r's source row
+template <typename RowOff>
+__device__ __forceinline__ void fb_a_offsets(uint32_t (&off)[8], RowOff row_off) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * wave + 4 * i + (lane >> 4);
+    off[i] = 2u * (row_off(r) + 8u * (uint32_t)((lane & 15) ^ (r & 15)));   // bytes
+  }
+}
+
+__device__ __forceinline__ void facc_zero(FAcc& acc) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc.c[mb][nb][e] = 0.f;
+}
+
+// gate/up at the Flint shape: tile columns interleave gate and up rows of
+// pairs i0 .. i0 + 127 (column 2 i gate row i0 + i, 2 i + 1 up row i0 + i)
+__global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, PrefillWs ws, int T,
+                                                                const uint16_t* xin) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
+  const TileIdx ti = tile_of_block(2 * FI / FBN);
+  if (ti.m >= *ws.ntiles) return;
+  const int2 tile = ws.tiles[ti.m];
+  const int g = tile.x, m0 = tile.y;
+  const int E = a.E, K = a.K;
+  const bool shared = g == E;
+  const int cnt = shared ? T : ws.counts[g];
+  const int base = shared ? 0 : ws.offsets[g];
+  const int i0 = ti.n * (FBN / 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  uint32_t a_off[8];
+  fb_a_offsets(a_off, [&](int r) {
+    const int rr = m0 + r < cnt ? m0 + r : cnt - 1;
+    const int tok = shared ? rr : ws.perm_tok[base + rr];
+    return (uint32_t)tok * FH;
+  });
+  constexpr size_t MC = (size_t)FI * FH / 2, MS = (size_t)FI * FH / 16;
+  const uint8_t* c0 = shared ? a.sh_gu_codes : a.gu_codes + (size_t)(2 * g) * MC;
+  const uint8_t* s0 = shared ? a.sh_gu_scales : a.gu_scales + (size_t)(2 * g) * MS;
+  FbRows<FH / FBK> br;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int col = 64 * wave + 32 * nb + (lane & 31);
+    const int wrow = i0 + (col >> 1), up = col & 1;
+    br.c[nb] = c0 + up * MC + (size_t)wrow * (FH / 2);
+    br.s[nb] = s0 + up * MS + (size_t)wrow * (FH / 16);
+  }
+  const float* gsp = shared ? a.sh_gscale : a.gscale + 3 * g;
+  const float gs_g = gsp[0], gs_u = gsp[1];
+
+  FAcc acc;
+  facc_zero(acc);
+  fb_gemm<FH / FBK>(acc, s_a, xin, a_off, br);
+
+  // even lanes hold gate columns, odd lanes the matching up columns: the
+  // lanes of a pair swap half of their blocks so that the even lane
+  // finishes M blocks 0, 2 and the odd lane M blocks 1, 3.  h goes to LDS
+  // (the A stages are free once every wave is past its last MFMA), then to
+  // memory as whole 256-byte rows.
+  __builtin_amdgcn_s_barrier();
+  uint16_t* s_h = reinterpret_cast<uint16_t*>(&s_a[0][0]);   // [128 rows][128 pairs]
+  const bool even = (lane & 1) == 0;
+  const int h = lane >> 5;
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float gacc[2], uacc[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float a0 = acc.c[2 * pr][nb][e + q], a1 = acc.c[2 * pr + 1][nb][e + q];
+          const float recv = dpp_f<0xB1>(even ? a1 : a0);
+          gacc[q] = even ? a0 : recv;
+          uacc[q] = even ? recv : a1;
+        }
+        // rows r and r + 1 (elements e, e + 1), the same pair column
+        const uint32_t gw = pack_bf16x2_rne(gacc[0] * gs_g, gacc[1] * gs_g);
+        const uint32_t uw = pack_bf16x2_rne(uacc[0] * gs_u, uacc[1] * gs_u);
+        const uint32_t aw = pack_bf16x2_rne(silu_fast(bf16_lo(gw)), silu_fast(bf16_hi(gw)));
+        const uint32_t hw = pack_bf16x2_rne(bf16_lo(aw) * bf16_lo(uw), bf16_hi(aw) * bf16_hi(uw));
+        const int mb = 2 * pr + (even ? 0 : 1);
+        const int r = 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int c = (64 * wave + 32 * nb + (lane & 31)) >> 1;
+        s_h[r * 128 + c] = (uint16_t)(hw & 0xffffu);
+        s_h[(r + 1) * 128 + c] = (uint16_t)(hw >> 16);
+      }
+  __syncthreads();
+  {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {                  // 2048 segments of 16 bytes
+      const int q = tid + 256 * k, r = q >> 4, seg = q & 15;
+      if (m0 + r < cnt) {
+        const size_t row = shared ? (size_t)T * K + m0 + r : (size_t)base + m0 + r;
+        *reinterpret_cast<uint4*>(ws.h + row * FI + i0 + 8 * seg) =
+            *reinterpret_cast<const uint4*>(s_h + r * 128 + 8 * seg);
+      }
+    }
+  }
+}
+
+// down at the Flint shape: y = h . W_d^T (fp32, tensor scale applied)
+__global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, PrefillWs ws, int T) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
+  const TileIdx ti = tile_of_block(FH / FBN);
+  if (ti.m >= *ws.ntiles) return;
+  const int2 tile = ws.tiles[ti.m];
+  const int g = tile.x, m0 = tile.y;
+  const int E = a.E, K = a.K;
+  const bool shared = g == E;
+  const int cnt = shared ? T : ws.counts[g];
+  const size_t base = shared ? (size_t)T * K : (size_t)ws.offsets[g];
+  const int n0 = ti.n * FBN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  uint32_t a_off[8];
+  fb_a_offsets(a_off, [&](int r) {
+    const int rr = m0 + r < cnt ? m0 + r : cnt - 1;
+    return (uint32_t)((base + rr) * FI);
+  });
+  const uint8_t* c0 = shared ? a.sh_d_codes : a.d_codes + (size_t)g * FH * (FI / 2);
+  const uint8_t* s0 = shared ? a.sh_d_scales : a.d_scales + (size_t)g * FH * (FI / 16);
+  FbRows<FI / FBK> br;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + 64 * wave + 32 * nb + (lane & 31);
+    br.c[nb] = c0 + (size_t)n * (FI / 2);
+    br.s[nb] = s0 + (size_t)n * (FI / 16);
+  }
+  const float gd = shared ? a.sh_gscale[2] : a.gscale[3 * g + 2];
+
+  FAcc acc;
+  facc_zero(acc);
+  fb_gemm<FI / FBK>(acc, s_a, ws.h, a_off, br);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = m0 + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int c = n0 + 64 * wave + 32 * nb + (lane & 31);
+        if (r < cnt) ws.y[(base + r) * FH + c] = acc.c[mb][nb][e] * gd;
+      }
+}
+
 // --------------------------------------------------------------- combine --
 // One workgroup per token; 8 columns per thread per pass.
 __global__ __launch_bounds__(256) void prefill_combine_kernel(LayerArgs a, PrefillWs ws, int T) {
@@ -729,9 +1019,17 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
   const dim3 ggu(grouped_grid(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2)));
   const dim3 gdn(grouped_grid(ws.max_tiles, (a.H + BN - 1) / BN));
+  // the Flint-shape GEMMs address A with 32-bit byte offsets
+  const bool flint = !bf && a.H == FH && a.I == FI && a.SI == FI && FBM == BM &&
+                     (int64_t)T * FH * 2 < (1ll << 32) && ((int64_t)T * a.K + T) * FI * 2 < (1ll << 32);
   if (bf) {
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_BF16>, ggu, dim3(256), 0, st, a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_kernel<FMT_BF16>, gdn, dim3(256), 0, st, a, ws, T);
+  } else if (flint) {
+    hipLaunchKernelGGL(prefill_gate_up_f_kernel, dim3(grouped_grid(ws.max_tiles, 2 * FI / FBN)), dim3(256), 0, st,
+                       a, ws, T, xin);
+    hipLaunchKernelGGL(prefill_down_f_kernel, dim3(grouped_grid(ws.max_tiles, FH / FBN)), dim3(256), 0, st, a, ws,
+                       T);
   } else {
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_NVFP4>, ggu, dim3(256), 0, st, a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_kernel<FMT_NVFP4>, gdn, dim3(256), 0, st, a, ws, T);
