@@ -5,11 +5,14 @@
 // 4 KV heads of dimension 128, per-head Q/K RMSNorm, RoPE on the
 // sliding-window layers, BF16 KV cache).
 //
-// One wave per (token, head) of the projection row [q heads | k heads |
-// v heads]; lane l holds the pair (x_l, x_{l+64}) of its head, which is
-// exactly the pair the rotate-half RoPE mixes, so the rotation needs no
-// exchange between lanes.  Per q or k head: the mean of squares over the
-// head (float64 wave sum), BF16(BF16(x / rms) * gamma) with the library's
+// 64 / NP lanes per (token, head) of the projection row [q heads | k heads |
+// v heads]: lane j of a head holds elements NP j .. NP j + NP - 1 and
+// 64 + NP j .. 64 + NP j + NP - 1, i.e. the pairs (x_i, x_{i+64}) that the
+// rotate-half RoPE mixes, so the rotation needs no exchange between lanes.
+// NP = 8 (16-byte accesses, eight heads per wave) for many tokens; NP = 1
+// (one head per wave, the shortest dependent chain per lane) for a few
+// decode tokens, where the launch is latency-bound.  Per q or k head: the mean of squares
+// over the head (float64), BF16(BF16(x / rms) * gamma) with the library's
 // RMSNorm rounding, then (with FLINT_ATTN_ROPE) the rotation by the table
 // row of the token's position, taken in float64 (the products of a BF16
 // value and a float32 table entry are exact there) and rounded to BF16
@@ -39,46 +42,104 @@ struct AttnArgs {
   float eps;
 };
 
+template <int LPH>
+__device__ __forceinline__ double group_sum_f64(double v) {
+#pragma unroll
+  for (int off = 1; off < LPH; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// the lane's NP elements at p (NP = 8: 16 bytes; NP = 1: 2 bytes) as NP / 2
+// words, and back
+template <int NP>
+__device__ __forceinline__ void load_half(uint32_t (&w)[NP > 1 ? NP / 2 : 1], const uint16_t* p) {
+  if constexpr (NP == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    w[0] = *p;
+  }
+}
+template <int NP>
+__device__ __forceinline__ void store_half(uint16_t* p, const uint32_t (&w)[NP > 1 ? NP / 2 : 1]) {
+  if constexpr (NP == 8) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  else *p = (uint16_t)w[0];
+}
+// (low: x_i, high: x_{i+64}) words of the lane's NP pairs
+template <int NP>
+__device__ __forceinline__ void pair_words(uint32_t (&w)[NP], const uint32_t (&lo)[NP > 1 ? NP / 2 : 1],
+                                           const uint32_t (&hi)[NP > 1 ? NP / 2 : 1]) {
+  if constexpr (NP == 1) {
+    w[0] = (lo[0] & 0xffffu) | (hi[0] << 16);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NP / 2; ++k) {
+      w[2 * k] = (lo[k] & 0xffffu) | (hi[k] << 16);
+      w[2 * k + 1] = (lo[k] >> 16) | (hi[k] & 0xffff0000u);
+    }
+  }
+}
+
+// grid (tokens, head groups of blockDim / LPH): lane group hg (LPH lanes)
+// takes head (blockDim / LPH) blockIdx.y + hg
+template <int NP>
 __global__ __launch_bounds__(256) void qk_norm_rope_kv_kernel(AttnArgs a) {
-  constexpr int D = kHeadDim, HALF = D / 2;
+  constexpr int D = kHeadDim, HALF = D / 2, LPH = HALF / NP, NW = NP > 1 ? NP / 2 : 1;
   const int t = blockIdx.x;
-  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int head = blockIdx.y * (blockDim.x / LPH) + threadIdx.x / LPH;
+  const int j = threadIdx.x % LPH;
   const int n_heads = a.n_q + 2 * a.n_kv;
-  if (head >= n_heads) return;                     // the whole wave
+  if (head >= n_heads) return;                     // whole lane groups
   const bool rope = (a.flags & FLINT_ATTN_ROPE) != 0;
   const int slot = a.slots[t];
   const int pos = rope ? a.positions[t] : 0;
   // an index outside its table or cache: nothing of this token is written
   if ((rope && (pos < 0 || pos >= a.n_positions)) || slot >= a.n_slots) {
-    if (a.error && head == 0 && lane == 0) *a.error = 1;
+    if (a.error && head == 0 && j == 0) *a.error = 1;
     return;
   }
   const uint16_t* row = a.qkv + (size_t)t * n_heads * D + (size_t)head * D;
-  const uint32_t xa = row[lane], xb = row[lane + HALF];
+  uint32_t xa[NW], xb[NW];
+  load_half<NP>(xa, row + NP * j);                 // x_{NP j} ..
+  load_half<NP>(xb, row + HALF + NP * j);          // x_{64 + NP j} ..
   const bool is_q = head < a.n_q, is_k = !is_q && head < a.n_q + a.n_kv;
   if (!is_q && !is_k) {                            // V head: to the cache, unchanged
     if (slot >= 0) {
       uint16_t* dst = a.v_cache + ((size_t)slot * a.n_kv + (head - a.n_q - a.n_kv)) * D;
-      dst[lane] = (uint16_t)xa;
-      dst[lane + HALF] = (uint16_t)xb;
+      store_half<NP>(dst + NP * j, xa);
+      store_half<NP>(dst + HALF + NP * j, xb);
     }
     return;
   }
   const uint16_t* gamma = is_q ? a.gamma_q : a.gamma_k;
-  // RMSNorm of the head: the pair as one packed word (low: x_l, high: x_{l+64})
-  uint32_t v[1] = {xa | (xb << 16)};
-  const uint32_t g[1] = {(uint32_t)gamma[lane] | ((uint32_t)gamma[lane + HALF] << 16)};
-  const double lo = bf16_lo(v[0]), hi = bf16_hi(v[0]);
-  const double ss = wave_sum_f64(lo * lo + hi * hi);
-  rms_norm_words<1>(v, g, make_rms(sqrt(ss / (double)D + (double)a.eps)));
-  uint16_t ya = (uint16_t)(v[0] & 0xffffu), yb = (uint16_t)(v[0] >> 16);
+  uint32_t ga[NW], gb[NW], v[NP], g[NP];
+  load_half<NP>(ga, gamma + NP * j);
+  load_half<NP>(gb, gamma + HALF + NP * j);
+  pair_words<NP>(v, xa, xb);
+  pair_words<NP>(g, ga, gb);
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const double lo = bf16_lo(v[i]), hi = bf16_hi(v[i]);
+    ss = fma(lo, lo, ss);
+    ss = fma(hi, hi, ss);
+  }
+  ss = group_sum_f64<LPH>(ss);
+  rms_norm_words<NP>(v, g, make_rms(sqrt(ss / (double)D + (double)a.eps)));
+  uint32_t ya[NP], yb[NP];                          // BF16 bits of y_i, y_{i+64}
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    ya[i] = v[i] & 0xffffu;
+    yb[i] = v[i] >> 16;
+  }
   if (rope) {
     const float* cs = a.cos_sin + (size_t)pos * D;
-    const double c = cs[lane], s = cs[HALF + lane];
-    const double p = bf16_lo(v[0]), q = bf16_hi(v[0]);
-    ya = f64_to_bf16_bits(p * c - q * s);
-    yb = f64_to_bf16_bits(q * c + p * s);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const double p = bf16_lo(v[i]), q = bf16_hi(v[i]), c = cs[NP * j + i], sv = cs[HALF + NP * j + i];
+      ya[i] = f64_to_bf16_bits(p * c - q * sv);
+      yb[i] = f64_to_bf16_bits(q * c + p * sv);
+    }
   }
   uint16_t* dst;
   if (is_q) {
@@ -87,8 +148,14 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kv_kernel(AttnArgs a) {
     if (slot < 0) return;                          // a padding token keeps no KV
     dst = a.k_cache + ((size_t)slot * a.n_kv + (head - a.n_q)) * D;
   }
-  dst[lane] = ya;
-  dst[lane + HALF] = yb;
+  uint32_t oa[NW], ob[NW];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    oa[k] = NP > 1 ? ya[2 * k] | (ya[2 * k + 1] << 16) : ya[0];
+    ob[k] = NP > 1 ? yb[2 * k] | (yb[2 * k + 1] << 16) : yb[0];
+  }
+  store_half<NP>(dst + NP * j, oa);
+  store_half<NP>(dst + HALF + NP * j, ob);
 }
 
 }  // namespace
@@ -133,7 +200,14 @@ extern "C" int32_t flint_qk_norm_rope_kv(const flint_attn_shape* shape, const vo
   a.flags = shape->flags;
   a.eps = shape->rms_eps;
   const int heads = a.n_q + 2 * a.n_kv;
-  hipLaunchKernelGGL(qk_norm_rope_kv_kernel, dim3(n_tokens, (heads + 3) / 4), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  // a few decode tokens: one head per wave, four per workgroup (the shortest
+  // chain per lane, the most workgroups); many tokens: 16-byte accesses, 32
+  // heads per workgroup
+  if (n_tokens < 256)
+    hipLaunchKernelGGL(qk_norm_rope_kv_kernel<1>, dim3(n_tokens, (heads + 3) / 4), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL(qk_norm_rope_kv_kernel<8>, dim3(n_tokens, (heads + 31) / 32), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? FLINT_OK : FLINT_ERR_DEVICE;
 }
