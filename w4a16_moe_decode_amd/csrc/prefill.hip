@@ -903,7 +903,9 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, 
   }
 }
 
-// down at the Flint shape: y = h . W_d^T (fp32, tensor scale applied)
+// down at the Flint shape: y = h . W_d^T (fp32, tensor scale applied) for
+// the routed groups (the shared expert's tiles are left to the fused
+// kernel below)
 __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, PrefillWs ws, int T) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
   const TileIdx ti = tile_of_block(FH / FBN);
@@ -912,6 +914,7 @@ __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, Pre
   const int g = tile.x, m0 = tile.y;
   const int E = a.E, K = a.K;
   const bool shared = g == E;
+  if (shared) return;
   const int cnt = shared ? T : ws.counts[g];
   const size_t base = shared ? (size_t)T * K : (size_t)ws.offsets[g];
   const int n0 = ti.n * FBN;
@@ -947,6 +950,106 @@ __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, Pre
         const int c = n0 + 64 * wave + 32 * nb + (lane & 31);
         if (r < cnt) ws.y[(base + r) * FH + c] = acc.c[mb][nb][e] * gd;
       }
+}
+
+// The shared expert's down GEMM fused with the combine, at the Flint shape:
+// workgroup (token tile mt, column tile nt) computes the shared expert's
+// y for tokens 128 mt .. + 127 and columns 256 nt .. + 255 in registers,
+// then, for each of them, out = BF16(sum_k w_k y[pos(t, k)] + y_shared) (+
+// residual, rounded again): the routed rows in selection order, then the
+// shared one, as in prefill_combine_kernel.  The routed y rows were written
+// by prefill_down_f_kernel (the previous launch); the shared expert's y
+// never goes to memory, and no separate combine pass reads any of it.
+// KC: the top-k as a compile-time constant (straight-line epilogue), or 0.
+template <int KC>
+__global__ __launch_bounds__(256, 2) void prefill_down_shared_combine_f_kernel(LayerArgs a, PrefillWs ws, int T) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
+  __shared__ int s_pos[FBM][FLINT_MAX_TOP_K];
+  __shared__ float s_w[FBM][FLINT_MAX_TOP_K];
+  const TileIdx ti = tile_of_block(FH / FBN);
+  const int m0 = ti.m * FBM;
+  if (m0 >= T) return;
+  const int K = KC ? KC : a.K;
+  constexpr int KM = KC ? KC : FLINT_MAX_TOP_K;   // unrolled selections
+  const size_t base = (size_t)T * K;
+  const int n0 = ti.n * FBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool resid = (a.flags & FLINT_RESIDUAL) != 0;
+
+  for (int q = tid; q < FBM * FLINT_MAX_TOP_K; q += 256) {   // the tile's tokens' positions and weights
+    const int r = q / FLINT_MAX_TOP_K, k = q % FLINT_MAX_TOP_K;
+    const bool ok = m0 + r < T && k < K;
+    s_pos[r][k] = ok ? ws.pos[(size_t)(m0 + r) * K + k] : 0;
+    s_w[r][k] = ok ? a.topk_w[(size_t)(m0 + r) * K + k] : 0.f;
+  }
+  uint32_t a_off[8];
+  fb_a_offsets(a_off, [&](int r) {
+    const int rr = m0 + r < T ? m0 + r : T - 1;
+    return (uint32_t)((base + rr) * FI);
+  });
+  FbRows<FI / FBK> br;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + 64 * wave + 32 * nb + (lane & 31);
+    br.c[nb] = a.sh_d_codes + (size_t)n * (FI / 2);
+    br.s[nb] = a.sh_d_scales + (size_t)n * (FI / 16);
+  }
+  const float gd = a.sh_gscale[2];
+
+  FAcc acc;
+  facc_zero(acc);
+  fb_gemm<FI / FBK>(acc, s_a, ws.h, a_off, br);
+  __syncthreads();                                 // A stages free, s_pos / s_w visible
+
+  // the weighted sum of each (token, column) of the lane into LDS as BF16
+  uint16_t* s_o = reinterpret_cast<uint16_t*>(&s_a[0][0]);   // [128 rows][256 columns]
+  const int h = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int c = 64 * wave + 32 * nb + (lane & 31);
+#pragma unroll
+      for (int e0 = 0; e0 < 16; e0 += 4) {       // four rows' routed values in flight together
+        float yv[4][KM];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 32 * mb + 8 * (e0 >> 2) + 4 * h + q;
+#pragma unroll
+          for (int k = 0; k < KM; ++k)
+            yv[q][k] = k < K ? ws.y[(size_t)s_pos[r][k] * FH + n0 + c] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 32 * mb + 8 * (e0 >> 2) + 4 * h + q;
+          float sum = 0.f;
+#pragma unroll
+          for (int k = 0; k < KM; ++k)
+            if (k < K) sum = fmaf(s_w[r][k], yv[q][k], sum);
+          sum += acc.c[mb][nb][e0 + q] * gd;
+          s_o[r * 256 + c] = f32_to_bf16_bits(sum);
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int k = 0; k < 16; ++k) {                   // 4096 segments of 16 bytes: + residual, to memory
+    const int q = tid + 256 * k, r = q >> 5, seg = q & 31;
+    if (m0 + r < T) {
+      const size_t o = (size_t)(m0 + r) * FH + n0 + 8 * seg;
+      uint4 v = *reinterpret_cast<const uint4*>(s_o + r * 256 + 8 * seg);
+      if (resid) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(a.x + o);
+        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vs[i] = pack_bf16x2(bf16_lo(xs[i]) + bf16_lo(vs[i]), bf16_hi(xs[i]) + bf16_hi(vs[i]));
+        v = make_uint4(vs[0], vs[1], vs[2], vs[3]);
+      }
+      *reinterpret_cast<uint4*>(a.out + o) = v;
+    }
+  }
 }
 
 // --------------------------------------------------------------- combine --
@@ -1030,6 +1133,10 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
                        a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_f_kernel, dim3(grouped_grid(ws.max_tiles, FH / FBN)), dim3(256), 0, st, a, ws,
                        T);
+    const dim3 gsc(grouped_grid((T + FBM - 1) / FBM, FH / FBN));
+    if (a.K == 6) hipLaunchKernelGGL(prefill_down_shared_combine_f_kernel<6>, gsc, dim3(256), 0, st, a, ws, T);
+    else hipLaunchKernelGGL(prefill_down_shared_combine_f_kernel<0>, gsc, dim3(256), 0, st, a, ws, T);
+    return hipGetLastError();
   } else {
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_NVFP4>, ggu, dim3(256), 0, st, a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_kernel<FMT_NVFP4>, gdn, dim3(256), 0, st, a, ws, T);
