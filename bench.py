@@ -423,7 +423,7 @@ def bench_prefill(layer, shape, seed, T=8192, reps=5):
               f"hist max/mean {out[kind]['hist_max_over_mean']}", file=sys.stderr, flush=True)
         del g
     out.update({"tokens": T, "gflop": round(prefill_flops(shape, T) / 1e9, 2),
-                "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "dtype": "bf16 mfma (nvfp4 weights dequantised in LDS)"})
+                "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "dtype": "bf16 mfma (nvfp4 weights decoded to bf16 in registers)"})
     return out
 
 

@@ -223,6 +223,21 @@ __device__ __forceinline__ TileIdx tile_of_block(int ntn) {
   return TileIdx{mg * 8 + xcd, slot - mg * ntn};
 }
 inline unsigned grouped_grid(int max_tiles, int ntn) { return (unsigned)(((max_tiles + 7) / 8) * 8 * ntn); }
+// The same with runs of FG consecutive M tiles per XCD, N-major inside a
+// run: N tile n of tiles FG q .. FG q + FG - 1 (mostly one expert's) runs
+// back to back on one XCD, so its weight rows come from that XCD's L2 after
+// the first tile, as the run's A rows do for the other N tiles.  (The
+// gate/up GEMM gains from it; the down GEMM, with 8 N tiles and a quarter of
+// the weights per tile, does not and keeps the plain mapping.)
+constexpr int FG = 4;
+__device__ __forceinline__ TileIdx tile_of_block_runs(int ntn) {
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const int lg = slot / (FG * ntn), w = slot - lg * (FG * ntn);
+  return TileIdx{(lg * 8 + xcd) * FG + w % FG, w / FG};
+}
+inline unsigned grouped_grid_runs(int max_tiles, int ntn) {
+  return (unsigned)(((max_tiles + 8 * FG - 1) / (8 * FG)) * 8 * FG * ntn);
+}
 
 // ---------------------------------------------------------- workspaces ----
 }  // namespace
@@ -329,6 +344,98 @@ __global__ __launch_bounds__(256) void prefill_router_kernel(LayerArgs a, Prefil
         const int r = m0 + acc_row(i, e), c = n0 + acc_col(j);
         if (r < T && c < E) ws.logits[(size_t)r * E + c] = acc.c[i][j][e];
       }
+}
+
+// Router at hidden 2048 (expert count a multiple of 128).  Tile: 64 tokens x
+// 128 experts, 4 waves; wave w owns experts 32 w .. 32 w + 31 of the tile for
+// all 64 tokens (two 32x32 blocks of MFMA 32x32x16).  K chunks of 512, the
+// next chunk's loads issued before the current chunk's 64 MFMAs per wave:
+//   A  the token rows go straight into LDS (global_load_lds), two stages of
+//      64 rows x 1 KB; 16-byte segment g of tile row r sits at slot
+//      g ^ (r & 31), so a wave's operand reads of 32 rows hit 32 slots;
+//   B  the router rows go straight into registers: for MFMA s of a chunk,
+//      lane (h, n) holds the 8 values at k = 16 s + 8 h .. + 7 of expert row
+//      n, so the two lanes of a row read 32 contiguous bytes per load, and A
+//      is read in the same k order.
+// The router weights (1 MB) stay in L2; every workgroup reads a quarter of
+// them, against 64 token rows.
+constexpr int RTM = 64, RTN = 128, RKC = 512, RH = 2048;
+
+struct RtB { uint4 v[RKC / 16]; };
+
+__global__ __launch_bounds__(256, 1) void prefill_router_f_kernel(LayerArgs a, PrefillWs ws, int T,
+                                                               const uint16_t* xin) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][RTM * RKC * 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+  const int E = a.E;
+  const int m0 = blockIdx.x * RTM, e = blockIdx.y * RTN + 32 * wave + n;
+  // copy i of wave w fills tile row 16 w + i, slot `lane` <- segment lane ^ (row & 31)
+  uint32_t off[RTM / 4];
+#pragma unroll
+  for (int i = 0; i < RTM / 4; ++i) {
+    const int r = 16 * wave + i;
+    const int tok = m0 + r < T ? m0 + r : T - 1;
+    off[i] = 2u * ((uint32_t)tok * RH + 8u * (uint32_t)(lane ^ (r & 31)));
+  }
+  const uint8_t* x_base = reinterpret_cast<const uint8_t*>(xin);
+  auto copy_x = [&](int c, int buf) {
+    uint64_t sb = reinterpret_cast<uint64_t>(x_base + (size_t)c * RKC * 2);
+    asm volatile("" : "+s"(sb));             // keep the base scalar (offsets stay 32-bit)
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(sb);
+#pragma unroll
+    for (int i = 0; i < RTM / 4; ++i)
+      __builtin_amdgcn_global_load_lds(src + (uint64_t)off[i], &s_x[buf][(16 * wave + i) * 1024], 16, 0, 0);
+  };
+  const uint16_t* wrow = a.router + (size_t)e * RH + 8 * h;
+  auto load_b = [&](RtB& b, int c) {
+#pragma unroll
+    for (int s = 0; s < RKC / 16; ++s) b.v[s] = ldg<uint4>(wrow + c * RKC + 16 * s);
+  };
+  f32x16 acc[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+  auto step = [&](int c, const RtB& cur, RtB& nxt, int buf) {
+    // everything of chunk c (issued one chunk earlier) has landed; no wave
+    // still reads the stage chunk c + 1 overwrites
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < RH / RKC) {
+      copy_x(c + 1, buf ^ 1);
+      load_b(nxt, c + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* la = s_x[buf];
+#pragma unroll
+    for (int s = 0; s < RKC / 16; ++s) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int r = 32 * mb + n;
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(la + r * 1024 + 16 * ((2 * s + h) ^ (r & 31)));
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, cur.v[s]), acc[mb], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  RtB b0, b1;
+  load_b(b0, 0);
+  copy_x(0, 0);
+  static_assert((RH / RKC) % 2 == 0, "chunks go in pairs");
+#pragma unroll 1
+  for (int c = 0; c < RH / RKC; c += 2) {
+    step(c, b0, b1, 0);
+    step(c + 1, b1, b0, 1);
+  }
+  // element i of block mb: token 32 mb + 8 (i / 4) + 4 h + i % 4, expert e
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = m0 + 32 * mb + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (t < T) ws.logits[(size_t)t * E + e] = acc[mb][i];
+    }
 }
 
 // ------------------------------------------------------------------ topk --
@@ -674,8 +781,10 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(LayerArgs a, PrefillW
 //      k index 8 h + e (lane half h) stands for column 64 h + 8 j + e (the
 //      same order for A and B), so lane (h, n) needs 64 consecutive codes
 //      (32 bytes) and their 4 scale bytes of weight row n per step: loaded
-//      two steps ahead into a ring of three, decoded to exact BF16 (E2M1 x
-//      UE4M3 has at most 6 significant bits) just before each MFMA.
+//      one step ahead into the second of two register buffers, decoded to
+//      exact BF16 (E2M1 x UE4M3 has at most 6 significant bits) just before
+//      each MFMA.
+// A tile's M blocks past its last row get no copies and no MFMAs.
 // Each B value is decoded once per 128 rows: 2 VALU per value against 16
 // MFMA rows, and LDS carries only A.
 constexpr int FBM = 128, FBN = 256, FBK = 128;
@@ -720,14 +829,16 @@ __device__ __forceinline__ bf16x8_t fb_decode(const FBRaw& r, int nb) {
 
 struct FAcc { f32x16 c[4][2]; };   // [M block][N block]
 
-// One K step on A stage `la` (128 rows x 256 bytes, swizzled) and B ring entry r.
+// One K step on A stage `la` (128 rows x 256 bytes, swizzled) and B ring
+// entry r, for the tile's first NMB M blocks (the rest hold no rows).
+template <int NMB>
 __device__ __forceinline__ void fb_step(FAcc& acc, const uint8_t* la, const FBRaw& r, int lane) {
   const int h = lane >> 5, m = lane & 31;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    bf16x8_t av[4];
+    bf16x8_t av[NMB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
       const int row = 32 * mb + m;
       av[mb] = *reinterpret_cast<const bf16x8_t*>(la + row * 256 + 16 * ((8 * h + j) ^ (m & 15)));
     }
@@ -739,25 +850,29 @@ __device__ __forceinline__ void fb_step(FAcc& acc, const uint8_t* la, const FBRa
     }
 #undef FB_DEC
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         acc.c[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc.c[mb][nb], 0, 0, 0);
   }
 }
 
-// The K loop: NK steps, A stages double-buffered in s_a, B ring of three.
-// a_src: workgroup-uniform base of step 0's A elements; a_off[i]: this
-// lane's element offset of its i-th copy; each step advances by FBK.
-template <int NK>
+// The K loop: NK steps (even), A stages double-buffered in s_a, B rows
+// double-buffered in registers; NMB M blocks hold rows.  a_src: workgroup-
+// uniform base of step 0's A elements; a_off[i]: this lane's byte offset of
+// its i-th copy; each step advances by FBK.
+template <int NK, int NMB>
 __device__ __forceinline__ void fb_gemm(FAcc& acc, uint8_t (&s_a)[2][FBM * 256], const uint16_t* a_src,
                                         const uint32_t (&a_off)[8], const FbRows<NK>& brows) {
+  static_assert(NK % 2 == 0, "steps go in pairs");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
   // byte offsets on a workgroup-uniform base: the copies take the scalar
   // base + 32-bit offset form, so no address register of a copy in flight is
   // ever rewritten (the compiler would wait for the copy first)
   const uint8_t* a_base = reinterpret_cast<const uint8_t*>(a_src);
   auto copy_a = [&](int t, int buf) {
+    // wave w copies exactly M block w: an empty block is neither copied nor read
+    if (wave >= NMB) return;
     // the step's base as an opaque scalar pair: folded into the per-lane
     // offsets it would make 64-bit addresses again
     uint64_t sb = reinterpret_cast<uint64_t>(a_base + (size_t)t * FBK * 2);
@@ -772,23 +887,41 @@ __device__ __forceinline__ void fb_gemm(FAcc& acc, uint8_t (&s_a)[2][FBM * 256],
   // then multiply.  Waiting for everything leaves the compiler no wait of its
   // own to add: with a copy into LDS in flight it could only wait for all
   // loads (it cannot tell the copies' memory counts from the loads').  One
-  // step of latency is covered by the other workgroup on the CU.
-  FBRaw ring[2];
-  fb_load(ring[0], brows, 0, h);
-  copy_a(0, 0);
-#pragma unroll
-  for (int t = 0; t < NK; ++t) {
+  // step of latency is covered by the other workgroup on the CU.  The loop
+  // runs a pair of steps per iteration (static register buffers) and is not
+  // unrolled further, so four instances of it fit the instruction cache.
+  auto step = [&](int t, const FBRaw& cur, FBRaw& nxt, int buf) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     // a bare barrier: a workgroup fence would add nothing here
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < NK) {
-      copy_a(t + 1, (t + 1) & 1);
-      fb_load(ring[(t + 1) & 1], brows, t + 1, h);
+      copy_a(t + 1, buf ^ 1);
+      fb_load(nxt, brows, t + 1, h);
     }
     __builtin_amdgcn_sched_barrier(0);
-    fb_step(acc, s_a[t & 1], ring[t & 1], lane);
+    fb_step<NMB>(acc, s_a[buf], cur, lane);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  FBRaw r0, r1;
+  fb_load(r0, brows, 0, h);
+  copy_a(0, 0);
+#pragma unroll 1
+  for (int t = 0; t < NK; t += 2) {
+    step(t, r0, r1, 0);
+    step(t + 1, r1, r0, 1);
+  }
+}
+
+// fb_gemm for a tile holding `rows` (1 .. FBM) rows
+template <int NK>
+__device__ __forceinline__ void fb_gemm_rows(FAcc& acc, uint8_t (&s_a)[2][FBM * 256], const uint16_t* a_src,
+                                             const uint32_t (&a_off)[8], const FbRows<NK>& brows, int rows) {
+  switch ((rows + 31) >> 5) {
+    case 1: fb_gemm<NK, 1>(acc, s_a, a_src, a_off, brows); break;
+    case 2: fb_gemm<NK, 2>(acc, s_a, a_src, a_off, brows); break;
+    case 3: fb_gemm<NK, 3>(acc, s_a, a_src, a_off, brows); break;
+    default: fb_gemm<NK, 4>(acc, s_a, a_src, a_off, brows); break;
   }
 }
 
@@ -819,7 +952,7 @@ __device__ __forceinline__ void facc_zero(FAcc& acc) {
 __global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, PrefillWs ws, int T,
                                                                 const uint16_t* xin) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
-  const TileIdx ti = tile_of_block(2 * FI / FBN);
+  const TileIdx ti = tile_of_block_runs(2 * FI / FBN);
   if (ti.m >= *ws.ntiles) return;
   const int2 tile = ws.tiles[ti.m];
   const int g = tile.x, m0 = tile.y;
@@ -852,7 +985,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, 
 
   FAcc acc;
   facc_zero(acc);
-  fb_gemm<FH / FBK>(acc, s_a, xin, a_off, br);
+  fb_gemm_rows<FH / FBK>(acc, s_a, xin, a_off, br, cnt - m0);
 
   // even lanes hold gate columns, odd lanes the matching up columns: the
   // lanes of a pair swap half of their blocks so that the even lane
@@ -938,7 +1071,7 @@ __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, Pre
 
   FAcc acc;
   facc_zero(acc);
-  fb_gemm<FI / FBK>(acc, s_a, ws.h, a_off, br);
+  fb_gemm_rows<FI / FBK>(acc, s_a, ws.h, a_off, br, cnt - m0);
   const int h = lane >> 5;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -998,7 +1131,7 @@ __global__ __launch_bounds__(256, 2) void prefill_down_shared_combine_f_kernel(L
 
   FAcc acc;
   facc_zero(acc);
-  fb_gemm<FI / FBK>(acc, s_a, ws.h, a_off, br);
+  fb_gemm_rows<FI / FBK>(acc, s_a, ws.h, a_off, br, T - m0);
   __syncthreads();                                 // A stages free, s_pos / s_w visible
 
   // the weighted sum of each (token, column) of the lane into LDS as BF16
@@ -1115,8 +1248,12 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   const int C = (T + CHUNK - 1) / CHUNK;
   const int imax = a.I > a.SI ? a.I : a.SI;
   if (norm) hipLaunchKernelGGL(prefill_norm_kernel, dim3((T + 3) / 4), dim3(256), 0, st, a, ws, T);
-  hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
-                     st, a, ws, T, xin);
+  if (a.H == RH && a.E % RTN == 0 && (int64_t)T * RH * 2 < (1ll << 32))
+    hipLaunchKernelGGL(prefill_router_f_kernel, dim3((T + RTM - 1) / RTM, a.E / RTN), dim3(256), 0, st, a, ws, T,
+                       xin);
+  else
+    hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
+                       st, a, ws, T, xin);
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
@@ -1129,7 +1266,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_BF16>, ggu, dim3(256), 0, st, a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_kernel<FMT_BF16>, gdn, dim3(256), 0, st, a, ws, T);
   } else if (flint) {
-    hipLaunchKernelGGL(prefill_gate_up_f_kernel, dim3(grouped_grid(ws.max_tiles, 2 * FI / FBN)), dim3(256), 0, st,
+    hipLaunchKernelGGL(prefill_gate_up_f_kernel, dim3(grouped_grid_runs(ws.max_tiles, 2 * FI / FBN)), dim3(256), 0, st,
                        a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_f_kernel, dim3(grouped_grid(ws.max_tiles, FH / FBN)), dim3(256), 0, st, a, ws,
                        T);
