@@ -439,67 +439,80 @@ __global__ __launch_bounds__(256, 1) void prefill_router_f_kernel(LayerArgs a, P
 }
 
 // ------------------------------------------------------------------ topk --
-// One workgroup of 16 waves per chunk of 64 tokens, 4 tokens per wave, all
-// their logits fetched before the selection.  Writes the chunk's token
-// bitmask per expert and its pair count per expert.
-__global__ __launch_bounds__(1024) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
-  __shared__ unsigned long long s_mask[FLINT_MAX_EXPERTS];
+// One workgroup of 8 waves per half chunk (32 tokens), 4 tokens per wave,
+// all their logits fetched before the selection.  A round of a token takes
+// the wave maximum of the 32-bit order keys and finds the lowest expert that
+// holds it with ballots (lane l holds experts l + 64 q, so q = 0 is searched
+// first, then the lowest lane), then removes that key.  Writes the half
+// chunk's token bitmask per expert: its own 32-bit half of the chunk's
+// 64-bit mask, so no two workgroups write the same word.
+__global__ __launch_bounds__(512) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
+  constexpr int HT = CHUNK / 2, TPW = HT / 8;
+  __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
-  const int c = blockIdx.x;
-  if (threadIdx.x < FLINT_MAX_EXPERTS) s_mask[threadIdx.x] = 0ull;
+  const int c = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int t0 = c * CHUNK + half * HT;
+  if (threadIdx.x < FLINT_MAX_EXPERTS) s_mask[threadIdx.x] = 0u;
   __syncthreads();
   const bool renorm = (a.flags & FLINT_RENORM) != 0;
-  constexpr int TPW = CHUNK / 16;
-  uint64_t key[TPW][4];
+  // key 0 (below every order key) marks an expert past E or already taken
+  uint32_t key[TPW][4];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const int t = c * CHUNK + wave * TPW + u;
+    const int t = t0 + wave * TPW + u;
     const int tt = t < T ? t : T - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int ex = lane + 64 * q;
-      key[u][q] = ex < E ? (((uint64_t)float_order_key(ws.logits[(size_t)tt * E + ex]) << 32) |
-                            (uint32_t)~(uint32_t)ex)
-                         : 0ull;
+      key[u][q] = ex < E ? float_order_key(ws.logits[(size_t)tt * E + ex]) : 0u;
     }
   }
-  // the TPW tokens of a wave take their K rounds together (four independent
+  // the TPW tokens of a wave take their K rounds together (independent
   // chains of wave reductions, so their latencies overlap)
-  float my_s[TPW], ssum[TPW];
+  uint32_t my_m[TPW];                              // lane k: the key of selection k
   int my_e[TPW];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) { my_s[u] = 0.f; ssum[u] = 0.f; my_e[u] = 0; }
+  for (int u = 0; u < TPW; ++u) { my_m[u] = 0u; my_e[u] = 0; }
   for (int k = 0; k < K; ++k) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      uint64_t m = key[u][0];
+      const uint32_t m = wave_max_u32(max(max(key[u][0], key[u][1]), max(key[u][2], key[u][3])));
+      int win = -1;                                // workgroup-uniform
 #pragma unroll
-      for (int q = 1; q < 4; ++q) m = key[u][q] > m ? key[u][q] : m;
-      m = wave_max_key(m);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (key[u][q] == m) key[u][q] = 0ull;
-      const float sg = 1.0f / (1.0f + expf(-float_from_order_key((uint32_t)(m >> 32))));
-      ssum[u] += sg;
-      if (lane == k) { my_s[u] = sg; my_e[u] = (int)~(uint32_t)m; }
+      for (int q = 0; q < 4; ++q) {
+        if (win < 0) {
+          const unsigned long long b = __ballot(key[u][q] == m);
+          if (b != 0ull) {
+            const int w = __ffsll((long long)b) - 1;
+            win = w + 64 * q;
+            if (lane == w) key[u][q] = 0u;
+          }
+        }
+      }
+      if (lane == k) { my_m[u] = m; my_e[u] = win; }
     }
   }
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int j = wave * TPW + u;
-    const int t = c * CHUNK + j;
+    const int t = t0 + j;
+    // each selection's sigmoid once (lane k), summed in selection order
+    const float sg = 1.0f / (1.0f + expf(-float_from_order_key(my_m[u])));
+    float ssum = 0.f;
+    for (int k = 0; k < K; ++k) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), k));
     if (t < T && lane < K) {
       a.topk_idx[(size_t)t * K + lane] = my_e[u];
-      a.topk_w[(size_t)t * K + lane] = renorm ? my_s[u] / ssum[u] : my_s[u];
-      atomicOr(&s_mask[my_e[u]], 1ull << j);
+      a.topk_w[(size_t)t * K + lane] = renorm ? sg / ssum : sg;
+      atomicOr(&s_mask[my_e[u]], 1u << j);
     }
   }
   __syncthreads();
-  if (threadIdx.x < E) {
-    const uint64_t m = s_mask[threadIdx.x];
-    ws.cmask[(size_t)c * E + threadIdx.x] = m;
-    ws.cbase[(size_t)c * E + threadIdx.x] = __popcll(m);
+  if (threadIdx.x < E) {   // little-endian: half h of word w is subword 2 w + h
+    const uint32_t m = s_mask[threadIdx.x];
+    const size_t w = (size_t)c * E + threadIdx.x;
+    reinterpret_cast<uint32_t*>(ws.cmask)[2 * w + half] = m;
+    reinterpret_cast<uint16_t*>(ws.cbase)[2 * w + half] = (uint16_t)__popc(m);
   }
 }
 
@@ -507,8 +520,9 @@ __global__ __launch_bounds__(1024) void prefill_topk_kernel(LayerArgs a, Prefill
 // One workgroup of 1024 threads: thread (part, e) sums the counts of expert e
 // over its quarter of the chunks (all loads of a pass in flight together),
 // the parts and then the experts are scanned through LDS and wave prefix
-// sums, and a second pass writes every chunk's base (the counts the top-k
-// kernel left in cbase become bases).  Then the tile list.
+// sums, and a second pass writes every chunk's base over its count (the two
+// 16-bit half-chunk counts the top-k kernel left in cbase).  Then the tile
+// list.
 __global__ __launch_bounds__(1024) void prefill_scan_kernel(LayerArgs a, PrefillWs ws, int T) {
   constexpr int NB = 32;                           // chunk loads per thread per batch
   __shared__ int s_cnt[4][FLINT_MAX_EXPERTS];
@@ -521,11 +535,11 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(LayerArgs a, Prefill
   int cnt = 0;
   if (e < E) {
     for (int c0 = c_lo; c0 < c_hi; c0 += NB) {
-      int v[NB];
+      int cw[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) v[u] = ws.cbase[(size_t)(c0 + u < c_hi ? c0 + u : c_lo) * E + e];
+      for (int u = 0; u < NB; ++u) cw[u] = ws.cbase[(size_t)(c0 + u < c_hi ? c0 + u : c_lo) * E + e];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) cnt += c0 + u < c_hi ? v[u] : 0;
+      for (int u = 0; u < NB; ++u) cnt += c0 + u < c_hi ? (cw[u] & 0xffff) + (cw[u] >> 16) : 0;
     }
   }
   s_cnt[part][e] = cnt;
@@ -558,14 +572,14 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(LayerArgs a, Prefill
     }
     int run = offset + before_part;
     for (int c0 = c_lo; c0 < c_hi; c0 += NB) {
-      int v[NB];
+      int cw[NB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) v[u] = ws.cbase[(size_t)(c0 + u < c_hi ? c0 + u : c_lo) * E + e];
+      for (int u = 0; u < NB; ++u) cw[u] = ws.cbase[(size_t)(c0 + u < c_hi ? c0 + u : c_lo) * E + e];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         if (c0 + u < c_hi) {
           ws.cbase[(size_t)(c0 + u) * E + e] = run;
-          run += v[u];
+          run += (cw[u] & 0xffff) + (cw[u] >> 16);
         }
       }
     }
@@ -1254,7 +1268,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   else
     hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
                        st, a, ws, T, xin);
-  hipLaunchKernelGGL(prefill_topk_kernel, dim3(C), dim3(1024), 0, st, a, ws, T);
+  hipLaunchKernelGGL(prefill_topk_kernel, dim3(2 * C), dim3(512), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
   const dim3 ggu(grouped_grid(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2)));
