@@ -1086,17 +1086,36 @@ __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, Pre
   FAcc acc;
   facc_zero(acc);
   fb_gemm_rows<FI / FBK>(acc, s_a, ws.h, a_off, br, cnt - m0);
-  const int h = lane >> 5;
+  // y goes through LDS in two halves of 64 rows x 256 fp32 columns and out
+  // as whole 1 KB rows, 16 bytes a lane.  The stores are non-temporal: with
+  // them the combine kernel that reads y back ran 12 % faster at 8,192 tokens.  Column c of row r sits at
+  // c ^ (32 ((r >> 2) & 1)): the two lane halves of a write (rows 4 apart)
+  // then fill the two different halves of the 64 banks.
+  float* s_y = reinterpret_cast<float*>(&s_a[0][0]);   // [64][256]
+  const int h = lane >> 5, tid = threadIdx.x;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int hf = 0; hf < 2; ++hf) {
+    __syncthreads();                               // the A stages, then the previous half, are free
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = m0 + 32 * mb + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int c = n0 + 64 * wave + 32 * nb + (lane & 31);
-        if (r < cnt) ws.y[(base + r) * FH + c] = acc.c[mb][nb][e] * gd;
-      }
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * mq + 8 * (e >> 2) + 4 * h + (e & 3);
+          const int c = 64 * wave + 32 * nb + (lane & 31);
+          s_y[r * FBN + (c ^ (32 * ((r >> 2) & 1)))] = acc.c[2 * hf + mq][nb][e] * gd;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {                 // 4096 segments of 16 bytes
+      const int q = tid + 256 * k, r = q >> 6, g = q & 63;
+      const int row = m0 + 64 * hf + r;
+      if (row < cnt)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(s_y + r * FBN + 4 * (g ^ (8 * ((r >> 2) & 1)))),
+                                    reinterpret_cast<f32x4_t*>(ws.y + (base + row) * FH + n0 + 4 * g));
+    }
+  }
 }
 
 // The shared expert's down GEMM fused with the combine, at the Flint shape:
