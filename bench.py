@@ -391,11 +391,13 @@ def prefill_flops(shape: gen.MoeShape, T: int) -> float:
     return 2.0 * T * (H * E + K * 3 * I * H + 3 * SI * H)
 
 
-def bench_prefill(layer, shape, seed, T=8192, reps=5):
+def bench_prefill(layer, shape, seed, T=8192, reps=5, tiled=True):
     """The 8,192-token prefill through one Flint-shaped layer (NVFP4), for
-    i.i.d. tokens and for correlated tokens whose routing is skewed."""
+    i.i.d. tokens and for correlated tokens whose routing is skewed.  With
+    ``tiled`` the weights are also given in the prefill layout
+    (flint_moe_prefill_tiled; regrouped once, outside the timed region)."""
     out = {}
-    runner = fm.PrefillRunner(layer, shape.top_k, T, 0)
+    runner = fm.PrefillRunner(layer, shape.top_k, T, 0, tiled=tiled)
     dev = layer.router.device
     idx = torch.zeros((T, shape.top_k), dtype=torch.int32, device=dev)
     w = torch.zeros((T, shape.top_k), dtype=torch.float32, device=dev)
@@ -423,7 +425,8 @@ def bench_prefill(layer, shape, seed, T=8192, reps=5):
               f"hist max/mean {out[kind]['hist_max_over_mean']}", file=sys.stderr, flush=True)
         del g
     out.update({"tokens": T, "gflop": round(prefill_flops(shape, T) / 1e9, 2),
-                "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "dtype": "bf16 mfma (nvfp4 weights decoded to bf16 in registers)"})
+                "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "dtype": "bf16 mfma (nvfp4 weights decoded to bf16 in registers)",
+                "weights": "prefill layout (flint_moe_prefill_tiled)" if tiled else "packed planes (flint_moe_prefill)"})
     return out
 
 

@@ -356,6 +356,59 @@ FLINT_API int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_mo
                           float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
                           void* stream);
 
+/* Prefill layout of packed NVFP4 weights, for the grouped GEMMs of the
+ * 8,192-token prefill ([D0] "Optimizations": the prefill runs on the same
+ * NVFP4 weights).  Row by row, a GEMM step of 128 columns reads 64 bytes of
+ * each of 32 rows, so every load instruction touches 32 rows; in this
+ * layout it reads 1 KB in one piece.  The same bytes, regrouped (lossless):
+ * the matrices of a set become blocks of 32 (virtual) rows x 128 columns;
+ * block (vb, kb) of set m starts at code byte 2048 (m nb + vb (cols/128) +
+ * kb) and scale byte 256 (m nb + vb (cols/128) + kb), nb the blocks per
+ * set.  Inside a block, bytes 32 h + 16 p .. + 15 of row n's 64 code bytes
+ * sit at 1024 p + 16 (2 n + h), and bytes 4 h .. 4 h + 3 of its 8 scale
+ * bytes at 4 (2 n + h) (h, p in {0, 1}, n < 32).
+ *   codes, scales  (device) packed planes of n_mats matrices [rows][cols],
+ *                  flint_moe_repack's layout, 16-byte aligned
+ *   interleave     0: a set is one matrix, virtual row r = row r;
+ *                  1: a set is a (gate, up) pair of consecutive matrices
+ *                  and virtual row 2 i + u is row i of matrix u, the order
+ *                  in which the fused gate/up GEMM pairs them (n_mats even)
+ *   rows, cols     rows (1 + interleave) a multiple of 32, cols of 128
+ *   out_codes, out_scales  (device) as many bytes as the inputs, 16-byte
+ *                  aligned; they must not overlap the inputs
+ * Returns FLINT_ERR_INVALID_ARG for null pointers, bad sizes or overlap,
+ * FLINT_ERR_ALIGNMENT for misaligned planes. */
+FLINT_API int32_t flint_moe_prefill_layout(const void* codes, const void* scales, int64_t n_mats,
+                                           int32_t rows, int32_t cols, int32_t interleave,
+                                           void* out_codes, void* out_scales, void* stream);
+
+/* One layer's weights in the prefill layout (device pointers): routed
+ * gate/up (interleave 1 over the [E][2] matrices), routed down (interleave
+ * 0 over [E]), and the shared expert's the same way (NULL when
+ * shared_inter is 0). */
+typedef struct flint_moe_prefill_planes {
+  const void* gu_codes;
+  const void* gu_scales;
+  const void* d_codes;
+  const void* d_scales;
+  const void* sh_gu_codes;
+  const void* sh_gu_scales;
+  const void* sh_d_codes;
+  const void* sh_d_scales;
+} flint_moe_prefill_planes;
+
+/* flint_moe_prefill with the NVFP4 weights also in the prefill layout.  The
+ * grouped GEMMs read `planes` at hidden 2048 with routed and shared
+ * intermediate 512 (the shapes they are specialised for) and ignore it
+ * otherwise; the result is bit-identical to flint_moe_prefill's either way.
+ * planes == NULL is flint_moe_prefill; a non-null planes with a missing
+ * plane gives FLINT_ERR_INVALID_ARG, one not 16-byte aligned
+ * FLINT_ERR_ALIGNMENT.  Other arguments as flint_moe_prefill. */
+FLINT_API int32_t flint_moe_prefill_tiled(const flint_moe_shape* shape, const flint_moe_weights* weights,
+                                          const flint_moe_prefill_planes* planes, const void* x,
+                                          int32_t n_tokens, void* out, int32_t* topk_idx, float* topk_w,
+                                          const void* gamma, void* ws, int64_t ws_bytes, void* stream);
+
 /* --------------------------------------------------------------- dense GEMV -- */
 
 /* Small-batch dense GEMV on the same packed NVFP4 weights ([D0]

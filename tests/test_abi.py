@@ -302,3 +302,37 @@ def test_decode_attention_validation_codes():
     assert fm.flint_decode_attention_workspace_bytes(ok, 513, 1, 32) == 0
     assert fm.flint_decode_attention_workspace_bytes(ok, 513, 8, 100000) > 0
     assert L.flint_decode_attention_workspace_bytes(ctypes.byref(fm.FlintAttnShape(32, 4, 64, 0, 0.0)), 0, 1, 10) < 0
+
+
+def test_prefill_layout_and_tiled_validation_codes():
+    """Argument checks of flint_moe_prefill_layout and flint_moe_prefill_tiled
+    (each call fails before any work is queued)."""
+    L = fm.lib()
+    v = ctypes.c_void_p
+    lay = L.flint_moe_prefill_layout
+    ok = (v(4096), v(1 << 20), 4, 64, 256, 0, v(1 << 24), v(1 << 28), None)
+    assert lay(None, *ok[1:]) == fm.FLINT_ERR_INVALID_ARG
+    assert lay(*ok[:6], None, *ok[7:]) == fm.FLINT_ERR_INVALID_ARG
+    assert lay(*ok[:2], 0, *ok[3:]) == fm.FLINT_ERR_INVALID_ARG              # no matrices
+    assert lay(*ok[:4], 192, *ok[5:]) == fm.FLINT_ERR_INVALID_ARG            # cols not a multiple of 128
+    assert lay(*ok[:3], 48, *ok[4:]) == fm.FLINT_ERR_INVALID_ARG             # rows not a multiple of 32
+    assert lay(v(4096), v(1 << 20), 3, 16, 256, 1, *ok[6:]) == fm.FLINT_ERR_INVALID_ARG   # odd pair count
+    assert lay(*ok[:5], 2, *ok[6:]) == fm.FLINT_ERR_INVALID_ARG              # interleave 0 or 1
+    assert lay(v(4100), *ok[1:]) == fm.FLINT_ERR_ALIGNMENT
+    assert lay(*ok[:7], v((1 << 28) + 4), None) == fm.FLINT_ERR_ALIGNMENT
+    # overlap: 4 x 64 x 256 matrices are 32 KB of codes; outputs starting inside the inputs
+    assert lay(v(4096), v(1 << 20), 4, 64, 256, 0, v(4096 + 16384), v(1 << 28), None) == fm.FLINT_ERR_INVALID_ARG
+    assert lay(v(4096), v(1 << 20), 4, 64, 256, 0, v(1 << 24), v((1 << 20) + 1024), None) == fm.FLINT_ERR_INVALID_ARG
+    # the tiled prefill: a planes struct with a missing or misaligned plane
+    s = fm.FlintMoeShape(2048, 256, 512, 512, 6, 0, 1e-6)
+    w = _fake_weights()
+    ws_bytes = fm.flint_moe_workspace_bytes(s, 16)
+    def tiled(planes):
+        return L.flint_moe_prefill_tiled(ctypes.byref(s), ctypes.byref(w), ctypes.byref(planes), v(16), 16, v(32),
+                                         None, None, None, v(4096), ws_bytes, None)
+    full = {f: 1 << (20 + i) for i, (f, _) in enumerate(fm.FlintPrefillPlanes._fields_)}
+    for f in full:
+        p = fm.FlintPrefillPlanes(**{k: (None if k == f else a) for k, a in full.items()})
+        assert tiled(p) == fm.FLINT_ERR_INVALID_ARG, f
+        p = fm.FlintPrefillPlanes(**{k: (a + 4 if k == f else a) for k, a in full.items()})
+        assert tiled(p) == fm.FLINT_ERR_ALIGNMENT, f

@@ -147,3 +147,97 @@ def test_prefill_bit_reproducible(flint):
     b = r(x)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------- the prefill layout --
+
+def prefill_layout_reference(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int,
+                             interleave: int):
+    """flint_moe_prefill_layout's definition (include/flint_moe.h), written
+    out block by block: 32 virtual rows x 128 columns per block; virtual row
+    2 i + u of a pair set is row i of matrix u (interleave), else row v."""
+    n_mats = codes.shape[0] // (rows * cols // 2)
+    c = codes.reshape(n_mats, rows, cols // 2)
+    s = scales.reshape(n_mats, rows, cols // 16)
+    per = 1 + interleave
+    n_sets, rv, nkb = n_mats // per, rows * per, cols // 128
+    oc = np.zeros_like(codes).reshape(n_sets, rv // 32, nkb, 2048)
+    os_ = np.zeros_like(scales).reshape(n_sets, rv // 32, nkb, 256)
+    for m in range(n_sets):
+        for v in range(rv):
+            mat, row = (per * m + v % 2, v // 2) if interleave else (m, v)
+            vb, n = divmod(v, 32)
+            for kb in range(nkb):
+                for h in range(2):
+                    for p in range(2):
+                        src = c[mat, row, 64 * kb + 32 * h + 16 * p: 64 * kb + 32 * h + 16 * p + 16]
+                        oc[m, vb, kb, 1024 * p + 16 * (2 * n + h): 1024 * p + 16 * (2 * n + h) + 16] = src
+                    os_[m, vb, kb, 4 * (2 * n + h): 4 * (2 * n + h) + 4] = s[mat, row, 8 * kb + 4 * h: 8 * kb + 4 * h + 4]
+    return oc.reshape(-1), os_.reshape(-1)
+
+
+@pytest.mark.parametrize("n_mats,rows,cols,interleave", [(3, 64, 256, 0), (4, 48, 384, 1), (2, 16, 128, 1)])
+def test_prefill_layout_matches_definition(n_mats, rows, cols, interleave):
+    g = torch.Generator().manual_seed(n_mats * 1000 + rows + cols + interleave)
+    codes = torch.randint(0, 256, (n_mats * rows * cols // 2,), generator=g, dtype=torch.uint8)
+    scales = torch.randint(0, 256, (n_mats * rows * cols // 16,), generator=g, dtype=torch.uint8)
+    oc = torch.empty_like(codes, device="cuda")
+    os_ = torch.empty_like(scales, device="cuda")
+    fm.flint_moe_prefill_layout(codes.cuda(), scales.cuda(), n_mats, rows, cols, interleave, oc, os_)
+    torch.cuda.synchronize()
+    wc, ws_ = prefill_layout_reference(codes.numpy(), scales.numpy(), rows, cols, interleave)
+    assert np.array_equal(oc.cpu().numpy(), wc)
+    assert np.array_equal(os_.cpu().numpy(), ws_)
+
+
+def _prefill_pair(layer, shape, T, seed, flags=0, x_kind="iid"):
+    """The same call through flint_moe_prefill and flint_moe_prefill_tiled."""
+    x = gen.activations(gen.seed_for(seed, "tx", T), T, shape.hidden, "cuda", x_kind)
+    gamma = gen.rmsnorm_gamma(gen.seed_for(seed, "tg"), shape.hidden).cuda()
+    res = []
+    for tiled in (False, True):
+        runner = fm.PrefillRunner(layer, shape.top_k, T, flags, tiled=tiled)
+        idx = torch.full((T, shape.top_k), -1, dtype=torch.int32, device="cuda")
+        wts = torch.zeros((T, shape.top_k), dtype=torch.float32, device="cuda")
+        out = runner(x, topk_idx=idx, topk_w=wts, gamma=gamma)
+        torch.cuda.synchronize()
+        res.append((out.cpu(), idx.cpu(), wts.cpu()))
+    return res
+
+
+@pytest.mark.parametrize("T,flags,x_kind", [
+    (1, 0, "iid"), (100, fm.FLINT_RENORM, "iid"), (2048, fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL, "iid"),
+    (8192, fm.FLINT_RENORM, "correlated")])
+def test_flint_prefill_tiled_is_bit_identical(flint, T, flags, x_kind):
+    """The prefill layout changes only where the grouped GEMMs read their
+    weights from: outputs, indices and weights equal the packed-plane path's
+    bit for bit (that path is checked against the oracle above)."""
+    _, layer = flint
+    (o0, i0, w0), (o1, i1, w1) = _prefill_pair(layer, FLINT, T, 40 + T, flags, x_kind)
+    assert torch.equal(i0, i1) and torch.equal(w0, w1)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
+def test_flint_prefill_tiled_against_oracle(flint):
+    src, layer = flint
+    T = 333
+    x = gen.activations(gen.seed_for(41, "px", T), T, FLINT.hidden, "cpu", "iid")
+    runner = fm.PrefillRunner(layer, FLINT.top_k, T, 0, tiled=True)
+    idx = torch.full((T, FLINT.top_k), -1, dtype=torch.int32, device="cuda")
+    wts = torch.zeros((T, FLINT.top_k), dtype=torch.float32, device="cuda")
+    out = runner(x.cuda(), topk_idx=idx, topk_w=wts)
+    torch.cuda.synchronize()
+    ex = oracle_experts(src)
+    xo = gen.numpy_f64(x)
+    r = moe.route(xo, ex.router, FLINT.top_k, False)
+    forced = check_routing(idx.cpu().numpy(), wts.cpu().numpy(), r, False)
+    want, _ = moe.moe_layer(xo, ex, FLINT.top_k, False, forced_idx=forced)
+    compare_outputs(gen.numpy_f64(out), want)
+
+
+def test_prefill_planes_ignored_at_other_shapes():
+    src = gen.moe_layer_source(TINY, 42)
+    layer = pack(src)
+    (o0, i0, w0), (o1, i1, w1) = _prefill_pair(layer, TINY, 130, 43, fm.FLINT_RENORM)
+    assert torch.equal(i0, i1) and torch.equal(w0, w1)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))

@@ -62,7 +62,7 @@ EXPORTS = (
     "flint_version", "flint_status_string", "flint_nvfp4_packed_bytes",
     "flint_moe_workspace_bytes", "flint_moe_workspace_error", "flint_moe_repack", "flint_moe_unpack", "flint_nvfp4_dequant",
     "flint_moe_decode", "flint_moe_decode_noalloc", "flint_moe_decode_stage", "flint_moe_decode_path", "flint_moe_decode_stack",
-    "flint_moe_prefill", "flint_dense_gemv", "flint_qk_norm_rope_kv", "flint_decode_attention",
+    "flint_moe_prefill", "flint_moe_prefill_layout", "flint_moe_prefill_tiled", "flint_dense_gemv", "flint_qk_norm_rope_kv", "flint_decode_attention",
     "flint_decode_attention_workspace_bytes", "flint_stream_read",
 )
 
@@ -89,6 +89,12 @@ class FlintMoeWeights(ctypes.Structure):
         "router", "gu_codes", "gu_scales", "d_codes", "d_scales", "gscale",
         "sh_gu_codes", "sh_gu_scales", "sh_d_codes", "sh_d_scales", "sh_gscale",
         "gu_bf16", "d_bf16", "sh_gu_bf16", "sh_d_bf16")]
+
+
+class FlintPrefillPlanes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "gu_codes", "gu_scales", "d_codes", "d_scales",
+        "sh_gu_codes", "sh_gu_scales", "sh_d_codes", "sh_d_scales")]
 
 
 _lib = None
@@ -132,6 +138,10 @@ def lib() -> ctypes.CDLL:
         L.flint_moe_decode_path.argtypes = [ctypes.POINTER(FlintMoeShape), i32]
         L.flint_moe_prefill.restype = i32
         L.flint_moe_prefill.argtypes = dec
+        L.flint_moe_prefill_layout.restype = i32
+        L.flint_moe_prefill_layout.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp]
+        L.flint_moe_prefill_tiled.restype = i32
+        L.flint_moe_prefill_tiled.argtypes = dec[:2] + [ctypes.POINTER(FlintPrefillPlanes)] + dec[2:]
         L.flint_dense_gemv.restype = i32
         L.flint_dense_gemv.argtypes = [vp, vp, vp, vp, i32, i32, u32, vp, i32, vp, i32, vp, vp,
                                        ctypes.c_float, vp]
@@ -261,10 +271,22 @@ def weights_table(layers, device) -> torch.Tensor:
 
 
 def flint_moe_prefill(shape, weights, x, n_tokens, out, topk_idx, topk_w, gamma, ws, ws_bytes,
-                      stream=None):
-    _check("flint_moe_prefill", lib().flint_moe_prefill(
-        ctypes.byref(shape), ctypes.byref(weights), _p(x), n_tokens, _p(out), _p(topk_idx),
-        _p(topk_w), _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+                      stream=None, planes=None):
+    """flint_moe_prefill, or flint_moe_prefill_tiled when ``planes`` (a
+    FlintPrefillPlanes) is given."""
+    if planes is None:
+        _check("flint_moe_prefill", lib().flint_moe_prefill(
+            ctypes.byref(shape), ctypes.byref(weights), _p(x), n_tokens, _p(out), _p(topk_idx),
+            _p(topk_w), _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+    else:
+        _check("flint_moe_prefill_tiled", lib().flint_moe_prefill_tiled(
+            ctypes.byref(shape), ctypes.byref(weights), ctypes.byref(planes), _p(x), n_tokens, _p(out),
+            _p(topk_idx), _p(topk_w), _p(gamma), _p(ws), ws_bytes, _stream(stream)))
+
+
+def flint_moe_prefill_layout(codes, scales, n_mats, rows, cols, interleave, out_codes, out_scales, stream=None):
+    _check("flint_moe_prefill_layout", lib().flint_moe_prefill_layout(
+        _p(codes), _p(scales), n_mats, rows, cols, interleave, _p(out_codes), _p(out_scales), _stream(stream)))
 
 
 def flint_dense_gemv(codes, scales, gscale, w_bf16, rows, cols, flags, x, batch, y, epilogue,
@@ -361,6 +383,27 @@ class PackedMoeLayer:
             t = getattr(self, f)
             setattr(w, f, None if t is None else t.data_ptr())
         return w
+
+    def prefill_planes(self, stream=None):
+        """The NVFP4 planes regrouped into the prefill layout (new device
+        tensors, flint_moe_prefill_layout).  Returns the FlintPrefillPlanes
+        struct and the tensors it points into (keep them alive)."""
+        E, H, I, SI = self.n_experts, self.hidden, self.inter, self.shared_inter
+        keep = {}
+        def one(name, codes, scales, n_mats, rows, cols, interleave):
+            oc, os_ = torch.empty_like(codes), torch.empty_like(scales)
+            flint_moe_prefill_layout(codes, scales, n_mats, rows, cols, interleave, oc, os_, stream)
+            keep[name + "_codes"], keep[name + "_scales"] = oc, os_
+        one("gu", self.gu_codes, self.gu_scales, 2 * E, I, H, 1)
+        one("d", self.d_codes, self.d_scales, E, H, I, 0)
+        if SI > 0:
+            one("sh_gu", self.sh_gu_codes, self.sh_gu_scales, 2, SI, H, 1)
+            one("sh_d", self.sh_d_codes, self.sh_d_scales, 1, H, SI, 0)
+        p = FlintPrefillPlanes()
+        for f, _ in FlintPrefillPlanes._fields_:
+            t = keep.get(f)
+            setattr(p, f, None if t is None else t.data_ptr())
+        return p, keep
 
     def nvfp4_bytes(self) -> int:
         return sum(t.numel() for t in (self.gu_codes, self.gu_scales, self.d_codes, self.d_scales)
@@ -601,16 +644,19 @@ class DecodeStep:
 
 class PrefillRunner:
     """Holds a workspace for up to ``max_tokens`` tokens and calls
-    flint_moe_prefill for a layer."""
+    flint_moe_prefill (or, with ``tiled``, flint_moe_prefill_tiled) for a
+    layer."""
 
     def __init__(self, layer: PackedMoeLayer, top_k: int, max_tokens: int, flags: int = 0,
-                 rms_eps: float = 1e-6):
+                 rms_eps: float = 1e-6, tiled: bool = False):
         self.layer = layer
         self.shape = layer.shape(top_k, flags, rms_eps)
         self.cweights = layer.weights()
         self.max_tokens = max_tokens
         self.ws_bytes = flint_moe_workspace_bytes(self.shape, max_tokens)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=layer.router.device)
+        # tiled: the NVFP4 planes also in the prefill layout (flint_moe_prefill_tiled)
+        self.planes, self._planes_keep = layer.prefill_planes() if tiled else (None, None)
 
     def __call__(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, topk_idx=None, topk_w=None,
                  gamma=None, stream=None):
@@ -620,5 +666,5 @@ class PrefillRunner:
         if out is None:
             out = torch.empty_like(x)
         flint_moe_prefill(self.shape, self.cweights, x, T, out, topk_idx, topk_w, gamma, self.ws,
-                          self.ws_bytes, stream)
+                          self.ws_bytes, stream, planes=self.planes)
         return out

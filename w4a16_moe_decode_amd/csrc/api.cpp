@@ -365,10 +365,29 @@ int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_moe_weights*
                           const void* x, int32_t n_tokens, void* out, int32_t* topk_idx,
                           float* topk_w, const void* gamma, void* ws, int64_t ws_bytes,
                           void* stream) {
+  return flint_moe_prefill_tiled(shape, weights, nullptr, x, n_tokens, out, topk_idx, topk_w, gamma, ws,
+                                 ws_bytes, stream);
+}
+
+int32_t flint_moe_prefill_tiled(const flint_moe_shape* shape, const flint_moe_weights* weights,
+                                const flint_moe_prefill_planes* planes, const void* x, int32_t n_tokens,
+                                void* out, int32_t* topk_idx, float* topk_w, const void* gamma, void* ws,
+                                int64_t ws_bytes, void* stream) {
   int st = check_shape(shape);
   if (st != FLINT_OK) return st;
   st = check_weights(shape, weights);
   if (st != FLINT_OK) return st;
+  if (planes) {
+    const bool sh = shape->shared_inter > 0;
+    const void* c[4] = {planes->gu_codes, planes->d_codes, sh ? planes->sh_gu_codes : nullptr,
+                        sh ? planes->sh_d_codes : nullptr};
+    const void* sc[4] = {planes->gu_scales, planes->d_scales, sh ? planes->sh_gu_scales : nullptr,
+                         sh ? planes->sh_d_scales : nullptr};
+    for (int i = 0; i < (sh ? 4 : 2); ++i) {
+      FLINT_NEED(c[i]);
+      FLINT_NEED(sc[i]);
+    }
+  }
   if (n_tokens <= 0) return FLINT_ERR_INVALID_ARG;
   if (n_tokens > (1 << 22)) return FLINT_ERR_UNSUPPORTED;
   FLINT_NEED(x);
@@ -385,7 +404,38 @@ int32_t flint_moe_prefill(const flint_moe_shape* shape, const flint_moe_weights*
   LayerArgs a = make_args(shape, weights, x, n_tokens < 8 ? n_tokens : 8, out, gamma);
   a.topk_idx = topk_idx ? topk_idx : w.idx;
   a.topk_w = topk_w ? topk_w : w.wgt;
+  if (planes) {
+    auto u8 = [](const void* p) { return static_cast<const uint8_t*>(p); };
+    a.pf_gu_codes = u8(planes->gu_codes); a.pf_gu_scales = u8(planes->gu_scales);
+    a.pf_d_codes = u8(planes->d_codes);   a.pf_d_scales = u8(planes->d_scales);
+    if (shape->shared_inter > 0) {
+      a.pf_sh_gu_codes = u8(planes->sh_gu_codes); a.pf_sh_gu_scales = u8(planes->sh_gu_scales);
+      a.pf_sh_d_codes = u8(planes->sh_d_codes);   a.pf_sh_d_scales = u8(planes->sh_d_scales);
+    }
+  }
   return to_status(launch_prefill(a, w, n_tokens, static_cast<hipStream_t>(stream)));
+}
+
+int32_t flint_moe_prefill_layout(const void* codes, const void* scales, int64_t n_mats, int32_t rows,
+                                 int32_t cols, int32_t interleave, void* out_codes, void* out_scales,
+                                 void* stream) {
+  if (n_mats <= 0 || rows <= 0 || cols <= 0 || (interleave != 0 && interleave != 1)) return FLINT_ERR_INVALID_ARG;
+  if (cols % 128 || ((int64_t)rows * (1 + interleave)) % 32 || (interleave && n_mats % 2)) return FLINT_ERR_INVALID_ARG;
+  FLINT_NEED(codes);
+  FLINT_NEED(scales);
+  FLINT_NEED(out_codes);
+  FLINT_NEED(out_scales);
+  const int64_t cb = n_mats * rows * (int64_t)cols / 2, sb = cb / 8;
+  auto apart = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x + (uint64_t)na <= y || y + (uint64_t)nb <= x;
+  };
+  if (!apart(codes, cb, out_codes, cb) || !apart(codes, cb, out_scales, sb) || !apart(scales, sb, out_codes, cb) ||
+      !apart(scales, sb, out_scales, sb))
+    return FLINT_ERR_INVALID_ARG;
+  return to_status(launch_prefill_layout(static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                                         n_mats, rows, cols, interleave, static_cast<uint8_t*>(out_codes),
+                                         static_cast<uint8_t*>(out_scales), static_cast<hipStream_t>(stream)));
 }
 
 int32_t flint_dense_gemv(const void* codes, const void* scales, const float* gscale,

@@ -372,6 +372,11 @@ struct LayerArgs {
   const float* sh_gscale;
   const uint16_t* gu_bf16; const uint16_t* d_bf16;
   const uint16_t* sh_gu_bf16; const uint16_t* sh_d_bf16;
+  // the NVFP4 planes in the prefill layout (flint_moe_prefill_tiled), or null
+  const uint8_t* pf_gu_codes; const uint8_t* pf_gu_scales;
+  const uint8_t* pf_d_codes;  const uint8_t* pf_d_scales;
+  const uint8_t* pf_sh_gu_codes; const uint8_t* pf_sh_gu_scales;
+  const uint8_t* pf_sh_d_codes;  const uint8_t* pf_sh_d_scales;
   const uint16_t* x;       // [B][H] layer input (residual with PRE_RMSNORM)
   const uint16_t* gamma;   // [H]
   uint16_t* out;           // [B][H]
@@ -422,6 +427,9 @@ hipError_t launch_repack(const uint8_t* src, int64_t n_mats, int rows, int cols,
                          uint8_t* codes, uint8_t* scales, int64_t mat_stride, hipStream_t st);
 hipError_t launch_unpack(const uint8_t* codes, const uint8_t* scales, int64_t n_mats, int rows,
                          int cols, int layout, int64_t mat_stride, uint8_t* dst, hipStream_t st);
+// The prefill layout of packed planes (flint_moe_prefill_layout).
+hipError_t launch_prefill_layout(const uint8_t* codes, const uint8_t* scales, int64_t n_mats, int rows, int cols,
+                                 int interleave, uint8_t* out_codes, uint8_t* out_scales, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n_mats, int rows,
                           int cols, const float* tscale, float* out, hipStream_t st);
 

@@ -815,14 +815,34 @@ struct FbRows {      // this lane's weight rows (codes, scales) of its two N blo
   const uint8_t* s[2];
 };
 
-template <int NK>
+// TL: the weights in the prefill layout, where the lane's pointers already
+// hold its place in a 32-row block and a step is one block (2 KB of codes,
+// 256 B of scales); else the packed planes, row by row.
+template <int NK, bool TL>
 __device__ __forceinline__ void fb_load(FBRaw& r, const FbRows<NK>& b, int t, int h) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    r.c[nb][0] = ldg<uint4>(b.c[nb] + 64 * t + 32 * h);
-    r.c[nb][1] = ldg<uint4>(b.c[nb] + 64 * t + 32 * h + 16);
-    r.s[nb] = ldg<uint32_t>(b.s[nb] + 8 * t + 4 * h);
+    if constexpr (TL) {
+      r.c[nb][0] = ldg<uint4>(b.c[nb] + 2048 * t);
+      r.c[nb][1] = ldg<uint4>(b.c[nb] + 2048 * t + 1024);
+      r.s[nb] = ldg<uint32_t>(b.s[nb] + 256 * t);
+    } else {
+      r.c[nb][0] = ldg<uint4>(b.c[nb] + 64 * t + 32 * h);
+      r.c[nb][1] = ldg<uint4>(b.c[nb] + 64 * t + 32 * h + 16);
+      r.s[nb] = ldg<uint32_t>(b.s[nb] + 8 * t + 4 * h);
+    }
   }
+}
+
+// the lane's B pointers for N block nb in the prefill layout: virtual row
+// block vb of a set whose blocks start at codes / scales, nkb K steps per
+// block row; lane (h, n) at 16 (2 n + h) / 4 (2 n + h)
+template <int NKB>
+__device__ __forceinline__ void fb_tiled_rows(const uint8_t*& c, const uint8_t*& sc, const uint8_t* codes,
+                                              const uint8_t* scales, int vb, int lane) {
+  const int ln = 2 * (lane & 31) + (lane >> 5);
+  c = codes + (size_t)vb * NKB * 2048 + 16 * ln;
+  sc = scales + (size_t)vb * NKB * 256 + 4 * ln;
 }
 
 // the 8 codes of word j (columns 64 h + 8 j .. + 7) times their UE4M3 scale
@@ -875,7 +895,7 @@ __device__ __forceinline__ void fb_step(FAcc& acc, const uint8_t* la, const FBRa
 // double-buffered in registers; NMB M blocks hold rows.  a_src: workgroup-
 // uniform base of step 0's A elements; a_off[i]: this lane's byte offset of
 // its i-th copy; each step advances by FBK.
-template <int NK, int NMB>
+template <int NK, int NMB, bool TL>
 __device__ __forceinline__ void fb_gemm(FAcc& acc, uint8_t (&s_a)[2][FBM * 256], const uint16_t* a_src,
                                         const uint32_t (&a_off)[8], const FbRows<NK>& brows) {
   static_assert(NK % 2 == 0, "steps go in pairs");
@@ -911,14 +931,14 @@ __device__ __forceinline__ void fb_gemm(FAcc& acc, uint8_t (&s_a)[2][FBM * 256],
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < NK) {
       copy_a(t + 1, buf ^ 1);
-      fb_load(nxt, brows, t + 1, h);
+      fb_load<NK, TL>(nxt, brows, t + 1, h);
     }
     __builtin_amdgcn_sched_barrier(0);
     fb_step<NMB>(acc, s_a[buf], cur, lane);
     __builtin_amdgcn_sched_barrier(0);
   };
   FBRaw r0, r1;
-  fb_load(r0, brows, 0, h);
+  fb_load<NK, TL>(r0, brows, 0, h);
   copy_a(0, 0);
 #pragma unroll 1
   for (int t = 0; t < NK; t += 2) {
@@ -928,14 +948,14 @@ __device__ __forceinline__ void fb_gemm(FAcc& acc, uint8_t (&s_a)[2][FBM * 256],
 }
 
 // fb_gemm for a tile holding `rows` (1 .. FBM) rows
-template <int NK>
+template <int NK, bool TL>
 __device__ __forceinline__ void fb_gemm_rows(FAcc& acc, uint8_t (&s_a)[2][FBM * 256], const uint16_t* a_src,
                                              const uint32_t (&a_off)[8], const FbRows<NK>& brows, int rows) {
   switch ((rows + 31) >> 5) {
-    case 1: fb_gemm<NK, 1>(acc, s_a, a_src, a_off, brows); break;
-    case 2: fb_gemm<NK, 2>(acc, s_a, a_src, a_off, brows); break;
-    case 3: fb_gemm<NK, 3>(acc, s_a, a_src, a_off, brows); break;
-    default: fb_gemm<NK, 4>(acc, s_a, a_src, a_off, brows); break;
+    case 1: fb_gemm<NK, 1, TL>(acc, s_a, a_src, a_off, brows); break;
+    case 2: fb_gemm<NK, 2, TL>(acc, s_a, a_src, a_off, brows); break;
+    case 3: fb_gemm<NK, 3, TL>(acc, s_a, a_src, a_off, brows); break;
+    default: fb_gemm<NK, 4, TL>(acc, s_a, a_src, a_off, brows); break;
   }
 }
 
@@ -963,6 +983,7 @@ __device__ __forceinline__ void facc_zero(FAcc& acc) {
 
 // gate/up at the Flint shape: tile columns interleave gate and up rows of
 // pairs i0 .. i0 + 127 (column 2 i gate row i0 + i, 2 i + 1 up row i0 + i)
+template <bool TL>
 __global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, PrefillWs ws, int T,
                                                                 const uint16_t* xin) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
@@ -989,17 +1010,23 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, 
   FbRows<FH / FBK> br;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int col = 64 * wave + 32 * nb + (lane & 31);
-    const int wrow = i0 + (col >> 1), up = col & 1;
-    br.c[nb] = c0 + up * MC + (size_t)wrow * (FH / 2);
-    br.s[nb] = s0 + up * MS + (size_t)wrow * (FH / 16);
+    if constexpr (TL) {                            // column 2 i + u is virtual row 2 i + u of the pair set
+      const uint8_t* tc = shared ? a.pf_sh_gu_codes : a.pf_gu_codes + (size_t)(2 * g) * MC;
+      const uint8_t* ts = shared ? a.pf_sh_gu_scales : a.pf_gu_scales + (size_t)(2 * g) * MS;
+      fb_tiled_rows<FH / FBK>(br.c[nb], br.s[nb], tc, ts, ti.n * (FBN / 32) + 2 * wave + nb, lane);
+    } else {
+      const int col = 64 * wave + 32 * nb + (lane & 31);
+      const int wrow = i0 + (col >> 1), up = col & 1;
+      br.c[nb] = c0 + up * MC + (size_t)wrow * (FH / 2);
+      br.s[nb] = s0 + up * MS + (size_t)wrow * (FH / 16);
+    }
   }
   const float* gsp = shared ? a.sh_gscale : a.gscale + 3 * g;
   const float gs_g = gsp[0], gs_u = gsp[1];
 
   FAcc acc;
   facc_zero(acc);
-  fb_gemm_rows<FH / FBK>(acc, s_a, xin, a_off, br, cnt - m0);
+  fb_gemm_rows<FH / FBK, TL>(acc, s_a, xin, a_off, br, cnt - m0);
 
   // even lanes hold gate columns, odd lanes the matching up columns: the
   // lanes of a pair swap half of their blocks so that the even lane
@@ -1053,6 +1080,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_f_kernel(LayerArgs a, 
 // down at the Flint shape: y = h . W_d^T (fp32, tensor scale applied) for
 // the routed groups (the shared expert's tiles are left to the fused
 // kernel below)
+template <bool TL>
 __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, PrefillWs ws, int T) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
   const TileIdx ti = tile_of_block(FH / FBN);
@@ -1077,15 +1105,20 @@ __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, Pre
   FbRows<FI / FBK> br;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + 64 * wave + 32 * nb + (lane & 31);
-    br.c[nb] = c0 + (size_t)n * (FI / 2);
-    br.s[nb] = s0 + (size_t)n * (FI / 16);
+    if constexpr (TL) {
+      fb_tiled_rows<FI / FBK>(br.c[nb], br.s[nb], a.pf_d_codes + (size_t)g * FH * (FI / 2),
+                              a.pf_d_scales + (size_t)g * FH * (FI / 16), ti.n * (FBN / 32) + 2 * wave + nb, lane);
+    } else {
+      const int n = n0 + 64 * wave + 32 * nb + (lane & 31);
+      br.c[nb] = c0 + (size_t)n * (FI / 2);
+      br.s[nb] = s0 + (size_t)n * (FI / 16);
+    }
   }
   const float gd = shared ? a.sh_gscale[2] : a.gscale[3 * g + 2];
 
   FAcc acc;
   facc_zero(acc);
-  fb_gemm_rows<FI / FBK>(acc, s_a, ws.h, a_off, br, cnt - m0);
+  fb_gemm_rows<FI / FBK, TL>(acc, s_a, ws.h, a_off, br, cnt - m0);
   // y goes through LDS in two halves of 64 rows x 256 fp32 columns and out
   // as whole 1 KB rows, 16 bytes a lane.  The stores are non-temporal: with
   // them the combine kernel that reads y back ran 12 % faster at 8,192 tokens.  Column c of row r sits at
@@ -1127,7 +1160,7 @@ __global__ __launch_bounds__(256, 2) void prefill_down_f_kernel(LayerArgs a, Pre
 // by prefill_down_f_kernel (the previous launch); the shared expert's y
 // never goes to memory, and no separate combine pass reads any of it.
 // KC: the top-k as a compile-time constant (straight-line epilogue), or 0.
-template <int KC>
+template <int KC, bool TL>
 __global__ __launch_bounds__(256, 2) void prefill_down_shared_combine_f_kernel(LayerArgs a, PrefillWs ws, int T) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][FBM * 256];
   __shared__ int s_pos[FBM][FLINT_MAX_TOP_K];
@@ -1156,15 +1189,20 @@ __global__ __launch_bounds__(256, 2) void prefill_down_shared_combine_f_kernel(L
   FbRows<FI / FBK> br;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + 64 * wave + 32 * nb + (lane & 31);
-    br.c[nb] = a.sh_d_codes + (size_t)n * (FI / 2);
-    br.s[nb] = a.sh_d_scales + (size_t)n * (FI / 16);
+    if constexpr (TL) {
+      fb_tiled_rows<FI / FBK>(br.c[nb], br.s[nb], a.pf_sh_d_codes, a.pf_sh_d_scales,
+                              ti.n * (FBN / 32) + 2 * wave + nb, lane);
+    } else {
+      const int n = n0 + 64 * wave + 32 * nb + (lane & 31);
+      br.c[nb] = a.sh_d_codes + (size_t)n * (FI / 2);
+      br.s[nb] = a.sh_d_scales + (size_t)n * (FI / 16);
+    }
   }
   const float gd = a.sh_gscale[2];
 
   FAcc acc;
   facc_zero(acc);
-  fb_gemm_rows<FI / FBK>(acc, s_a, ws.h, a_off, br, T - m0);
+  fb_gemm_rows<FI / FBK, TL>(acc, s_a, ws.h, a_off, br, T - m0);
   __syncthreads();                                 // A stages free, s_pos / s_w visible
 
   // the weighted sum of each (token, column) of the lane into LDS as BF16
@@ -1299,13 +1337,19 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_BF16>, ggu, dim3(256), 0, st, a, ws, T, xin);
     hipLaunchKernelGGL(prefill_down_kernel<FMT_BF16>, gdn, dim3(256), 0, st, a, ws, T);
   } else if (flint) {
-    hipLaunchKernelGGL(prefill_gate_up_f_kernel, dim3(grouped_grid_runs(ws.max_tiles, 2 * FI / FBN)), dim3(256), 0, st,
-                       a, ws, T, xin);
-    hipLaunchKernelGGL(prefill_down_f_kernel, dim3(grouped_grid(ws.max_tiles, FH / FBN)), dim3(256), 0, st, a, ws,
-                       T);
+    const dim3 ggu(grouped_grid_runs(ws.max_tiles, 2 * FI / FBN)), gdn(grouped_grid(ws.max_tiles, FH / FBN));
     const dim3 gsc(grouped_grid((T + FBM - 1) / FBM, FH / FBN));
-    if (a.K == 6) hipLaunchKernelGGL(prefill_down_shared_combine_f_kernel<6>, gsc, dim3(256), 0, st, a, ws, T);
-    else hipLaunchKernelGGL(prefill_down_shared_combine_f_kernel<0>, gsc, dim3(256), 0, st, a, ws, T);
+    if (a.pf_gu_codes) {                           // the weights in the prefill layout
+      hipLaunchKernelGGL(prefill_gate_up_f_kernel<true>, ggu, dim3(256), 0, st, a, ws, T, xin);
+      hipLaunchKernelGGL(prefill_down_f_kernel<true>, gdn, dim3(256), 0, st, a, ws, T);
+      if (a.K == 6) hipLaunchKernelGGL((prefill_down_shared_combine_f_kernel<6, true>), gsc, dim3(256), 0, st, a, ws, T);
+      else hipLaunchKernelGGL((prefill_down_shared_combine_f_kernel<0, true>), gsc, dim3(256), 0, st, a, ws, T);
+    } else {
+      hipLaunchKernelGGL(prefill_gate_up_f_kernel<false>, ggu, dim3(256), 0, st, a, ws, T, xin);
+      hipLaunchKernelGGL(prefill_down_f_kernel<false>, gdn, dim3(256), 0, st, a, ws, T);
+      if (a.K == 6) hipLaunchKernelGGL((prefill_down_shared_combine_f_kernel<6, false>), gsc, dim3(256), 0, st, a, ws, T);
+      else hipLaunchKernelGGL((prefill_down_shared_combine_f_kernel<0, false>), gsc, dim3(256), 0, st, a, ws, T);
+    }
     return hipGetLastError();
   } else {
     hipLaunchKernelGGL(prefill_gate_up_kernel<FMT_NVFP4>, ggu, dim3(256), 0, st, a, ws, T, xin);

@@ -119,6 +119,34 @@ inline unsigned grid_for(int64_t n) {
   return (unsigned)(g < 65536 ? (g < 1 ? 1 : g) : 65536);
 }
 
+// Prefill layout: one thread per 16 code bytes of the output.  Output unit
+// w (0..127) of block (set, vb, kb) is piece p = w / 64 of half h = w & 1
+// of virtual row n = (w & 63) / 2: code bytes 64 kb + 32 h + 16 p .. + 15 of
+// that row; the unit with p = 0 also moves the row's scale bytes 8 kb + 4 h
+// .. + 3.  Virtual row v of a set is row v of its matrix, or (interleave)
+// row v / 2 of matrix v & 1 of its pair.
+__global__ __launch_bounds__(256) void prefill_layout_kernel(const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales, int64_t n_sets,
+                                                             int rows, int cols, int interleave,
+                                                             uint8_t* __restrict__ oc, uint8_t* __restrict__ os) {
+  const int64_t nkb = cols / 128, nvb = (int64_t)rows * (1 + interleave) / 32;
+  const int64_t blocks = n_sets * nvb * nkb, units = blocks * 128;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int64_t blk = u >> 7;                    // global block index (set, vb, kb)
+    const int w = (int)(u & 127), p = w >> 6, nh = w & 63, n = nh >> 1, h = nh & 1;
+    const int64_t set = blk / (nvb * nkb), rest = blk - set * nvb * nkb;
+    const int64_t vb = rest / nkb, kb = rest - vb * nkb;
+    const int64_t v = vb * 32 + n;
+    const int64_t mat = interleave ? 2 * set + (v & 1) : set, row = interleave ? v >> 1 : v;
+    const int64_t r = mat * rows + row;            // row of the packed planes
+    *reinterpret_cast<uint4*>(oc + blk * 2048 + 16 * w) =
+        *reinterpret_cast<const uint4*>(codes + r * (cols / 2) + kb * 64 + 32 * h + 16 * p);
+    if (p == 0)
+      *reinterpret_cast<uint32_t*>(os + blk * 256 + 4 * nh) =
+          *reinterpret_cast<const uint32_t*>(scales + r * (cols / 16) + kb * 8 + 4 * h);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_repack(const uint8_t* src, int64_t n_mats, int rows, int cols, int layout,
@@ -144,6 +172,15 @@ hipError_t launch_unpack(const uint8_t* codes, const uint8_t* scales, int64_t n_
   else
     hipLaunchKernelGGL(unpack_kernel<FLINT_SRC_SCALES_FIRST>, dim3(grid_for(n)), dim3(256), 0, st,
                        codes, scales, n, bpm, mat_stride, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_layout(const uint8_t* codes, const uint8_t* scales, int64_t n_mats, int rows, int cols,
+                                 int interleave, uint8_t* out_codes, uint8_t* out_scales, hipStream_t st) {
+  const int64_t units = n_mats * rows * (int64_t)(cols / 128) * 4;   // 16-byte code units
+  const int64_t blocks = (units + 255) / 256;
+  hipLaunchKernelGGL(prefill_layout_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st,
+                     codes, scales, n_mats / (1 + interleave), rows, cols, interleave, out_codes, out_scales);
   return hipGetLastError();
 }
 
