@@ -1214,14 +1214,15 @@ __global__ __launch_bounds__(256, 2) void prefill_down_shared_combine_f_kernel(L
     for (int nb = 0; nb < 2; ++nb) {
       const int c = 64 * wave + 32 * nb + (lane & 31);
 #pragma unroll
-      for (int e0 = 0; e0 < 16; e0 += 4) {       // four rows' routed values in flight together
+      for (int e0 = 0; e0 < 16; e0 += 4) {       // four rows' routed values in flight together (y is
+                                                 // read once: non-temporal loads, 94.8 -> 87.7 us)
         float yv[4][KM];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = 32 * mb + 8 * (e0 >> 2) + 4 * h + q;
 #pragma unroll
           for (int k = 0; k < KM; ++k)
-            yv[q][k] = k < K ? ws.y[(size_t)s_pos[r][k] * FH + n0 + c] : 0.f;
+            yv[q][k] = k < K ? __builtin_nontemporal_load(&ws.y[(size_t)s_pos[r][k] * FH + n0 + c]) : 0.f;
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
