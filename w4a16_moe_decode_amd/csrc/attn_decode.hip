@@ -121,9 +121,9 @@ __device__ __forceinline__ void step_load(StepData& d, const AdArgs& a, const St
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) d.k[4 * i + s] = ldg<uint4>(a.k_cache + r.k[i] + 32 * s + 8 * q4);
+    for (int s = 0; s < 4; ++s) d.k[4 * i + s] = ldg_nt(a.k_cache + r.k[i] + 32 * s + 8 * q4);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) d.v[j] = ldg<uint4>(a.v_cache + r.v[j] + 8 * hh);
+  for (int j = 0; j < 8; ++j) d.v[j] = ldg_nt(a.v_cache + r.v[j] + 8 * hh);
 }
 
 struct Online {

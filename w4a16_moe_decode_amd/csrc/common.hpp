@@ -218,6 +218,18 @@ __device__ __forceinline__ uint4 ldg<uint4>(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same 16 bytes as a non-temporal load, for data that streams through
+// once (weight rows of a batch, KV rows): the batch-8 layer ran 31.07 ->
+// 30.13 us with them and a 513-token window of attention 9.16 -> 8.53 us.
+// Data that many workgroups read (a token, hand-off words) keeps plain
+// loads: the batch-1 layer with every load non-temporal ran 11.1 -> 14.5 us.
+__device__ __forceinline__ uint4 ldg_nt(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const v4u GV;
+  const v4u v = __builtin_nontemporal_load((GV*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt 0 and leaves
 // expcnt and lgkmcnt unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;

@@ -75,8 +75,8 @@ __device__ __forceinline__ void gu4_load(GU4& v, const uint8_t* codes, const uin
   const uint8_t* s = scales + (size_t)row * (FL_H / 16) + 2 * li;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    v.g[k] = ldg<uint4>(c + 256 * k);
-    v.u[k] = ldg<uint4>(c + F8_MC + 256 * k);
+    v.g[k] = ldg_nt(c + 256 * k);
+    v.u[k] = ldg_nt(c + F8_MC + 256 * k);
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -173,7 +173,7 @@ __device__ __forceinline__ void down_load_pairs(DownRows& d, const uint8_t* code
 #pragma unroll
   for (int rw = 0; rw < 2; ++rw) {
     const int n = row0 + 2 * grp + rw;
-    d.c[rw] = ldg<uint4>(codes + (size_t)n * (FL_I / 2) + 16 * li);
+    d.c[rw] = ldg_nt(codes + (size_t)n * (FL_I / 2) + 16 * li);
     d.s[rw] = ldg<uint16_t>(scales + (size_t)n * (FL_I / 16) + 2 * li);
   }
 }
