@@ -219,10 +219,12 @@ __device__ __forceinline__ uint4 ldg<uint4>(const void* p) {
 }
 
 // The same 16 bytes as a non-temporal load, for data that streams through
-// once (weight rows of a batch, KV rows): the batch-8 layer ran 31.07 ->
-// 30.13 us with them and a 513-token window of attention 9.16 -> 8.53 us.
-// Data that many workgroups read (a token, hand-off words) keeps plain
-// loads: the batch-1 layer with every load non-temporal ran 11.1 -> 14.5 us.
+// once (weight rows of a decode layer, KV rows): the batch-8 layer ran
+// 31.07 -> 30.13 us with them, the batch-1 layer 11.08 -> 10.92 us and a
+// 513-token window of attention 9.16 -> 8.53 us.  Data that many
+// workgroups read (a token, hand-off words) keeps plain loads: the batch-1
+// layer with every load non-temporal ran 11.1 -> 14.5 us; so does the LM
+// head's stream (33 -> 49 us as non-temporal loads).
 __device__ __forceinline__ uint4 ldg_nt(const void* p) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(1))) const v4u GV;

@@ -70,7 +70,7 @@ __device__ __forceinline__ void item_load(GUItem<1>& it, const uint8_t* gc, cons
     const int row = 2 * p + rr;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      it.c[rr][m][0] = ldg<uint4>(gc + m * MC + (size_t)row * (FL_H / 2) + 16 * lane);
+      it.c[rr][m][0] = ldg_nt(gc + m * MC + (size_t)row * (FL_H / 2) + 16 * lane);
       it.s[rr][m][0] = ldg<uint16_t>(gs + m * MS + (size_t)row * (FL_H / 16) + 2 * lane);
     }
   }

@@ -31,7 +31,7 @@ __device__ __forceinline__ void down_load(DownRows& d, const uint8_t* codes, con
 #pragma unroll
   for (int rw = 0; rw < 2; ++rw) {
     const int n = row0 + 4 * rw + grp;
-    d.c[rw] = ldg<uint4>(codes + (size_t)n * (FL_I / 2) + 16 * li);
+    d.c[rw] = ldg_nt(codes + (size_t)n * (FL_I / 2) + 16 * li);
     d.s[rw] = ldg<uint16_t>(scales + (size_t)n * (FL_I / 16) + 2 * li);
   }
 }
