@@ -36,7 +36,6 @@
 namespace flint {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int AD_D = 128;                  // head dimension
 constexpr int AD_STEP = 32;                // positions per wave step

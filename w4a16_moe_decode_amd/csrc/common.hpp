@@ -13,6 +13,7 @@ namespace flint {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // two floats -> packed BF16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {

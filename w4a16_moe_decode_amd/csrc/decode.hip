@@ -1711,6 +1711,100 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
   }
 }
 
+// Dense NVFP4 GEMV for 2..8 tokens at 2048 columns on MFMA 16x16x32 BF16:
+// y[t][r] = BF16(g . sum_c W[r][c] x[t][c]) (+ residual, rounded again), the
+// same definition as dense_nv_kernel.  There each weight value costs about
+// five VALU instructions at batch 8 (a dot product per token); here the
+// tokens are the B operand (16 columns, those past the batch zero) and only
+// the exact BF16 decode of the weights (E2M1 x UE4M3 has at most 6
+// significant bits) stays on the VALU.
+// A wave takes DM_TILES tiles of 16 rows (A: lane (q, r) = (lane / 16, lane %
+// 16) holds row r), all of their loads issued first.  K steps of 128
+// columns: lane (q, r) loads the 16 code bytes (32 codes) of row r at column
+// 128 j + 32 q and their 2 scale bytes; MFMA i of step j takes columns
+// 128 j + 32 q + 8 i .. + 7 from lane group q, for A and B alike.  The tokens
+// sit in LDS as [8][2048] BF16, 16-byte chunk c of token t at slot c ^ (t &
+// 15), so that the 16 lanes of a group, one token each, read 16 different
+// bank groups.  (One 8-wave workgroup per CU, each wave taking five tiles
+// with two in registers at a time, ran slower: 61 against 56 us.)
+constexpr int DM_TILES = 2;
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void dense_nv_mfma_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint8_t* __restrict__ scales,
+                                                                const float* __restrict__ gscale,
+                                                                const uint16_t* __restrict__ x, int B, int rows,
+                                                                uint16_t* y, const uint16_t* aux, int resid) {
+  constexpr int C = 2048, CH = C / 8, NT = 64 * NW;
+  __shared__ uint4 s_x[kMaxB * CH];                // 32 KB
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int q = lane >> 4, r = lane & 15;
+  const int rbase = (blockIdx.x * NW + wave) * 16 * DM_TILES;
+  // every load is made: rows past the matrix read row 0 and are not stored
+  uint4 wc[DM_TILES][16];
+  uint32_t ws[DM_TILES][16];
+#pragma unroll
+  for (int tt = 0; tt < DM_TILES; ++tt) {
+    const int row = rbase + 16 * tt + r;
+    const size_t rr = row < rows ? (size_t)row : 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      wc[tt][j] = ldg<uint4>(codes + rr * (C / 2) + 64 * j + 16 * q);
+      ws[tt][j] = ldg<uint16_t>(scales + rr * (C / 16) + 8 * j + 2 * q);
+    }
+  }
+  for (int k = threadIdx.x; k < kMaxB * CH; k += NT) {   // tokens past the batch read token 0
+    const int t = k / CH, c = k - t * CH;
+    s_x[t * CH + (c ^ (t & 15))] = *reinterpret_cast<const uint4*>(x + (size_t)(t < B ? t : 0) * C + 8 * c);
+  }
+  __syncthreads();
+  const float g0 = gscale[0];
+  const int tx = r < kMaxB ? r : 0;                // this lane's token slot as B column
+  const bool live = r < B;
+  f32x4_t acc[DM_TILES];
+#pragma unroll
+  for (int tt = 0; tt < DM_TILES; ++tt) acc[tt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * j + 4 * q + i;
+      uint4 xv = s_x[tx * CH + (c ^ (tx & 15))];
+      if (!live) xv = make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, xv);
+#pragma unroll
+      for (int tt = 0; tt < DM_TILES; ++tt) {
+        const uint32_t w = i == 0 ? wc[tt][j].x : i == 1 ? wc[tt][j].y : i == 2 ? wc[tt][j].z : wc[tt][j].w;
+        const float sc = i < 2 ? e4m3_to_f32<0>(ws[tt][j]) : e4m3_to_f32<1>(ws[tt][j]);
+        const f32x2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        const f32x2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        const f32x2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        const f32x2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2_rne(f0.x * sc, f0.y * sc),
+                                                                    pack_bf16x2_rne(f1.x * sc, f1.y * sc),
+                                                                    pack_bf16x2_rne(f2.x * sc, f2.y * sc),
+                                                                    pack_bf16x2_rne(f3.x * sc, f3.y * sc)));
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[tt], 0, 0, 0);
+      }
+    }
+  }
+  // lane (q, t) holds rows 4 q .. 4 q + 3 of each tile for token t = r
+  if (live) {
+#pragma unroll
+    for (int tt = 0; tt < DM_TILES; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rbase + 16 * tt + 4 * q + i;
+        if (row < rows) {
+          const size_t o = (size_t)r * rows + row;
+          float v = round_bf16(acc[tt][i] * g0);
+          if (resid) v = bf16_bits_to_f32(aux[o]) + v;
+          y[o] = f32_to_bf16_bits(v);
+        }
+      }
+  }
+}
+
 // the tall-matrix kernel covers NVFP4 weights with 2048 or 4096 columns
 bool dense_nv_supported(int cols, int batch) {
   return (cols == 2048 || cols == 4096) && batch >= 1 && batch <= kMaxB;
@@ -1793,7 +1887,13 @@ hipError_t launch_down(const LayerArgs& a, const DecodeWs& ws, bool dense, int d
 #define FLINT_DENSE_NV(NW_, CPL_, RPL_, BT_)                                                                   \
   dense_nv_launch<NW_, CPL_, RPL_, BT_, false, false>(a.sh_d_codes, a.sh_d_scales, a.sh_gscale, hin, a.B, a.H,  \
                                                       a.SI, a.out, aux, resid, nullptr, 0.f, st)
-    if (a.SI == 2048) return a.B == 1 ? FLINT_DENSE_NV(1, 4, 2, 1) : FLINT_DENSE_NV(4, 4, 2, kMaxB);
+    if (a.SI == 2048 && a.B > 1) {                 // the MFMA form (see dense_nv_mfma_kernel)
+      constexpr int NW = 4, per = NW * 16 * DM_TILES;
+      hipLaunchKernelGGL(dense_nv_mfma_kernel<NW>, dim3((a.H + per - 1) / per), dim3(64 * NW), 0, st, a.sh_d_codes,
+                         a.sh_d_scales, a.sh_gscale, hin, a.B, a.H, a.out, aux, resid);
+      return hipGetLastError();
+    }
+    if (a.SI == 2048) return FLINT_DENSE_NV(1, 4, 2, 1);
     return a.B == 1 ? FLINT_DENSE_NV(1, 8, 1, 1) : FLINT_DENSE_NV(4, 8, 1, kMaxB);
 #undef FLINT_DENSE_NV
   }
