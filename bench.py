@@ -391,7 +391,7 @@ def prefill_flops(shape: gen.MoeShape, T: int) -> float:
     return 2.0 * T * (H * E + K * 3 * I * H + 3 * SI * H)
 
 
-def bench_prefill(layer, shape, seed, T=8192, reps=5, tiled=True):
+def bench_prefill(layer, shape, seed, T=8192, reps=4, tiled=True, warm=16, timed_reps=16):
     """The 8,192-token prefill through one Flint-shaped layer (NVFP4), for
     i.i.d. tokens and for correlated tokens whose routing is skewed.  With
     ``tiled`` the weights are also given in the prefill layout
@@ -414,12 +414,17 @@ def bench_prefill(layer, shape, seed, T=8192, reps=5, tiled=True):
         with torch.cuda.graph(g):
             for _ in range(reps):
                 runner(x, y, idx, w)
-        g.replay()
-        secs = timed(g) / reps
+        # Warm-up replays: the first few milliseconds of prefill work in a
+        # process run up to 15 % slower than the rest.
+        for _ in range(warm):
+            g.replay()
+        each, total = timed_replays(g, timed_reps)
+        secs = total / (timed_reps * reps)
         hist = torch.bincount(idx.reshape(-1).long(), minlength=shape.n_experts).float()
         fl = prefill_flops(shape, T)
         out[kind] = {"us": round(secs * 1e6, 1), "tflops": round(fl / secs / 1e12, 1),
                      "frac_mfma_peak": round(fl / secs / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "us_replays_p10_p50_p90": [round(v / reps * 1e6, 1) for v in percentiles(each)],
                      "hist_max_over_mean": round(float(hist.max() / hist.mean()), 2)}
         print(f"[bench] prefill {kind}: {secs * 1e6:.1f} us, {fl / secs / 1e12:.1f} TFLOP/s, "
               f"hist max/mean {out[kind]['hist_max_over_mean']}", file=sys.stderr, flush=True)

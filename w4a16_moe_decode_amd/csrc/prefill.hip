@@ -278,6 +278,7 @@ PrefillWs carve_prefill_ws(void* base, const flint_moe_shape& s, int T) {
   w.pos = reinterpret_cast<int32_t*>(take((int64_t)T * K * 4));
   w.h = reinterpret_cast<uint16_t*>(take(rows * imax * 2));
   w.y = reinterpret_cast<float*>(take(rows * H * 4));
+  w.router_f = (H == 2048 && E == 256) ? reinterpret_cast<uint16_t*>(take((int64_t)E * H * 2)) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -438,39 +439,17 @@ __global__ __launch_bounds__(256, 1) void prefill_router_f_kernel(LayerArgs a, P
 }
 
 // ------------------------------------------------------------------ topk --
-// One workgroup of 8 waves per half chunk (32 tokens), 4 tokens per wave,
-// all their logits fetched before the selection.  A round of a token takes
-// the wave maximum of the 32-bit order keys and finds the lowest expert that
-// holds it with ballots (lane l holds experts l + 64 q, so q = 0 is searched
-// first, then the lowest lane), then removes that key.  Writes the half
-// chunk's token bitmask per expert: its own 32-bit half of the chunk's
-// 64-bit mask, so no two workgroups write the same word.
-__global__ __launch_bounds__(512) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
-  constexpr int HT = CHUNK / 2, TPW = HT / 8;
-  __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int E = a.E, K = a.K;
-  const int c = blockIdx.x >> 1, half = blockIdx.x & 1;
-  const int t0 = c * CHUNK + half * HT;
-  if (threadIdx.x < FLINT_MAX_EXPERTS) s_mask[threadIdx.x] = 0u;
-  __syncthreads();
-  const bool renorm = (a.flags & FLINT_RENORM) != 0;
-  // key 0 (below every order key) marks an expert past E or already taken
-  uint32_t key[TPW][4];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int t = t0 + wave * TPW + u;
-    const int tt = t < T ? t : T - 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ex = lane + 64 * q;
-      key[u][q] = ex < E ? float_order_key(ws.logits[(size_t)tt * E + ex]) : 0u;
-    }
-  }
-  // the TPW tokens of a wave take their K rounds together (independent
-  // chains of wave reductions, so their latencies overlap)
-  uint32_t my_m[TPW];                              // lane k: the key of selection k
-  int my_e[TPW];
+// The selection of one half chunk (32 tokens) by 8 waves, 4 tokens per wave.
+// A round of a token takes the wave maximum of the 32-bit order keys and
+// finds the lowest expert that holds it with ballots (lane l holds experts
+// l + 64 q, so q = 0 is searched first, then the lowest lane), then removes
+// that key.  Key 0 (below every order key) marks an expert past E or already
+// taken.  The TPW tokens of a wave take their K rounds together (independent
+// chains of wave reductions, so their latencies overlap).  Lane k ends with
+// selection k of each token: its order key and its expert.
+constexpr int HT = CHUNK / 2, TPW = HT / 8;
+__device__ __forceinline__ void select_topk(uint32_t (&key)[TPW][4], int K, uint32_t (&my_m)[TPW],
+                                            int (&my_e)[TPW], int lane) {
 #pragma unroll
   for (int u = 0; u < TPW; ++u) { my_m[u] = 0u; my_e[u] = 0; }
   for (int k = 0; k < K; ++k) {
@@ -492,11 +471,20 @@ __global__ __launch_bounds__(512) void prefill_topk_kernel(LayerArgs a, PrefillW
       if (lane == k) { my_m[u] = m; my_e[u] = win; }
     }
   }
+}
+
+// Writes the selections of the wave's tokens (token t0 + 4 wave + u): each
+// selection's sigmoid once (lane k), summed in selection order for the
+// renormalised weights; and sets bit j of the token in its experts' half
+// chunk masks in LDS.
+__device__ __forceinline__ void emit_topk(const LayerArgs& a, int T, int t0, int wave, int lane,
+                                          const uint32_t (&my_m)[TPW], const int (&my_e)[TPW], uint32_t* s_mask) {
+  const int K = a.K;
+  const bool renorm = (a.flags & FLINT_RENORM) != 0;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int j = wave * TPW + u;
     const int t = t0 + j;
-    // each selection's sigmoid once (lane k), summed in selection order
     const float sg = 1.0f / (1.0f + expf(-float_from_order_key(my_m[u])));
     float ssum = 0.f;
     for (int k = 0; k < K; ++k) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sg), k));
@@ -506,13 +494,183 @@ __global__ __launch_bounds__(512) void prefill_topk_kernel(LayerArgs a, PrefillW
       atomicOr(&s_mask[my_e[u]], 1u << j);
     }
   }
-  __syncthreads();
-  if (threadIdx.x < E) {   // little-endian: half h of word w is subword 2 w + h
+}
+
+// The half chunk's token bitmask per expert: its own 32-bit half of the
+// chunk's 64-bit mask, so no two workgroups write the same word, and the
+// half's count beside it (little-endian: half h of word w is subword 2 w + h).
+__device__ __forceinline__ void write_half_masks(const PrefillWs& ws, int E, int c, int half, const uint32_t* s_mask) {
+  if (threadIdx.x < E) {
     const uint32_t m = s_mask[threadIdx.x];
     const size_t w = (size_t)c * E + threadIdx.x;
     reinterpret_cast<uint32_t*>(ws.cmask)[2 * w + half] = m;
     reinterpret_cast<uint16_t*>(ws.cbase)[2 * w + half] = (uint16_t)__popc(m);
   }
+}
+
+// One workgroup per half chunk, all its logits fetched before the selection.
+__global__ __launch_bounds__(512) void prefill_topk_kernel(LayerArgs a, PrefillWs ws, int T) {
+  __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E;
+  const int c = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int t0 = c * CHUNK + half * HT;
+  if (threadIdx.x < FLINT_MAX_EXPERTS) s_mask[threadIdx.x] = 0u;
+  __syncthreads();
+  uint32_t key[TPW][4];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = t0 + wave * TPW + u;
+    const int tt = t < T ? t : T - 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ex = lane + 64 * q;
+      key[u][q] = ex < E ? float_order_key(ws.logits[(size_t)tt * E + ex]) : 0u;
+    }
+  }
+  uint32_t my_m[TPW];
+  int my_e[TPW];
+  select_topk(key, a.K, my_m, my_e, lane);
+  emit_topk(a, T, t0, wave, lane, my_m, my_e, s_mask);
+  __syncthreads();
+  write_half_masks(ws, E, c, half, s_mask);
+}
+
+// ------------------------------------------------- router + top-k, fused --
+// At hidden 2048 and 256 experts, one workgroup of 8 waves per half chunk
+// (32 tokens) computes all 256 logits of its tokens and selects their top-k,
+// so the logits never go to memory.  Wave w computes experts 32 w .. + 31
+// for the 32 tokens: one MFMA 32x32x16 block over K = 2048, with the same
+// operand layout and k order as prefill_router_f_kernel (identical logits).
+//   A  the 32 token rows (128 KB) are copied straight into LDS
+//      (global_load_lds), in 4 groups of 512 columns; slot p of row r holds
+//      the row's 16-byte segment p ^ (r & 31), so the 32 rows that one A
+//      read touches spread over the banks.  The first group goes out with
+//      the first router chunk, the other three with the second.
+//   B  the router rows stream from L2 straight into registers in chunks of
+//      256 columns, one chunk ahead, from a copy in fragment order
+//      (prefill_router_frag_kernel): each load instruction reads 1 KB in one
+//      piece.  Read from the row-major router, the 32 rows of a load are
+//      4 KB apart, and the kernel took 45 us at 8,192 tokens.
+// Each token's x row is read from memory once (the two-kernel path reads it
+// once per expert tile), and the router (1 MB) once per workgroup from L2.
+constexpr int RFK = 256;
+struct RfB { uint4 v[RFK / 16]; };
+
+// The router in fragment order: 1 KB piece f = 8 (16 ck + s) + w holds, at
+// lane (h, n), row 32 w + n, columns 256 ck + 16 s + 8 h .. + 7.  One thread
+// per 16 bytes, E H / 8 of them.
+__global__ __launch_bounds__(256) void prefill_router_frag_kernel(const uint16_t* router, uint16_t* out) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  const int lane = p & 63, f = p >> 6;
+  const int w = f & 7, s = (f >> 3) & 15, ck = f >> 7;
+  const int h = lane >> 5, n = lane & 31;
+  const uint4 v = ldg<uint4>(router + (size_t)(32 * w + n) * RH + RFK * ck + 16 * s + 8 * h);
+  *reinterpret_cast<uint4*>(out + (size_t)p * 8) = v;
+}
+
+__global__ __launch_bounds__(512, 1) void prefill_route_f_kernel(LayerArgs a, PrefillWs ws, int T,
+                                                              const uint16_t* xin) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[HT * RH * 2];
+  __shared__ uint32_t s_mask[FLINT_MAX_EXPERTS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, n = lane & 31;
+  const int c = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int t0 = c * CHUNK + half * HT;
+  const int e = 32 * wave + n;
+  if (threadIdx.x < FLINT_MAX_EXPERTS) s_mask[threadIdx.x] = 0u;
+  // copy i of wave w fills row 4 w + i of group g: 1 KB, slot 64 g + lane
+  uint32_t off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * wave + i;
+    const int tok = t0 + r < T ? t0 + r : T - 1;
+    off[i] = 2u * ((uint32_t)tok * RH + 8u * (uint32_t)(lane ^ (r & 31)));
+  }
+  const uint8_t* x_base = reinterpret_cast<const uint8_t*>(xin);
+  auto copy_x = [&](int g) {
+    uint64_t sb = reinterpret_cast<uint64_t>(x_base + (size_t)g * 1024);
+    asm volatile("" : "+s"(sb));             // keep the base scalar (offsets stay 32-bit)
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(sb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(src + (uint64_t)off[i], &s_x[(4 * wave + i) * (RH * 2) + g * 1024], 16, 0, 0);
+  };
+  const uint8_t* wfrag = reinterpret_cast<const uint8_t*>(ws.router_f) + 1024 * wave + 16 * lane;
+  auto load_b = [&](RfB& b, int ck) {
+#pragma unroll
+    for (int s = 0; s < RFK / 16; ++s) b.v[s] = ldg<uint4>(wfrag + (size_t)(8 * (16 * ck + s)) * 1024);
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  // MFMA s of chunk ck: lane (h, n) takes row n's segment 32 ck + 2 s + h
+  auto mfmas = [&](int ck, const RfB& b) {
+    const uint8_t* row = s_x + n * (RH * 2);
+#pragma unroll
+    for (int s = 0; s < RFK / 16; ++s) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(row + 16 * ((32 * ck + 2 * s + h) ^ n));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, b.v[s]), acc, 0, 0, 0);
+    }
+  };
+  RfB b0, b1;
+  copy_x(0);
+  load_b(b0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();                                 // x group 0 and the masks' zeros visible
+  // Chunk 0's A fragments are read before the other groups' copies go out:
+  // an LDS read issued behind a pending copy into LDS waits for the copy.
+  bf16x8_t a0[RFK / 16];
+  {
+    const uint8_t* row = s_x + n * (RH * 2);
+#pragma unroll
+    for (int s = 0; s < RFK / 16; ++s) a0[s] = *reinterpret_cast<const bf16x8_t*>(row + 16 * ((2 * s + h) ^ n));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  copy_x(1);
+  copy_x(2);
+  copy_x(3);
+  load_b(b1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < RFK / 16; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], __builtin_bit_cast(bf16x8_t, b0.v[s]), acc, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __builtin_amdgcn_s_barrier();                    // every group of x in LDS
+  __builtin_amdgcn_sched_barrier(0);
+  static_assert(RH / RFK == 8, "eight router chunks");
+#pragma unroll
+  for (int ck = 1; ck < RH / RFK - 1; ck += 2) {   // chunks 1 .. 6 in pairs; b1 holds chunk ck
+    load_b(b0, ck + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(ck, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    load_b(b1, ck + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(ck + 1, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+  mfmas(RH / RFK - 1, b1);
+  // the logits, [32 tokens][256 experts] fp32, over the x rows
+  __syncthreads();                                 // every wave is done with x
+  float* s_l = reinterpret_cast<float*>(s_x);
+  // element i: token 8 (i / 4) + 4 h + i % 4, expert e
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s_l[(8 * (i >> 2) + 4 * h + (i & 3)) * 256 + e] = acc[i];
+  __syncthreads();
+  uint32_t key[TPW][4];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) key[u][q] = float_order_key(s_l[(wave * TPW + u) * 256 + lane + 64 * q]);
+  uint32_t my_m[TPW];
+  int my_e[TPW];
+  select_topk(key, a.K, my_m, my_e, lane);
+  emit_topk(a, T, t0, wave, lane, my_m, my_e, s_mask);
+  __syncthreads();
+  write_half_masks(ws, a.E, c, half, s_mask);
 }
 
 // ------------------------------------------------------------------ scan --
@@ -1321,13 +1479,18 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillWs& ws, int T, hipStr
   const int C = (T + CHUNK - 1) / CHUNK;
   const int imax = a.I > a.SI ? a.I : a.SI;
   if (norm) hipLaunchKernelGGL(prefill_norm_kernel, dim3((T + 3) / 4), dim3(256), 0, st, a, ws, T);
-  if (a.H == RH && a.E % RTN == 0 && (int64_t)T * RH * 2 < (1ll << 32))
-    hipLaunchKernelGGL(prefill_router_f_kernel, dim3((T + RTM - 1) / RTM, a.E / RTN), dim3(256), 0, st, a, ws, T,
-                       xin);
-  else
-    hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
-                       st, a, ws, T, xin);
-  hipLaunchKernelGGL(prefill_topk_kernel, dim3(2 * C), dim3(512), 0, st, a, ws, T);
+  if (a.H == RH && a.E == 256 && (int64_t)T * RH * 2 < (1ll << 32)) {
+    hipLaunchKernelGGL(prefill_router_frag_kernel, dim3(a.E * RH / 8 / 256), dim3(256), 0, st, a.router, ws.router_f);
+    hipLaunchKernelGGL(prefill_route_f_kernel, dim3(2 * C), dim3(512), 0, st, a, ws, T, xin);
+  } else {
+    if (a.H == RH && a.E % RTN == 0 && (int64_t)T * RH * 2 < (1ll << 32))
+      hipLaunchKernelGGL(prefill_router_f_kernel, dim3((T + RTM - 1) / RTM, a.E / RTN), dim3(256), 0, st, a, ws, T,
+                         xin);
+    else
+      hipLaunchKernelGGL(prefill_router_kernel, dim3((T + BM - 1) / BM, (a.E + BN - 1) / BN), dim3(256), 0,
+                         st, a, ws, T, xin);
+    hipLaunchKernelGGL(prefill_topk_kernel, dim3(2 * C), dim3(512), 0, st, a, ws, T);
+  }
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(1024), 0, st, a, ws, T);
   hipLaunchKernelGGL(prefill_scatter_kernel, dim3(C), dim3(256), 0, st, a, ws, T);
   const dim3 ggu(grouped_grid(ws.max_tiles, (imax + BN / 2 - 1) / (BN / 2)));

@@ -21,6 +21,7 @@ struct PrefillWs {
   int32_t* pos;          // [T][K]
   uint16_t* h;           // [T*K + T][Imax]
   float* y;              // [T*K + T][H]
+  uint16_t* router_f;    // [E*H] the router in the fused routing kernel's fragment order (H 2048, E 256), else null
   int max_tiles;
   int64_t bytes;
 };
