@@ -1740,24 +1740,37 @@ __global__ __launch_bounds__(64 * NW) void dense_nv_mfma_kernel(const uint8_t* _
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4, r = lane & 15;
   const int rbase = (blockIdx.x * NW + wave) * 16 * DM_TILES;
+  // The tokens' loads go out first and the weights' after them, in the
+  // order the K steps use them: the staging then waits for the token loads
+  // only, and each step for its own weight loads, so the decode of the first
+  // steps runs while the later steps' rows are still arriving.
+  static_assert((kMaxB * CH) % NT == 0, "whole token loads per thread");
+  uint4 xs[kMaxB * CH / NT];
+#pragma unroll
+  for (int i = 0; i < kMaxB * CH / NT; ++i) {      // tokens past the batch read token 0
+    const int k = threadIdx.x + NT * i, t = k / CH, c = k - t * CH;
+    xs[i] = *reinterpret_cast<const uint4*>(x + (size_t)(t < B ? t : 0) * C + 8 * c);
+  }
   // every load is made: rows past the matrix read row 0 and are not stored
   uint4 wc[DM_TILES][16];
   uint32_t ws[DM_TILES][16];
 #pragma unroll
-  for (int tt = 0; tt < DM_TILES; ++tt) {
-    const int row = rbase + 16 * tt + r;
-    const size_t rr = row < rows ? (size_t)row : 0;
+  for (int j = 0; j < 16; ++j) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int tt = 0; tt < DM_TILES; ++tt) {
+      const int row = rbase + 16 * tt + r;
+      const size_t rr = row < rows ? (size_t)row : 0;
       wc[tt][j] = ldg<uint4>(codes + rr * (C / 2) + 64 * j + 16 * q);
       ws[tt][j] = ldg<uint16_t>(scales + rr * (C / 16) + 8 * j + 2 * q);
     }
   }
-  for (int k = threadIdx.x; k < kMaxB * CH; k += NT) {   // tokens past the batch read token 0
-    const int t = k / CH, c = k - t * CH;
-    s_x[t * CH + (c ^ (t & 15))] = *reinterpret_cast<const uint4*>(x + (size_t)(t < B ? t : 0) * C + 8 * c);
+#pragma unroll
+  for (int i = 0; i < kMaxB * CH / NT; ++i) {
+    const int k = threadIdx.x + NT * i, t = k / CH, c = k - t * CH;
+    s_x[t * CH + (c ^ (t & 15))] = xs[i];
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);       // the staged tokens are in LDS (no wait on the weights)
+  __builtin_amdgcn_s_barrier();
   const float g0 = gscale[0];
   const int tx = r < kMaxB ? r : 0;                // this lane's token slot as B column
   const bool live = r < B;
