@@ -236,7 +236,6 @@ __device__ __forceinline__ uint4 ldg_nt(const void* p) {
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt 0 and leaves
 // expcnt and lgkmcnt unconstrained.
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kWaitLgkmcnt0 = 0xC07F;            // vmcnt and expcnt left at their maxima
 
 // ------------------------------------------------------- wave reductions --
 

@@ -1729,6 +1729,10 @@ void dense_nv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
 // with two in registers at a time, ran slower: 61 against 56 us.)
 constexpr int DM_TILES = 2;
 
+// s_waitcnt immediate (gfx9 encoding) that waits for lgkmcnt 0 and leaves
+// vmcnt and expcnt at their maxima.
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void dense_nv_mfma_kernel(const uint8_t* __restrict__ codes,
                                                                 const uint8_t* __restrict__ scales,
