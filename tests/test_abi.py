@@ -145,7 +145,9 @@ def test_decode_path_rules():
     assert e.value.status == fm.FLINT_ERR_UNSUPPORTED
     for flags in (fm.FLINT_SPLIT, fm.FLINT_W_BF16):
         s = fm.FlintMoeShape(2048, 256, 512, 512, 6, flags, 1e-6)
-        assert fm.flint_moe_decode_path(s, 1) == fm.FLINT_PATH_SPLIT
+        # W16A16 at batch 1 takes the BF16 form of the single launch
+        want1 = fm.FLINT_PATH_SINGLE_ONE if flags == fm.FLINT_W_BF16 else fm.FLINT_PATH_SPLIT
+        assert fm.flint_moe_decode_path(s, 1) == want1
         assert fm.flint_moe_decode_path(s, 8) == fm.FLINT_PATH_SPLIT
     tiny = fm.FlintMoeShape(512, 32, 128, 128, 4, 0, 1e-6)          # hidden not a multiple of 2048
     assert fm.flint_moe_decode_path(tiny, 1) == fm.FLINT_PATH_SPLIT

@@ -98,10 +98,17 @@ def test_flint_batch_top_k(top_k, batch):
 
 
 def test_flint_layer_bf16_weights(flint_layer):
+    """W16A16 at the Flint shape: batch 1 runs the BF16 form of the single
+    launch (also with pre-norm + residual and renormalised weights), batch 8
+    the three kernels."""
     src, layer = flint_layer
     layer.add_bf16()
     try:
+        assert fm.flint_moe_decode_path(abi(FLINT, fm.FLINT_W_BF16), 1) == fm.FLINT_PATH_SINGLE_ONE
         run_decode_case(DecodeCase(FLINT, seed=200, batch=1, wbf16=True), src=src, layer=layer)
+        run_decode_case(DecodeCase(FLINT, seed=202, batch=1, wbf16=True, flags=fm.FLINT_RENORM), src=src, layer=layer)
+        run_decode_case(DecodeCase(FLINT, seed=203, batch=1, wbf16=True,
+                                   flags=fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL), src=src, layer=layer)
         run_decode_case(DecodeCase(FLINT, seed=201, batch=8, wbf16=True), src=src, layer=layer)
     finally:
         layer.gu_bf16 = layer.d_bf16 = layer.sh_gu_bf16 = layer.sh_d_bf16 = None

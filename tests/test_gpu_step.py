@@ -88,6 +88,11 @@ def test_decode_step_bf16_weights():
     _check_step(3, 2, 3, seed=3, wbf16=True)
 
 
+def test_decode_step_bf16_weights_batch1():
+    """W16A16 at batch 1: each MoE sublayer one launch of the BF16 form."""
+    _check_step(3, 2, 1, seed=5, wbf16=True)
+
+
 def test_step_graph_replay_matches_eager():
     srcs, layers, gmo, dsrc, dl, gde = _build(4, 2, seed=4)
     step = fm.DecodeStep(layers, gmo, dl, gde, SH.top_k)

@@ -324,7 +324,7 @@ int32_t flint_moe_decode_stack(const flint_moe_shape* shape, const flint_moe_wei
   a.H = shape->hidden; a.E = shape->n_experts; a.I = shape->inter; a.SI = shape->shared_inter;
   a.K = shape->top_k; a.B = 1; a.eps = shape->rms_eps;
   a.flags = shape->flags | FLINT_PRE_RMSNORM | FLINT_RESIDUAL;
-  const bool flint = flint_b1_supported(a);
+  const bool flint = !(a.flags & FLINT_W_BF16) && flint_b1_supported(a);   // the stack reads NVFP4 planes
   if (!flint && !fused_stack_supported(a)) return FLINT_ERR_UNSUPPORTED;
   sa.layers = layers;
   sa.gammas = static_cast<const uint16_t*>(gammas);

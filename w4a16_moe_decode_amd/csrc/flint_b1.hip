@@ -27,6 +27,10 @@
 //
 // Hand-offs between workgroups are the epoch-tagged 64-bit words of the
 // general kernel (one copy per XCD), with the same bounded waits.
+//
+// The same kernel runs the W16A16 form (BF16 expert weights, no tensor
+// scales): a lane then holds its 32 columns of each row as four 16-byte
+// words instead of one word of codes and its block scales.
 #include "flint_common.hpp"
 
 namespace flint {
@@ -76,18 +80,95 @@ __device__ __forceinline__ void item_load(GUItem<1>& it, const uint8_t* gc, cons
   }
 }
 
+// W16A16 (BF16 weights, no tensor scales): a lane holds the same 32
+// columns of each row as in the NVFP4 form, as four 16-byte words.
+struct GUItemBF { uint4 c[2][2][4]; };   // [row][gate|up][16-byte word]
+struct DownRowsBF { uint4 c[2][4]; };    // [row][16-byte word]: columns 32 li .. + 31
+template <int WF> struct FlRows;
+template <> struct FlRows<FMT_NVFP4> { using Item = GUItem<1>; using Down = DownRows; };
+template <> struct FlRows<FMT_BF16> { using Item = GUItemBF; using Down = DownRowsBF; };
+
+// 32 BF16 weights (four words) . 32 BF16 values (16 packed pairs), fp32.
+__device__ __forceinline__ float dot32_bf16(const uint4 (&w)[4], const uint32_t* v) {
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    p0 = dot2_bf16(w[q].x, v[4 * q], p0);
+    p0 = dot2_bf16(w[q].y, v[4 * q + 1], p0);
+    p0 = dot2_bf16(w[q].z, v[4 * q + 2], p0);
+    p0 = dot2_bf16(w[q].w, v[4 * q + 3], p0);
+  }
+#pragma unroll
+  for (int q = 2; q < 4; ++q) {
+    p1 = dot2_bf16(w[q].x, v[4 * q], p1);
+    p1 = dot2_bf16(w[q].y, v[4 * q + 1], p1);
+    p1 = dot2_bf16(w[q].z, v[4 * q + 2], p1);
+    p1 = dot2_bf16(w[q].w, v[4 * q + 3], p1);
+  }
+  return p0 + p1;
+}
+
+// rows 2p, 2p + 1 of the gate matrix at g and of the up matrix `up` elements
+// after it
+__device__ __forceinline__ void item_load(GUItemBF& it, const uint16_t* g, size_t up, int p, int lane) {
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        it.c[rr][m][q] = ldg_nt(g + m * up + (size_t)(2 * p + rr) * FL_H + 32 * lane + 8 * q);
+}
+
+__device__ __forceinline__ uint32_t item_h(const GUItemBF& it, float gsc, float usc, const XChunk<FMT_NVFP4>& xn) {
+  float h[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const float g = group_sum<64>(dot32_bf16(it.c[rr][0], xn.v));
+    const float u = group_sum<64>(dot32_bf16(it.c[rr][1], xn.v));
+    const float gv = round_bf16(g * gsc), uv = round_bf16(u * usc);
+    h[rr] = round_bf16(silu_f32(gv)) * uv;
+  }
+  return pack_bf16x2(h[0], h[1]);
+}
+
+// rows row0 + 4 rw + grp of the [H][I] matrix w, columns 32 li .. + 31
+__device__ __forceinline__ void down_load(DownRowsBF& d, const uint16_t* w, int row0, int lane) {
+  const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int rw = 0; rw < 2; ++rw)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d.c[rw][q] = ldg_nt(w + (size_t)(row0 + 4 * rw + grp) * FL_I + 32 * li + 8 * q);
+}
+
+__device__ __forceinline__ void down_dot(float (&acc)[2], const DownRowsBF& d, const uint32_t* hrow, float f, int lane) {
+  const int li = lane & 15;
+  uint32_t hx[16];
+  const uint4* hp = reinterpret_cast<const uint4*>(hrow + 16 * li);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = hp[i];
+    hx[4 * i] = v.x; hx[4 * i + 1] = v.y; hx[4 * i + 2] = v.z; hx[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int rw = 0; rw < 2; ++rw) acc[rw] = fmaf(f, dot32_bf16(d.c[rw], hx), acc[rw]);
+}
+
 // Loads of a layer that do not depend on its input, issued early: this
 // lane's 32 columns of gamma and of router row b (wave 0), the shared
 // expert's gate/up item b and its two tensor scales (wave 1), the
 // tensor-scale table entries.
-struct FlintPre {
+template <int WF>
+struct FlintPreT {
   uint4 g[4], r[4];
-  GUItem<1> sh;
+  typename FlRows<WF>::Item sh;
   GsPre gs;
   float shs[2];
 };
+using FlintPre = FlintPreT<FMT_NVFP4>;
 
-__device__ __forceinline__ void flint_prefetch(FlintPre& p, const LayerArgs& a, bool norm) {
+template <int WF>
+__device__ __forceinline__ void flint_prefetch(FlintPreT<WF>& p, const LayerArgs& a, bool norm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
   const uint16_t* gsrc = norm ? a.gamma : a.x;     // without the norm the gamma loads are dummies
@@ -97,19 +178,28 @@ __device__ __forceinline__ void flint_prefetch(FlintPre& p, const LayerArgs& a, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) p.r[i] = ldg<uint4>(a.router + (size_t)b * FL_H + 32 * lane + 8 * i);
   }
-  if (wave == 1) {
-    item_load(p.sh, a.sh_gu_codes, a.sh_gu_scales, b, lane);
+  if constexpr (WF == FMT_NVFP4) {
+    if (wave == 1) {
+      item_load(p.sh, a.sh_gu_codes, a.sh_gu_scales, b, lane);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) p.shs[j] = __hip_atomic_load(a.sh_gscale + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < 2; ++j) p.shs[j] = __hip_atomic_load(a.sh_gscale + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    gs_prefetch(p.gs, a.gscale, a.sh_gscale, FL_E);
+  } else {                                         // BF16 weights carry no tensor scales
+    if (wave == 1) item_load(p.sh, a.sh_gu_bf16, (size_t)FL_I * FL_H, b, lane);
+    p.shs[0] = p.shs[1] = 1.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) p.gs.v[q][j] = 1.f;
   }
-  gs_prefetch(p.gs, a.gscale, a.sh_gscale, FL_E);
 }
 
 // One layer; returns the epoch its hand-off words carry.  In a layer stack
 // (STACK) the token comes from LDS (lds_x) and the workgroup's output rows
 // go to LDS (lds_out); otherwise both are a.x and a.out in global memory.
-template <bool STACK, int KC>
-__device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const DecodeWs& ws, const FlintPre& pre,
+template <bool STACK, int KC, int WF = FMT_NVFP4>
+__device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const DecodeWs& ws, const FlintPreT<WF>& pre,
                                                 uint32_t epoch, uint32_t lim, const uint16_t* lds_x,
                                                 uint16_t* lds_out) {
   __shared__ float s_gs[FL_E + 1][3];
@@ -219,10 +309,13 @@ __device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const Decode
   const int item = K * b + (has_item ? wave : 0);
   const int islot = item / FL_IW, ip = item - islot * FL_IW;
   const int ie = __builtin_amdgcn_readfirstlane(s_exp[1 + islot]);
-  GUItem<1> it;
+  typename FlRows<WF>::Item it;
   if (has_item) {
-    constexpr size_t MC = (size_t)FL_I * FL_H / 2, MS = (size_t)FL_I * FL_H / 16;
-    item_load(it, a.gu_codes + (size_t)(2 * ie) * MC, a.gu_scales + (size_t)(2 * ie) * MS, ip, lane);
+    constexpr size_t MC = (size_t)FL_I * FL_H / 2, MS = (size_t)FL_I * FL_H / 16, MB = (size_t)FL_I * FL_H;
+    if constexpr (WF == FMT_NVFP4)
+      item_load(it, a.gu_codes + (size_t)(2 * ie) * MC, a.gu_scales + (size_t)(2 * ie) * MS, ip, lane);
+    else
+      item_load(it, a.gu_bf16 + (size_t)(2 * ie) * MB, MB, ip, lane);
   }
   if (wave == 0) {                                 // combine weights, off the load path
     const float my_s = lane < K ? 1.0f / (1.0f + expf(-my_logit)) : 0.f;
@@ -251,12 +344,17 @@ __device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const Decode
   const bool has_d1 = ds1 >= 1 && ds1 <= K, has_d2 = wave == 7 && K == 8;
   const int de1 = __builtin_amdgcn_readfirstlane(s_exp[has_d1 ? ds1 : 1]);
   const int de2 = __builtin_amdgcn_readfirstlane(s_exp[has_d2 ? 8 : 1]);
-  DownRows d1, d2;
-  constexpr size_t DC = (size_t)FL_H * FL_I / 2, DS = (size_t)FL_H * FL_I / 16;
-  if (has_d1) down_load(d1, a.d_codes + (size_t)de1 * DC, a.d_scales + (size_t)de1 * DS, FL_ROWS * b, lane);
-  DownRows dsh;                                    // the shared expert's (slot 0) on wave 7
-  if (wave == 7) down_load(dsh, a.sh_d_codes, a.sh_d_scales, FL_ROWS * b, lane);
-  if (has_d2) down_load(d2, a.d_codes + (size_t)de2 * DC, a.d_scales + (size_t)de2 * DS, FL_ROWS * b, lane);
+  typename FlRows<WF>::Down d1, d2, dsh;           // dsh: the shared expert's (slot 0) on wave 7
+  constexpr size_t DC = (size_t)FL_H * FL_I / 2, DS = (size_t)FL_H * FL_I / 16, DB = (size_t)FL_H * FL_I;
+  if constexpr (WF == FMT_NVFP4) {
+    if (has_d1) down_load(d1, a.d_codes + (size_t)de1 * DC, a.d_scales + (size_t)de1 * DS, FL_ROWS * b, lane);
+    if (wave == 7) down_load(dsh, a.sh_d_codes, a.sh_d_scales, FL_ROWS * b, lane);
+    if (has_d2) down_load(d2, a.d_codes + (size_t)de2 * DC, a.d_scales + (size_t)de2 * DS, FL_ROWS * b, lane);
+  } else {
+    if (has_d1) down_load(d1, a.d_bf16 + (size_t)de1 * DB, FL_ROWS * b, lane);
+    if (wave == 7) down_load(dsh, a.sh_d_bf16, FL_ROWS * b, lane);
+    if (has_d2) down_load(d2, a.d_bf16 + (size_t)de2 * DB, FL_ROWS * b, lane);
+  }
   {
     const uint64_t* hw = hw_all + (size_t)rep * HREP;
     // words per thread: (1 + k) slots of 256 words over 512 threads
@@ -306,15 +404,15 @@ __device__ __forceinline__ uint32_t flint_layer(const LayerArgs& a, const Decode
   return epoch;
 }
 
-template <int KC>
+template <int KC, int WF>
 __global__ __launch_bounds__(512) void flint_b1_kernel(LayerArgs a_arg, DecodeWs ws_arg) {
   const LayerArgs a = pin_layer_args(a_arg);
   const DecodeWs ws = pin_decode_ws(ws_arg);
-  FlintPre pre;
+  FlintPreT<WF> pre;
   flint_prefetch(pre, a, (a.flags & FLINT_PRE_RMSNORM) != 0);
   const uint32_t epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const uint32_t lim = wait_limit(ws);
-  flint_layer<false, KC>(a, ws, pre, epoch, lim, nullptr, nullptr);
+  flint_layer<false, KC, WF>(a, ws, pre, epoch, lim, nullptr, nullptr);
   // Every workgroup published its logit with the epoch it read at its start,
   // and workgroup 0 saw all of them before its top-k: none of this launch can
   // still be about to read the old value.
@@ -434,22 +532,34 @@ __global__ __launch_bounds__(512) void flint_stack_kernel(StackArgs sa_arg, Deco
 }  // namespace
 
 bool flint_b1_supported(const LayerArgs& a) {
-  if (a.B != 1 || (a.flags & FLINT_W_BF16)) return false;
+  if (a.B != 1) return false;
   if (a.H != FL_H || a.E != FL_E || a.I != FL_I || a.SI != FL_I || a.K > FLINT_MAX_TOP_K) return false;
   if (device_num_cu() < FL_G) return false;
-  static int per_cu = -1;                          // co-residency of the grid (see fused.hip)
+  static int per_cu = -1;                          // co-residency of the grid (see fused.hip), every form
   if (per_cu == -1) {
-    int ndev = 0, n = 0;
+    int ndev = 0, n[4] = {0, 0, 0, 0};
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) per_cu = -2;
-    else per_cu = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, flint_b1_kernel<0>, 512, 0) == hipSuccess ? n : -2;
+    else {
+      const bool ok =
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], flint_b1_kernel<0, FMT_NVFP4>, 512, 0) == hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], flint_b1_kernel<6, FMT_NVFP4>, 512, 0) == hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], flint_b1_kernel<0, FMT_BF16>, 512, 0) == hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[3], flint_b1_kernel<6, FMT_BF16>, 512, 0) == hipSuccess;
+      int m = n[0];
+      for (int i = 1; i < 4; ++i) m = n[i] < m ? n[i] : m;
+      per_cu = ok ? m : -2;
+    }
   }
   return per_cu == -2 || (int64_t)per_cu * device_num_cu() >= FL_G;
 }
 
 hipError_t launch_flint_b1(const LayerArgs& a, const DecodeWs& ws, hipStream_t st) {
   // the usual top-6 as a compile-time constant (straight-line selection)
-  if (a.K == 6) hipLaunchKernelGGL(flint_b1_kernel<6>, dim3(FL_G), dim3(512), 0, st, a, ws);
-  else hipLaunchKernelGGL(flint_b1_kernel<0>, dim3(FL_G), dim3(512), 0, st, a, ws);
+  const bool bf = (a.flags & FLINT_W_BF16) != 0;
+  if (a.K == 6 && bf) hipLaunchKernelGGL((flint_b1_kernel<6, FMT_BF16>), dim3(FL_G), dim3(512), 0, st, a, ws);
+  else if (bf) hipLaunchKernelGGL((flint_b1_kernel<0, FMT_BF16>), dim3(FL_G), dim3(512), 0, st, a, ws);
+  else if (a.K == 6) hipLaunchKernelGGL((flint_b1_kernel<6, FMT_NVFP4>), dim3(FL_G), dim3(512), 0, st, a, ws);
+  else hipLaunchKernelGGL((flint_b1_kernel<0, FMT_NVFP4>), dim3(FL_G), dim3(512), 0, st, a, ws);
   return hipGetLastError();
 }
 
