@@ -253,8 +253,9 @@ FLINT_API int32_t flint_nvfp4_dequant(const void* codes, const void* scales, int
  *   topk_w    (device) float [batch][K] or NULL; the combine weights
  *   gamma     (device) BF16 [H], required with FLINT_PRE_RMSNORM
  *   ws        (device) workspace of at least flint_moe_workspace_bytes(shape, batch)
- * With NVFP4 weights and hidden 2048 or 4096 (I, SI <= 2048) a batch-1 call
- * is one launch of a persistent grid (at most one workgroup per compute
+ * With NVFP4 weights and hidden 2048 or 4096 (I, SI <= 2048), and with BF16
+ * weights at the Flint shape (hidden 2048, 256 experts, I = SI = 512), a
+ * batch-1 call is one launch of a persistent grid (at most one workgroup per compute
  * unit) whose phases hand data over through epoch-tagged words in the
  * workspace.  That grid relies on all of its workgroups running at once:
  * the call checks at launch that the device can hold the whole grid (and
