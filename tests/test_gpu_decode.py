@@ -97,6 +97,20 @@ def test_flint_batch_top_k(top_k, batch):
                         src=src, layer=layer)
 
 
+@pytest.mark.parametrize("top_k", [1, 8])
+def test_flint_layer_bf16_weights_top_k(top_k):
+    """The BF16 form of the batch-1 single launch with a top-k other than 6
+    (its general variant): one routed expert, and eight (slot 8 on wave 7)."""
+    sh = dataclasses.replace(FLINT, top_k=top_k)
+    assert fm.flint_moe_decode_path(abi(sh, fm.FLINT_W_BF16), 1) == fm.FLINT_PATH_SINGLE_ONE
+    src = gen.moe_layer_source(sh, 170 + top_k, "cpu")
+    layer = pack(src)
+    layer.add_bf16()
+    for flags in (0, fm.FLINT_RENORM | fm.FLINT_PRE_RMSNORM | fm.FLINT_RESIDUAL):
+        run_decode_case(DecodeCase(sh, seed=180 + top_k + flags, batch=1, wbf16=True, flags=flags),
+                        src=src, layer=layer)
+
+
 def test_flint_layer_bf16_weights(flint_layer):
     """W16A16 at the Flint shape: batch 1 runs the BF16 form of the single
     launch (also with pre-norm + residual and renormalised weights), batch 8
