@@ -42,11 +42,29 @@ struct AttnArgs {
   float eps;
 };
 
+// a float64 value of the lane paired by a DPP pattern (two 32-bit moves)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// Sum over the head's LPH lanes, the same in each: pairs at distance 1,
+// then 2, then 4, ... (for 8 lanes the last step pairs lane i with 7 - i,
+// the other quad, through DPP instead of the LDS crossbar).
 template <int LPH>
 __device__ __forceinline__ double group_sum_f64(double v) {
+  if constexpr (LPH == 8) {
+    v += dpp_f64<0xB1>(v);                         // quad_perm [1, 0, 3, 2]
+    v += dpp_f64<0x4E>(v);                         // quad_perm [2, 3, 0, 1]
+    v += dpp_f64<0x141>(v);                        // row_half_mirror
+    return v;
+  } else {
 #pragma unroll
-  for (int off = 1; off < LPH; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
+    for (int off = 1; off < LPH; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+  }
 }
 
 // the lane's NP elements at p (NP = 8: 16 bytes; NP = 1: 2 bytes) as NP / 2
