@@ -50,21 +50,42 @@ __device__ __forceinline__ double dpp_f64(double v) {
   const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
-// Sum over the head's LPH lanes, the same in each: pairs at distance 1,
-// then 2, then 4, ... (for 8 lanes the last step pairs lane i with 7 - i,
-// the other quad, through DPP instead of the LDS crossbar).
+// v plus the value of the paired row (W = 16) or half wave (W = 32),
+// through permlane swaps of the two 32-bit halves (the swap returns both
+// values, the lane's own and its partner's)
+template <int W>
+__device__ __forceinline__ double swap_sum_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+  uint32_t l0, l1, h0, h1;
+  if constexpr (W == 16) {
+    const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    l0 = rl[0]; l1 = rl[1]; h0 = rh[0]; h1 = rh[1];
+  } else {
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    l0 = rl[0]; l1 = rl[1]; h0 = rh[0]; h1 = rh[1];
+  }
+  return __longlong_as_double((long long)(((uint64_t)h0 << 32) | l0)) +
+         __longlong_as_double((long long)(((uint64_t)h1 << 32) | l1));
+}
+// Sum over the head's LPH lanes, the same in each: blocks of 2, 4, ..
+// lanes, each the sum of its two halves (DPP within a row of 16, permlane
+// swaps across rows), the pairing of an xor butterfly without the LDS
+// crossbar.
 template <int LPH>
 __device__ __forceinline__ double group_sum_f64(double v) {
-  if constexpr (LPH == 8) {
-    v += dpp_f64<0xB1>(v);                         // quad_perm [1, 0, 3, 2]
-    v += dpp_f64<0x4E>(v);                         // quad_perm [2, 3, 0, 1]
-    v += dpp_f64<0x141>(v);                        // row_half_mirror
-    return v;
-  } else {
-#pragma unroll
-    for (int off = 1; off < LPH; off <<= 1) v += __shfl_xor(v, off, 64);
-    return v;
+  static_assert(LPH == 8 || LPH == 64, "heads of 8 or 64 lanes");
+  v += dpp_f64<0xB1>(v);                           // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);                           // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);                          // row_half_mirror
+  if constexpr (LPH == 64) {
+    v += dpp_f64<0x140>(v);                        // row_mirror
+    v = swap_sum_f64<16>(v);                       // rows 0 <-> 1, 2 <-> 3
+    v = swap_sum_f64<32>(v);                       // halves of the wave
   }
+  return v;
 }
 
 // the lane's NP elements at p (NP = 8: 16 bytes; NP = 1: 2 bytes) as NP / 2
